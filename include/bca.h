@@ -1,0 +1,206 @@
+/*
+ * bca.h — block-causal chunk attention over a ring-buffer KV cache (MI355X / gfx950).
+ *
+ * What is computed (sources are the web pages this library is built from):
+ *   - "WanToFight: Real-Time Generative Game Engine for Multi-Player Combat
+ *     Interaction" (xllm-io paper review), section 3 "model components" table,
+ *     rows Block-Causal Attention and Rolling KV Cache, and training Stage 2
+ *     (causal adaptation): tokens attend bidirectionally inside their own chunk
+ *     and, across chunks, only to the current chunk and the previous W chunks
+ *     (W = 2 there); the KV of recent chunks is kept in a rolling cache that is
+ *     updated after each chunk.
+ *   - "Matrix-Game 4.0: Harnessing Video Models for Real-Time Playable Game
+ *     Worlds" (paper summary), prerequisites "causal autoregression and KV cache"
+ *     and "technical novelty": the cache keeps a recent window (20 chunks) plus a
+ *     reference frame; a ring buffer overwrites the oldest slot in place instead
+ *     of moving the window; the window is cut into intervals computed in
+ *     parallel whose partial outputs are merged by log-sum-exp; K/V may be held
+ *     in 8-bit floating point.
+ *
+ * For one query chunk t of one layer and one head h the result is
+ *     O[i] = sum_j softmax_j(scale * <q_i, k_j>) v_j,   LSE[i] = ln sum_j exp(scale * <q_i, k_j>)
+ * where j runs over exactly the keys of the visible chunks:
+ *     the current chunk (k_cur, v_cur),
+ *     every ring chunk c with  t - W <= c <= t - 1,
+ *     the reference chunk, if use_ref is set and one has been appended.
+ * Segments (num_segments) only change the order of summation: each segment is an
+ * attention over a subset of keys, and the partial results are merged as
+ *     M = max_g LSE_g,  w_g = exp(LSE_g - M),  O = sum_g w_g O_g / sum_g w_g,
+ *     LSE = M + ln sum_g w_g.
+ *
+ * Conventions used by every entry point
+ *   - All device buffers are owned by the caller and allocated by the caller;
+ *     the library allocates no device memory and never synchronises a stream.
+ *   - Dense row-major layouts:
+ *       q, k_cur, v_cur, k, v, o : [n][H][d] in the stated dtype (the natural
+ *                                  output of a [n, H*d] projection)
+ *       lse                      : fp32 [H][n], natural logarithm
+ *       cache memory             : [L][K|V][H][S+R][n][d] in kv_dtype, R = has_ref;
+ *                                  the reference chunk is physical block S.
+ *   - Supported (qkv dtype, kv dtype) pairs: (F32, F32), (BF16, BF16),
+ *     (BF16, FP8_E4M3). head_dim must be 64 or 128 (FP8_E4M3: 128).
+ *   - Every argument is validated on the host before anything is enqueued. On
+ *     an error nothing is enqueued and the cache state is unchanged; the return
+ *     value says which class of error, bca_last_error() gives the text.
+ *   - One host thread and one stream per cache. Calls are asynchronous: results
+ *     are valid when the stream reaches them. The host-side slot table is
+ *     updated at call time, in stream order.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef BCA_H
+#define BCA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A HIP stream. This is the same type as hipStream_t; NULL is the null stream. */
+struct ihipStream_t;
+typedef struct ihipStream_t* bca_stream_t;
+
+typedef enum {
+  BCA_OK = 0,
+  BCA_ERR_INVALID_ARG = -1,  /* bad pointer, size, index or descriptor field          */
+  BCA_ERR_OUT_OF_ORDER = -2, /* chunk id went backwards, or the window is no longer
+                                resident in the ring                                   */
+  BCA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required            */
+  BCA_ERR_UNSUPPORTED = -4,  /* dtype pair or head_dim this build has no kernel for   */
+  BCA_ERR_HIP = -5           /* a HIP runtime call (launch, copy) failed              */
+} bca_status;
+
+typedef enum { BCA_F32 = 0, BCA_BF16 = 1, BCA_FP8_E4M3 = 2 } bca_dtype;
+
+typedef struct bca_cache bca_cache; /* opaque host handle */
+
+typedef struct {
+  int32_t num_layers;   /* L >= 1                                               */
+  int32_t num_heads;    /* H >= 1 (FP8_E4M3: H <= 64)                           */
+  int32_t head_dim;     /* d in {64, 128}                                       */
+  int32_t chunk_tokens; /* n >= 1: tokens per chunk (query chunk = cached chunk) */
+  int32_t ring_slots;   /* S in [1, 62]                                         */
+  int32_t has_ref;      /* R in {0, 1}: reserve one pinned reference block       */
+  int32_t kv_dtype;     /* bca_dtype of the cache: F32, BF16 or FP8_E4M3         */
+} bca_cache_desc;
+
+typedef struct {
+  int64_t q_chunk_id;   /* t >= 0: id of the query chunk                           */
+  int32_t history;      /* W in [0, S]: previous chunks visible (t-W .. t-1)       */
+  int32_t use_ref;      /* 1: the reference chunk is visible if it was appended    */
+  int32_t num_segments; /* G >= 1: split the visible keys into G contiguous
+                           segments per query tile and merge by log-sum-exp;
+                           0: the library chooses the split (balanced over the
+                           device's compute units); at most 64                    */
+  float scale;          /* softmax scale (finite), usually 1/sqrt(d)              */
+} bca_window_spec;
+
+/* Bytes of device memory a cache with this descriptor needs (K/V blocks of all
+ * layers). Returns 0 for an invalid descriptor. */
+size_t bca_cache_bytes(const bca_cache_desc* desc);
+
+/* Creates the host handle over caller memory dev_mem (at least
+ * bca_cache_bytes(desc) bytes, 256-byte aligned). All slots start empty
+ * (chunk id -1) and no reference chunk is present. Device memory is not
+ * touched. *out receives the handle. */
+bca_status bca_cache_create(const bca_cache_desc* desc, void* dev_mem, size_t bytes,
+                            bca_cache** out);
+
+/* Frees the host handle only; the device memory stays the caller's. NULL is a no-op. */
+bca_status bca_cache_destroy(bca_cache* cache);
+
+/* FP8_E4M3 caches only. Sets the per-head dequantisation scales of one layer:
+ * a stored code c means value decode(c) * scale. k_scale and v_scale are host
+ * arrays of H positive finite floats, copied before return. Appends quantise
+ * with round(x / scale) (fp32 division, round to nearest even, saturated to
+ * +-448). Setting scales empties that layer's slots and reference block, since
+ * chunks already stored were quantised with the old scales. Scales default to
+ * 1.0. Matrix-Game 4.0 summary, "technical novelty" and prerequisite
+ * "FP8 quantisation and CUDA Graph": attention K/V held in 8 bits. */
+bca_status bca_cache_set_kv_scales(bca_cache* cache, int32_t layer, const float* k_scale,
+                                   const float* v_scale);
+
+/* Writes one chunk's K and V (device, [n][H][d] in in_dtype) into the cache in
+ * place, as one fused kernel on `stream`: into ring slot chunk_id mod S, or into
+ * the reference block when is_ref is 1. The slot's previous content (the oldest
+ * chunk) is overwritten; nothing else moves (Matrix-Game 4.0 summary,
+ * prerequisite "causal autoregression and KV cache"; WanToFight review, rolling
+ * KV cache, updated after each chunk).
+ * in_dtype: F32 for an F32 cache, BF16 for BF16 and FP8_E4M3 caches (quantised
+ * on the fly with the layer's scales).
+ * Ordering: per layer, ring chunk ids are non-decreasing; an id equal to the
+ * last one re-writes that chunk in place; a smaller id returns
+ * BCA_ERR_OUT_OF_ORDER. chunk_id >= 0. For is_ref the id is recorded only. */
+bca_status bca_append_chunk(bca_cache* cache, int32_t layer, int64_t chunk_id, int32_t is_ref,
+                            const void* k, const void* v, int32_t in_dtype, bca_stream_t stream);
+
+/* Workspace bytes bca_attend needs for this spec (0 when it needs none). The
+ * figure covers any ring occupancy, so one buffer sized once serves every call
+ * with the same spec fields. Returns 0 as well for an invalid spec; check
+ * bca_attend's status. */
+size_t bca_attend_workspace_bytes(const bca_cache* cache, const bca_window_spec* spec);
+
+/* Block-causal attention of query chunk spec->q_chunk_id of one layer.
+ * q, k_cur, v_cur: device [n][H][d] in qkv_dtype; the current chunk's own K/V
+ * are passed here and are never read from the ring (the chunk is committed with
+ * bca_append_chunk after it is denoised: WanToFight review, section 5 "code
+ * analysis"; Matrix-Game 4.0 summary, method step 4). A ring slot holding id t
+ * itself is therefore not visible.
+ * o: device [n][H][d] in qkv_dtype. lse: device fp32 [H][n], may be NULL.
+ * workspace: device, at least bca_attend_workspace_bytes(); may be NULL when
+ * that is 0.
+ * Errors: BCA_ERR_OUT_OF_ORDER when a chunk of the window may already have been
+ * overwritten (the layer's newest ring id >= t - W + S).
+ * The visible set is resolved on the host from the slot table's chunk ids each
+ * call; invisible slots are never read, so their content (even NaN) cannot
+ * affect the result. */
+bca_status bca_attend(const bca_cache* cache, int32_t layer, const bca_window_spec* spec,
+                      const void* q, const void* k_cur, const void* v_cur, int32_t qkv_dtype,
+                      void* o, float* lse, void* workspace, size_t workspace_bytes,
+                      bca_stream_t stream);
+
+/* Host-side slot table query: chunk id held by ring slot `slot` (0 <= slot < S)
+ * of `layer`, -1 if empty. slot == S (with has_ref) reports the reference block
+ * (its recorded id, or -1). */
+bca_status bca_cache_slot_chunk(const bca_cache* cache, int32_t layer, int32_t slot,
+                                int64_t* chunk_id);
+
+/* Declares the content of a slot without touching device memory, for callers
+ * that filled the cache memory themselves (restoring a saved cache). Slot S
+ * (with has_ref) is the reference block. chunk_id -1 empties the slot. The
+ * layer's newest id is recomputed from the table. */
+bca_status bca_cache_set_slot_chunk(bca_cache* cache, int32_t layer, int32_t slot,
+                                    int64_t chunk_id);
+
+/* Host-only view of how bca_attend would run (no device work). */
+typedef struct {
+  int32_t num_visible_blocks; /* including the current chunk                          */
+  int32_t visible_blocks[64]; /* physical block per visible block, in key order;
+                                 0..S-1 ring slots, S the reference, -1 the current  */
+  int64_t visible_chunk_ids[64]; /* chunk id of each visible block (-1: current,
+                                    reference: its recorded id)                      */
+  int32_t visible_keys;       /* N_k = num_visible_blocks * n                         */
+  int32_t q_tiles;            /* query tiles per head                                 */
+  int32_t kv_tiles;           /* key tiles per query tile                             */
+  int32_t units;              /* H * q_tiles                                          */
+  int32_t workgroups;         /* work groups the attention kernel is launched with    */
+  int32_t max_pieces;         /* most segments any query tile is split into           */
+  int32_t merge;              /* 1 if the log-sum-exp merge kernel runs                */
+  size_t workspace_bytes;     /* what this call needs                                 */
+} bca_plan_info;
+
+bca_status bca_attend_plan(const bca_cache* cache, int32_t layer, const bca_window_spec* spec,
+                           bca_plan_info* out);
+
+/* Static text for a status code. */
+const char* bca_status_string(bca_status status);
+
+/* Text of the last error on the calling thread ("" if none). */
+const char* bca_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BCA_H */

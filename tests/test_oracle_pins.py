@@ -1,0 +1,15 @@
+"""The CPU oracle against its pins (no GPU)."""
+import pytest
+
+import oracle
+import oracle_pins
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return oracle.default()
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(lib, pin):
+    pin(lib)
