@@ -1,0 +1,547 @@
+// bca_api.cpp — the C interface of include/bca.h: cache handle, slot table,
+// window resolution, work planning, argument validation and kernel launches.
+//
+// Pure host C++: the only device work is the kernels bca_kernels.hip launches.
+//
+// Sources for the semantics (the web pages this library is built from):
+//  - "WanToFight: Real-Time Generative Game Engine for Multi-Player Combat
+//    Interaction" (xllm-io review), section 3 model components table
+//    (Block-Causal Attention: bidirectional in the chunk, across chunks the
+//    current one and the previous 2; Rolling KV Cache: the last 2 chunks,
+//    updated after each chunk) and section 5, code analysis (KV cached after the
+//    chunk is generated).
+//  - "Matrix-Game 4.0: Harnessing Video Models for Real-Time Playable Game
+//    Worlds" (paper summary), prerequisite "causal autoregression and KV cache"
+//    (recent window of 20 chunks plus a reference frame; the ring buffer writes
+//    the newest chunk over the oldest slot in place; split-window attention
+//    with a log-sum-exp merge) and "technical novelty" (7 intervals, 8-bit KV).
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "bca_internal.h"
+
+using namespace bca;
+
+struct bca_cache {
+  bca_cache_desc d;
+  char* mem = nullptr;
+  size_t bytes = 0;
+  std::vector<int64_t> slot;       // [L][S] chunk id per ring slot, -1 empty
+  std::vector<int64_t> newest;     // [L] newest ring chunk id, -1 none
+  std::vector<int64_t> ref_id;     // [L] recorded id of the reference chunk
+  std::vector<uint8_t> ref_valid;  // [L]
+  std::vector<float> k_scale;      // [L][H] fp8 dequantisation scales
+  std::vector<float> v_scale;
+  int num_cus = 0;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+bca_status fail(bca_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+bca_status fail(bca_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+size_t elem_size(int32_t dt) {
+  switch (dt) {
+    case BCA_F32: return 4;
+    case BCA_BF16: return 2;
+    case BCA_FP8_E4M3: return 1;
+  }
+  return 0;
+}
+
+bool desc_ok(const bca_cache_desc* d, std::string* why) {
+  auto bad = [&](const char* m) {
+    if (why) *why = m;
+    return false;
+  };
+  if (!d) return bad("desc is NULL");
+  if (d->num_layers < 1) return bad("num_layers must be >= 1");
+  if (d->num_heads < 1) return bad("num_heads must be >= 1");
+  if (d->head_dim != 64 && d->head_dim != 128) return bad("head_dim must be 64 or 128");
+  if (d->chunk_tokens < 1) return bad("chunk_tokens must be >= 1");
+  if (d->ring_slots < 1 || d->ring_slots > kMaxBlocks - 2)
+    return bad("ring_slots must be in [1, 62]");
+  if (d->has_ref != 0 && d->has_ref != 1) return bad("has_ref must be 0 or 1");
+  if (elem_size(d->kv_dtype) == 0) return bad("kv_dtype is not a bca_dtype");
+  if (d->kv_dtype == BCA_FP8_E4M3) {
+    if (d->num_heads > kMaxHeadsFp8) return bad("FP8_E4M3 caches support at most 64 heads");
+    if (d->head_dim != 128) return bad("FP8_E4M3 caches need head_dim 128");
+  }
+  // keys per head (all blocks plus the current chunk) must fit int32 with room
+  const int64_t blocks = (int64_t)d->ring_slots + d->has_ref + 1;
+  if (blocks * (int64_t)d->chunk_tokens > (int64_t)1 << 30) return bad("chunk_tokens too large");
+  return true;
+}
+
+// Bytes of one layer's K (or V) blocks: H * (S+R) * n * d elements.
+size_t half_layer_bytes(const bca_cache_desc& d) {
+  return (size_t)d.num_heads * (size_t)(d.ring_slots + d.has_ref) * (size_t)d.chunk_tokens *
+         (size_t)d.head_dim * elem_size(d.kv_dtype);
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool layer_ok(const bca_cache* c, int32_t layer) {
+  return layer >= 0 && layer < c->d.num_layers;
+}
+
+Kern kernel_for(int32_t qkv, int32_t kv) {
+  if (qkv == BCA_F32 && kv == BCA_F32) return Kern::F32;
+  if (qkv == BCA_BF16 && kv == BCA_BF16) return Kern::BF16;
+  return Kern::FP8;
+}
+
+bool pair_supported(int32_t qkv, int32_t kv) {
+  return (qkv == BCA_F32 && kv == BCA_F32) || (qkv == BCA_BF16 && kv == BCA_BF16) ||
+         (qkv == BCA_BF16 && kv == BCA_FP8_E4M3);
+}
+
+int wgs_per_cu(Kern k) {
+  static int override_ = [] {
+    const char* e = getenv("BCA_WGS_PER_CU");
+    return e ? atoi(e) : 0;
+  }();
+  if (override_ > 0) return override_;
+  // resident work groups per CU (LDS and register limited)
+  switch (k) {
+    case Kern::F32: return 4;
+    case Kern::BF16: return 1;
+    case Kern::FP8: return 1;
+  }
+  return 1;
+}
+
+int compute_units(const bca_cache* c) { return c->num_cus > 0 ? c->num_cus : 256; }
+
+// First work group whose iteration range contains iteration x when I
+// iterations are cut into P consecutive ranges [floor(w I / P), floor((w+1) I / P)).
+int64_t first_wg(int64_t x, int64_t I, int64_t P) { return ((x + 1) * P + I - 1) / I - 1; }
+
+// Partial-output slots a unit of T tiles needs when I = units*T iterations
+// are cut into P ranges (the largest number of ranges any unit touches).
+int32_t pieces_bound(int64_t units, int64_t T, int64_t P) {
+  int64_t I = units * T, worst = 1;
+  for (int64_t u = 0; u < units; ++u) {
+    int64_t a = first_wg(u * T, I, P), b = first_wg((u + 1) * T - 1, I, P);
+    if (b - a + 1 > worst) worst = b - a + 1;
+  }
+  return (int32_t)worst;
+}
+
+int64_t choose_wgs(const bca_cache* c, Kern k, int64_t units, int64_t T, int32_t G) {
+  const int64_t I = units * T;
+  if (G >= 1) return units * std::min<int64_t>(G, T);
+  int64_t target = (int64_t)compute_units(c) * wgs_per_cu(k);
+  return std::max<int64_t>(1, std::min(I, target));
+}
+
+size_t partial_bytes(int64_t units, int64_t jmax, int bm, int d) {
+  // part_o [units][jmax][bm][d] fp32, then part_lse [units][jmax][bm] fp32,
+  // each region 256-byte aligned
+  size_t po = (size_t)units * jmax * bm * d * 4;
+  size_t pl = (size_t)units * jmax * bm * 4;
+  po = (po + 255) & ~(size_t)255;
+  return po + ((pl + 255) & ~(size_t)255);
+}
+
+// Window resolution and planning shared by bca_attend, bca_attend_plan and
+// bca_attend_workspace_bytes. Validates everything except device pointers.
+bca_status make_plan(const bca_cache* c, int32_t layer, const bca_window_spec* s,
+                     int32_t qkv_dtype, Plan& p) {
+  if (!c) return fail(BCA_ERR_INVALID_ARG, "cache is NULL");
+  if (!s) return fail(BCA_ERR_INVALID_ARG, "spec is NULL");
+  if (!layer_ok(c, layer))
+    return fail(BCA_ERR_INVALID_ARG, "layer %d out of range [0, %d)", layer, c->d.num_layers);
+  const bca_cache_desc& d = c->d;
+  const int S = d.ring_slots, n = d.chunk_tokens;
+  if (s->q_chunk_id < 0) return fail(BCA_ERR_INVALID_ARG, "q_chunk_id must be >= 0");
+  if (s->history < 0 || s->history > S)
+    return fail(BCA_ERR_INVALID_ARG, "history %d must be in [0, ring_slots=%d]", s->history, S);
+  if (s->use_ref != 0 && s->use_ref != 1)
+    return fail(BCA_ERR_INVALID_ARG, "use_ref must be 0 or 1");
+  if (s->use_ref && !d.has_ref)
+    return fail(BCA_ERR_INVALID_ARG, "use_ref set but the cache has no reference block");
+  if (s->num_segments < 0 || s->num_segments > kMaxSegments)
+    return fail(BCA_ERR_INVALID_ARG, "num_segments must be in [0, 64]");
+  if (!std::isfinite(s->scale)) return fail(BCA_ERR_INVALID_ARG, "scale must be finite");
+  if (elem_size(qkv_dtype) == 0)
+    return fail(BCA_ERR_INVALID_ARG, "qkv_dtype is not a bca_dtype");
+  if (!pair_supported(qkv_dtype, d.kv_dtype))
+    return fail(BCA_ERR_UNSUPPORTED, "no kernel for qkv dtype %d with cache dtype %d",
+                qkv_dtype, d.kv_dtype);
+  const int64_t t = s->q_chunk_id, W = s->history;
+  const int64_t newest = c->newest[layer];
+  // Residency: chunk c is overwritten only by a chunk c' = c + k*S (k >= 1) that
+  // was appended later. If the newest ring id is below t - W + S, every such
+  // c' is >= c + S > newest for window chunks c >= t - W, so the window is intact.
+  if (newest >= 0 && newest >= t - W + S)
+    return fail(BCA_ERR_OUT_OF_ORDER,
+                "window of chunk %lld (history %lld) may be overwritten: newest ring chunk "
+                "is %lld with %d slots",
+                (long long)t, (long long)W, (long long)newest, S);
+
+  // a1: visible blocks, resolved from the slot table's chunk ids
+  p.nvis = 0;
+  for (int sl = 0; sl < S; ++sl) {
+    int64_t cid = c->slot[(size_t)layer * S + sl];
+    if (cid >= 0 && cid >= t - W && cid <= t - 1) {
+      p.vis_block[p.nvis] = sl;
+      p.vis_id[p.nvis++] = cid;
+    }
+  }
+  if (s->use_ref && c->ref_valid[layer]) {
+    p.vis_block[p.nvis] = S;
+    p.vis_id[p.nvis++] = c->ref_id[layer];
+  }
+  p.vis_block[p.nvis] = -1;
+  p.vis_id[p.nvis++] = -1;
+  p.nk = p.nvis * n;
+
+  // runs: consecutive physical blocks share one run
+  p.nruns = 0;
+  for (int i = 0; i < p.nvis; ++i) {
+    int b = p.vis_block[i];
+    if (b >= 0 && p.nruns > 0 && p.runs[p.nruns - 1].phys >= 0 &&
+        p.runs[p.nruns - 1].phys + p.runs[p.nruns - 1].len == b * n) {
+      p.runs[p.nruns - 1].len += n;
+      continue;
+    }
+    Run r;
+    r.vstart = i * n;
+    r.len = n;
+    r.phys = b >= 0 ? b * n : -1;
+    r.pad_ = 0;
+    p.runs[p.nruns++] = r;
+  }
+
+  // a3: work planning. Every query row of the chunk sees the same keys, so all
+  // units (head, query tile) have the same number of key tiles T. The
+  // units*T tile iterations are cut into P equal consecutive ranges, one per
+  // work group; a unit that spans several ranges is computed as several
+  // segments whose partial results are merged by log-sum-exp. With
+  // num_segments = G >= 1, P = units*min(G, T) makes every unit exactly G
+  // segments of near-equal length.
+  p.kern = kernel_for(qkv_dtype, d.kv_dtype);
+  TileShape ts = tile_shape(p.kern);
+  p.bm = ts.bm;
+  p.bn = ts.bn;
+  p.q_tiles = (n + p.bm - 1) / p.bm;
+  p.kv_tiles = (p.nk + p.bn - 1) / p.bn;
+  p.units = d.num_heads * p.q_tiles;
+  p.wgs = (int32_t)choose_wgs(c, p.kern, p.units, p.kv_tiles, s->num_segments);
+  p.jmax = pieces_bound(p.units, p.kv_tiles, p.wgs);
+  p.merge = p.jmax > 1 ? 1 : 0;
+  p.ws_bytes = p.merge ? partial_bytes(p.units, p.jmax, p.bm, d.head_dim) : 0;
+  return BCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t bca_cache_bytes(const bca_cache_desc* desc) {
+  std::string why;
+  if (!desc_ok(desc, &why)) return 0;
+  return 2 * (size_t)desc->num_layers * half_layer_bytes(*desc);
+}
+
+bca_status bca_cache_create(const bca_cache_desc* desc, void* dev_mem, size_t bytes,
+                            bca_cache** out) {
+  std::string why;
+  if (!out) return fail(BCA_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!desc_ok(desc, &why)) return fail(BCA_ERR_INVALID_ARG, "%s", why.c_str());
+  size_t need = bca_cache_bytes(desc);
+  if (!dev_mem) return fail(BCA_ERR_INVALID_ARG, "dev_mem is NULL");
+  if (!aligned(dev_mem, 256)) return fail(BCA_ERR_INVALID_ARG, "dev_mem not 256-byte aligned");
+  if (bytes < need)
+    return fail(BCA_ERR_INVALID_ARG, "cache memory %zu bytes < required %zu", bytes, need);
+  bca_cache* c = new (std::nothrow) bca_cache;
+  if (!c) return fail(BCA_ERR_INVALID_ARG, "out of host memory");
+  c->d = *desc;
+  c->mem = static_cast<char*>(dev_mem);
+  c->bytes = bytes;
+  const size_t L = desc->num_layers, S = desc->ring_slots, H = desc->num_heads;
+  c->slot.assign(L * S, -1);
+  c->newest.assign(L, -1);
+  c->ref_id.assign(L, -1);
+  c->ref_valid.assign(L, 0);
+  c->k_scale.assign(L * H, 1.0f);
+  c->v_scale.assign(L * H, 1.0f);
+  c->num_cus = device_compute_units();
+  *out = c;
+  g_err.clear();
+  return BCA_OK;
+}
+
+bca_status bca_cache_destroy(bca_cache* cache) {
+  delete cache;
+  return BCA_OK;
+}
+
+bca_status bca_cache_set_kv_scales(bca_cache* c, int32_t layer, const float* k_scale,
+                                   const float* v_scale) {
+  if (!c) return fail(BCA_ERR_INVALID_ARG, "cache is NULL");
+  if (c->d.kv_dtype != BCA_FP8_E4M3)
+    return fail(BCA_ERR_INVALID_ARG, "scales apply to FP8_E4M3 caches only");
+  if (!layer_ok(c, layer)) return fail(BCA_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (!k_scale || !v_scale) return fail(BCA_ERR_INVALID_ARG, "scale array is NULL");
+  const int H = c->d.num_heads;
+  for (int h = 0; h < H; ++h) {
+    if (!(std::isfinite(k_scale[h]) && k_scale[h] > 0.f && std::isfinite(v_scale[h]) &&
+          v_scale[h] > 0.f))
+      return fail(BCA_ERR_INVALID_ARG, "scale of head %d is not positive and finite", h);
+  }
+  for (int h = 0; h < H; ++h) {
+    c->k_scale[(size_t)layer * H + h] = k_scale[h];
+    c->v_scale[(size_t)layer * H + h] = v_scale[h];
+  }
+  // chunks stored under the old scales no longer decode correctly
+  const int S = c->d.ring_slots;
+  for (int s = 0; s < S; ++s) c->slot[(size_t)layer * S + s] = -1;
+  c->newest[layer] = -1;
+  c->ref_valid[layer] = 0;
+  c->ref_id[layer] = -1;
+  g_err.clear();
+  return BCA_OK;
+}
+
+bca_status bca_append_chunk(bca_cache* c, int32_t layer, int64_t chunk_id, int32_t is_ref,
+                            const void* k, const void* v, int32_t in_dtype,
+                            bca_stream_t stream) {
+  if (!c) return fail(BCA_ERR_INVALID_ARG, "cache is NULL");
+  if (!layer_ok(c, layer))
+    return fail(BCA_ERR_INVALID_ARG, "layer %d out of range [0, %d)", layer, c->d.num_layers);
+  if (chunk_id < 0) return fail(BCA_ERR_INVALID_ARG, "chunk_id must be >= 0");
+  if (is_ref != 0 && is_ref != 1) return fail(BCA_ERR_INVALID_ARG, "is_ref must be 0 or 1");
+  if (is_ref && !c->d.has_ref)
+    return fail(BCA_ERR_INVALID_ARG, "is_ref set but the cache has no reference block");
+  if (!k || !v) return fail(BCA_ERR_INVALID_ARG, "k or v is NULL");
+  if (!aligned(k, 16) || !aligned(v, 16))
+    return fail(BCA_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+  if (elem_size(in_dtype) == 0) return fail(BCA_ERR_INVALID_ARG, "in_dtype is not a bca_dtype");
+  const int32_t kv = c->d.kv_dtype;
+  bool ok = (in_dtype == BCA_F32 && kv == BCA_F32) || (in_dtype == BCA_BF16 && kv == BCA_BF16) ||
+            (in_dtype == BCA_BF16 && kv == BCA_FP8_E4M3);
+  if (!ok)
+    return fail(BCA_ERR_UNSUPPORTED, "cannot append dtype %d into a cache of dtype %d",
+                in_dtype, kv);
+  const int S = c->d.ring_slots;
+  if (!is_ref && chunk_id < c->newest[layer])
+    return fail(BCA_ERR_OUT_OF_ORDER, "chunk %lld appended after chunk %lld on layer %d",
+                (long long)chunk_id, (long long)c->newest[layer], layer);
+  // the oldest chunk's slot is overwritten in place: slot = id mod S
+  const int blk = is_ref ? S : (int)(chunk_id % S);
+  const size_t es = elem_size(kv);
+  const bca_cache_desc& d = c->d;
+  const size_t block_elems = (size_t)d.chunk_tokens * d.head_dim;
+  char* layer_k = c->mem + 2 * (size_t)layer * half_layer_bytes(d);
+  char* layer_v = layer_k + half_layer_bytes(d);
+  AppendArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.k = k;
+  a.v = v;
+  a.kdst = layer_k + (size_t)blk * block_elems * es;
+  a.vdst = layer_v + (size_t)blk * block_elems * es;
+  a.head_stride_elems = (int64_t)(S + d.has_ref) * (int64_t)block_elems;
+  a.n = d.chunk_tokens;
+  a.H = d.num_heads;
+  if (kv == BCA_FP8_E4M3)
+    for (int h = 0; h < d.num_heads; ++h) {
+      a.k_scale[h] = c->k_scale[(size_t)layer * d.num_heads + h];
+      a.v_scale[h] = c->v_scale[(size_t)layer * d.num_heads + h];
+    }
+  int err = launch_append((bca_dtype)in_dtype, (bca_dtype)kv, d.head_dim, a, (void*)stream);
+  if (err != 0) return fail(BCA_ERR_HIP, "append kernel launch failed (hip error %d)", err);
+  if (is_ref) {
+    c->ref_valid[layer] = 1;
+    c->ref_id[layer] = chunk_id;
+  } else {
+    c->slot[(size_t)layer * S + blk] = chunk_id;
+    c->newest[layer] = chunk_id;
+  }
+  g_err.clear();
+  return BCA_OK;
+}
+
+size_t bca_attend_workspace_bytes(const bca_cache* c, const bca_window_spec* s) {
+  if (!c || !s) return 0;
+  const int S = c->d.ring_slots, n = c->d.chunk_tokens;
+  if (s->history < 0 || s->history > S || s->num_segments < 0 || s->num_segments > kMaxSegments)
+    return 0;
+  // The qkv dtype follows from the cache dtype (F32 -> F32, otherwise BF16).
+  const int32_t qkv = c->d.kv_dtype == BCA_F32 ? BCA_F32 : BCA_BF16;
+  const Kern k = kernel_for(qkv, c->d.kv_dtype);
+  const TileShape ts = tile_shape(k);
+  const int64_t q_tiles = (n + ts.bm - 1) / ts.bm;
+  const int64_t units = (int64_t)c->d.num_heads * q_tiles;
+  // Bound over every ring occupancy: 1 visible block (the current chunk) up to
+  // all ring slots, the reference and the current chunk.
+  size_t worst = 0;
+  const int max_blocks = S + c->d.has_ref + 1;
+  for (int blocks = 1; blocks <= max_blocks; ++blocks) {
+    int64_t T = ((int64_t)blocks * n + ts.bn - 1) / ts.bn;
+    int64_t P = choose_wgs(c, k, units, T, s->num_segments);
+    int32_t jmax = pieces_bound(units, T, P);
+    if (jmax > 1) worst = std::max(worst, partial_bytes(units, jmax, ts.bm, c->d.head_dim));
+  }
+  return worst;
+}
+
+bca_status bca_attend(const bca_cache* c, int32_t layer, const bca_window_spec* s,
+                      const void* q, const void* k_cur, const void* v_cur, int32_t qkv_dtype,
+                      void* o, float* lse, void* workspace, size_t workspace_bytes,
+                      bca_stream_t stream) {
+  Plan p;
+  bca_status st = make_plan(c, layer, s, qkv_dtype, p);
+  if (st != BCA_OK) return st;
+  if (!q || !k_cur || !v_cur || !o)
+    return fail(BCA_ERR_INVALID_ARG, "q, k_cur, v_cur and o must not be NULL");
+  if (!aligned(q, 16) || !aligned(k_cur, 16) || !aligned(v_cur, 16) || !aligned(o, 16) ||
+      (lse && !aligned(lse, 4)))
+    return fail(BCA_ERR_INVALID_ARG, "q, k_cur, v_cur and o must be 16-byte aligned");
+  if (p.ws_bytes > 0) {
+    if (!workspace) return fail(BCA_ERR_WORKSPACE, "workspace of %zu bytes required", p.ws_bytes);
+    if (!aligned(workspace, 256))
+      return fail(BCA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < p.ws_bytes)
+      return fail(BCA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
+                  p.ws_bytes);
+  }
+  const bca_cache_desc& d = c->d;
+  AttnArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.q = q;
+  a.kcur = k_cur;
+  a.vcur = v_cur;
+  char* layer_k = c->mem + 2 * (size_t)layer * half_layer_bytes(d);
+  a.kc = layer_k;
+  a.vc = layer_k + half_layer_bytes(d);
+  a.o = o;
+  a.lse = lse;
+  if (p.merge) {
+    size_t po = (size_t)p.units * p.jmax * p.bm * d.head_dim * 4;
+    po = (po + 255) & ~(size_t)255;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + po);
+  }
+  a.cache_head_elems = (int64_t)(d.ring_slots + d.has_ref) * d.chunk_tokens * d.head_dim;
+  a.n = d.chunk_tokens;
+  a.H = d.num_heads;
+  a.nk = p.nk;
+  a.T = p.kv_tiles;
+  a.QT = p.q_tiles;
+  a.units = p.units;
+  a.P = p.wgs;
+  a.jmax = p.jmax;
+  a.scale = s->scale;
+  a.scale_log2 = (float)((double)s->scale * 1.4426950408889634);
+  a.xcd_remap = (p.wgs % 8 == 0) ? 1 : 0;
+  a.nruns = p.nruns;
+  for (int i = 0; i < p.nruns; ++i) a.runs[i] = p.runs[i];
+  if (d.kv_dtype == BCA_FP8_E4M3)
+    for (int h = 0; h < d.num_heads; ++h) {
+      a.k_scale[h] = c->k_scale[(size_t)layer * d.num_heads + h];
+      a.v_scale[h] = c->v_scale[(size_t)layer * d.num_heads + h];
+    }
+  int err = launch_attention(p, a, d.head_dim, (void*)stream);
+  if (err == -1) return fail(BCA_ERR_UNSUPPORTED, "no attention kernel for this dtype pair yet");
+  if (err != 0) return fail(BCA_ERR_HIP, "attention launch failed (hip error %d)", err);
+  g_err.clear();
+  return BCA_OK;
+}
+
+bca_status bca_cache_slot_chunk(const bca_cache* c, int32_t layer, int32_t slot,
+                                int64_t* chunk_id) {
+  if (!c || !chunk_id) return fail(BCA_ERR_INVALID_ARG, "cache or chunk_id is NULL");
+  if (!layer_ok(c, layer)) return fail(BCA_ERR_INVALID_ARG, "layer %d out of range", layer);
+  const int S = c->d.ring_slots;
+  if (slot == S && c->d.has_ref) {
+    *chunk_id = c->ref_valid[layer] ? c->ref_id[layer] : -1;
+    return BCA_OK;
+  }
+  if (slot < 0 || slot >= S) return fail(BCA_ERR_INVALID_ARG, "slot %d out of range", slot);
+  *chunk_id = c->slot[(size_t)layer * S + slot];
+  return BCA_OK;
+}
+
+bca_status bca_cache_set_slot_chunk(bca_cache* c, int32_t layer, int32_t slot,
+                                    int64_t chunk_id) {
+  if (!c) return fail(BCA_ERR_INVALID_ARG, "cache is NULL");
+  if (!layer_ok(c, layer)) return fail(BCA_ERR_INVALID_ARG, "layer %d out of range", layer);
+  if (chunk_id < -1) return fail(BCA_ERR_INVALID_ARG, "chunk_id must be >= -1");
+  const int S = c->d.ring_slots;
+  if (slot == S && c->d.has_ref) {
+    c->ref_valid[layer] = chunk_id >= 0 ? 1 : 0;
+    c->ref_id[layer] = chunk_id;
+    return BCA_OK;
+  }
+  if (slot < 0 || slot >= S) return fail(BCA_ERR_INVALID_ARG, "slot %d out of range", slot);
+  if (chunk_id >= 0 && chunk_id % S != slot)
+    return fail(BCA_ERR_INVALID_ARG, "chunk %lld belongs in slot %lld, not %d",
+                (long long)chunk_id, (long long)(chunk_id % S), slot);
+  c->slot[(size_t)layer * S + slot] = chunk_id;
+  int64_t nw = -1;
+  for (int sl = 0; sl < S; ++sl) nw = std::max(nw, c->slot[(size_t)layer * S + sl]);
+  c->newest[layer] = nw;
+  return BCA_OK;
+}
+
+bca_status bca_attend_plan(const bca_cache* c, int32_t layer, const bca_window_spec* s,
+                           bca_plan_info* out) {
+  if (!out) return fail(BCA_ERR_INVALID_ARG, "out is NULL");
+  if (!c) return fail(BCA_ERR_INVALID_ARG, "cache is NULL");
+  Plan p;
+  int32_t qkv = c->d.kv_dtype == BCA_F32 ? BCA_F32 : BCA_BF16;
+  bca_status st = make_plan(c, layer, s, qkv, p);
+  if (st != BCA_OK) return st;
+  std::memset(out, 0, sizeof *out);
+  out->num_visible_blocks = p.nvis;
+  for (int i = 0; i < p.nvis; ++i) {
+    out->visible_blocks[i] = p.vis_block[i];
+    out->visible_chunk_ids[i] = p.vis_id[i];
+  }
+  out->visible_keys = p.nk;
+  out->q_tiles = p.q_tiles;
+  out->kv_tiles = p.kv_tiles;
+  out->units = p.units;
+  out->workgroups = p.wgs;
+  out->max_pieces = p.jmax;
+  out->merge = p.merge;
+  out->workspace_bytes = p.ws_bytes;
+  g_err.clear();
+  return BCA_OK;
+}
+
+const char* bca_status_string(bca_status s) {
+  switch (s) {
+    case BCA_OK: return "BCA_OK";
+    case BCA_ERR_INVALID_ARG: return "BCA_ERR_INVALID_ARG";
+    case BCA_ERR_OUT_OF_ORDER: return "BCA_ERR_OUT_OF_ORDER";
+    case BCA_ERR_WORKSPACE: return "BCA_ERR_WORKSPACE";
+    case BCA_ERR_UNSUPPORTED: return "BCA_ERR_UNSUPPORTED";
+    case BCA_ERR_HIP: return "BCA_ERR_HIP";
+  }
+  return "BCA_ERR_UNKNOWN";
+}
+
+const char* bca_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,110 @@
+// Internal structures shared by the host logic (bca_host.cpp, bca_api.cpp) and the
+// HIP kernels (bca_kernels.hip). Not part of the public interface.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/bca.h"
+
+namespace bca {
+
+constexpr int kMaxBlocks = 64;  // ring slots + reference + current chunk
+constexpr int kMaxHeadsFp8 = 64;
+constexpr int kMaxSegments = 64;
+
+// A maximal range of consecutive visible keys that sits at one base address.
+// Visible keys are numbered 0 .. nk-1 in "key order": visible ring slots in
+// physical order, then the reference block, then the current chunk. Runs of
+// the cache are ranges of the head's [(S+R)*n][d] matrix; the current chunk is
+// a run of its own with row stride H*d.
+struct Run {
+  int32_t vstart;  // first key of the run in key order
+  int32_t len;     // number of keys
+  int32_t phys;    // first row in the head's cache matrix, or -1 for the current chunk
+  int32_t pad_;
+};
+
+// Kernel families; each has fixed tile sizes.
+enum class Kern : int { F32 = 0, BF16 = 1, FP8 = 2 };
+
+struct TileShape {
+  int bm;  // query rows per work group
+  int bn;  // keys per tile
+};
+
+inline TileShape tile_shape(Kern k) {
+  switch (k) {
+    case Kern::F32: return {64, 32};
+    case Kern::BF16: return {128, 64};
+    case Kern::FP8: return {128, 64};
+  }
+  return {128, 64};
+}
+
+// What one bca_attend call does, as resolved on the host.
+struct Plan {
+  Kern kern;
+  int32_t nvis;                     // visible blocks, current included
+  int32_t vis_block[kMaxBlocks];    // physical block (S = reference, -1 = current)
+  int64_t vis_id[kMaxBlocks];
+  int32_t nruns;
+  Run runs[kMaxBlocks];
+  int32_t nk;                       // visible keys
+  int32_t bm, bn;
+  int32_t q_tiles, kv_tiles, units; // units = H * q_tiles
+  int32_t wgs;                      // work groups (P)
+  int32_t jmax;                     // partial slots reserved per unit
+  int32_t merge;                    // 1: some unit is split over work groups
+  size_t ws_bytes;                  // workspace this call needs
+};
+
+// Arguments of the attention kernels (passed by value as kernel arguments).
+struct AttnArgs {
+  const void* q;      // [n][H][d]
+  const void* kcur;   // [n][H][d]
+  const void* vcur;   // [n][H][d]
+  const void* kc;     // this layer's K blocks: [H][S+R][n][d]
+  const void* vc;     // this layer's V blocks
+  void* o;            // [n][H][d]
+  float* lse;         // [H][n] or null
+  float* part_o;      // [units][jmax][bm][d] fp32
+  float* part_lse;    // [units][jmax][bm]
+  int64_t cache_head_elems;  // (S+R)*n*d
+  int32_t n, H, nk, T, QT, units, P, jmax;
+  float scale;        // softmax scale
+  float scale_log2;   // scale * log2(e)
+  int32_t xcd_remap;  // 1: spread work-group ids so each XCD gets a contiguous range
+  int32_t nruns;
+  Run runs[kMaxBlocks];
+  float k_scale[kMaxHeadsFp8];  // fp8 cache: dequantisation scale per head
+  float v_scale[kMaxHeadsFp8];
+};
+
+struct MergeArgs {
+  const float* part_o;
+  const float* part_lse;
+  void* o;
+  float* lse;
+  int32_t n, H, T, QT, units, P, jmax, bm;
+};
+
+struct AppendArgs {
+  const void* k;   // [n][H][d]
+  const void* v;
+  void* kdst;      // this layer's K blocks, block `blk`
+  void* vdst;
+  int64_t head_stride_elems;  // (S+R)*n*d
+  int32_t n, H;
+  float k_scale[kMaxHeadsFp8];  // fp8 cache only
+  float v_scale[kMaxHeadsFp8];
+};
+
+// Launchers (bca_kernels.hip). They return the HIP error code (0 = success).
+int launch_attention(const Plan& plan, const AttnArgs& args, int head_dim, void* stream);
+int launch_append(bca_dtype in, bca_dtype kv, int head_dim, const AppendArgs& args,
+                  void* stream);
+// Compute units of the current device, or 0 when it cannot be queried.
+int device_compute_units();
+
+}  // namespace bca

@@ -1,0 +1,701 @@
+// bca_kernels.hip — gfx950 kernels of block-causal ring-KV chunk attention.
+//
+//   attn_bf16_kernel  bf16 flash attention on MFMA (v_mfma_f32_32x32x16_bf16)
+//   attn_f32_kernel   fp32 flash attention on the vector ALUs
+//   merge_kernel      log-sum-exp merge of segment partials
+//   append_kernel     fused K/V write of one chunk into its ring slot
+//
+// What is computed follows "WanToFight" (xllm-io review), section 3 model
+// components table (block-causal attention: bidirectional in the chunk, causal
+// over a bounded window of chunks; rolling KV cache), and "Matrix-Game 4.0"
+// (paper summary), prerequisite "causal autoregression and KV cache" (ring
+// buffer overwritten in place; the window split into intervals merged by
+// log-sum-exp) and "technical novelty". The pages' kernels were written for
+// other GPUs; the tiling below is designed for CDNA4 wave64 MFMA and LDS.
+//
+// Work decomposition shared by the attention kernels. The keys a query chunk
+// sees are the same for every row of the chunk (the mask is block-causal), so
+// the host lists the visible keys as "runs" of consecutive rows and every
+// (head, query tile) unit has the same number T of key tiles. The units*T tile
+// iterations are cut into P consecutive, equal ranges, one per work group
+// ("stream-K"); a unit whose tiles span several ranges is computed as several
+// segments, each written as a normalised partial output plus its LSE, and
+// merge_kernel combines them. A unit computed whole writes the final output.
+#include <hip/hip_runtime.h>
+
+#include "bca_internal.h"
+
+namespace bca {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ __forceinline__ int64_t range_begin(int64_t w, int64_t I, int64_t P) {
+  return w * I / P;
+}
+
+// First work group whose range contains iteration x.
+__device__ __forceinline__ int64_t first_wg_of(int64_t x, int64_t I, int64_t P) {
+  return ((x + 1) * P + I - 1) / I - 1;
+}
+
+// Work-group ids are handed to the 8 XCDs round robin (id % 8). Remapping so
+// that XCD x gets the contiguous range [x P/8, (x+1) P/8) keeps the work
+// groups that read the same head's K/V on one XCD and its L2.
+__device__ __forceinline__ int logical_wg(const AttnArgs& a) {
+  int b = blockIdx.x;
+  if (a.xcd_remap) {
+    const int per = a.P >> 3;
+    b = (b & 7) * per + (b >> 3);
+  }
+  return b;
+}
+
+// K/V rows are read with buffer loads. Each head has two resources per
+// tensor: its cache matrix [(S+R)*n][d] and its rows of the current chunk
+// (row stride H*d). An offset past a resource's size reads as zero, which
+// is how rows beyond the last visible key become zero rows without a branch.
+constexpr int kBufDword3 = 0x00020000;  // raw buffer, gfx9 family
+constexpr int kOob = 0x7ffffff0;
+
+struct HeadSrc {
+  __amdgpu_buffer_rsrc_t cache;  // this head's cache matrix
+  __amdgpu_buffer_rsrc_t cur;    // this head's rows of the current chunk
+};
+
+__device__ __forceinline__ HeadSrc head_src(const void* cache_base, const void* cur_base,
+                                            const AttnArgs& a, int h, int D, int es_cache,
+                                            int es_cur) {
+  HeadSrc r;
+  const int64_t hc = (int64_t)h * a.cache_head_elems * es_cache;
+  r.cache = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(cache_base) + hc), (short)0,
+      (int)(a.cache_head_elems * es_cache), kBufDword3);
+  const int64_t hq = (int64_t)h * D * es_cur;
+  r.cur = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(cur_base) + hq), (short)0,
+      (int)(((int64_t)(a.n - 1) * a.H * D + D) * es_cur), kBufDword3);
+  return r;
+}
+
+__device__ __forceinline__ uint4 buf16(__amdgpu_buffer_rsrc_t r, int off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Loads 16 bytes at byte column `colb` of NR key rows (key numbers j[i]) of
+// the tile of BN keys starting at j0; `ri` is the run holding j0. Keys at or
+// beyond nk read as zeros.
+template <int NR, int BN>
+__device__ __forceinline__ void load_rows(const AttnArgs& a, const HeadSrc& src, int D,
+                                          int es_cache, int es_cur, int j0, int ri,
+                                          const int (&j)[NR], int colb, uint4 (&out)[NR]) {
+  const Run R0 = a.runs[ri];
+  if (j0 + BN <= R0.vstart + R0.len) {
+    // the whole tile lies in one run and every row is valid
+    if (R0.phys >= 0) {
+#pragma unroll
+      for (int i = 0; i < NR; ++i)
+        out[i] = buf16(src.cache, (R0.phys + j[i] - R0.vstart) * D * es_cache + colb);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NR; ++i)
+        out[i] = buf16(src.cur, (j[i] - R0.vstart) * a.H * D * es_cur + colb);
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < NR; ++i) out[i] = make_uint4(0, 0, 0, 0);
+  for (int r = ri; r < a.nruns; ++r) {
+    const Run R = a.runs[r];
+    if (R.vstart >= j0 + BN) break;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const bool in = j[i] >= R.vstart && j[i] < R.vstart + R.len;
+      uint4 v;
+      if (R.phys >= 0)
+        v = buf16(src.cache, in ? (R.phys + j[i] - R.vstart) * D * es_cache + colb : kOob);
+      else
+        v = buf16(src.cur, in ? (j[i] - R.vstart) * a.H * D * es_cur + colb : kOob);
+      out[i].x |= v.x;
+      out[i].y |= v.y;
+      out[i].z |= v.z;
+      out[i].w |= v.w;
+    }
+  }
+}
+
+// Advances ri to the run holding key j0 (runs are visited in increasing order).
+__device__ __forceinline__ int advance_run(const AttnArgs& a, int ri, int j0) {
+  while (ri + 1 < a.nruns && a.runs[ri].vstart + a.runs[ri].len <= j0) ++ri;
+  return ri;
+}
+
+__device__ __forceinline__ uint32_t u4_get(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+__device__ __forceinline__ float wave_swap32_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+__device__ __forceinline__ float wave_swap32_sum(float x) { return x + __shfl_xor(x, 32); }
+
+// ---------------------------------------------------------------------------
+// bf16 attention on MFMA.
+//
+// Work group: 256 threads = 4 waves; BM = 128 query rows (32 per wave); key
+// tiles of BN = 64, double-buffered in LDS.
+// Per wave and tile the scores are computed transposed, S^T = K Q^T, with
+// v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims from LDS, B = 16 dims x 32
+// queries held in registers for the whole unit). In the 32x32 result lane l
+// holds query l%32 and 16 keys, so a row's max and sum need one exchange with
+// lane l^32 only. P^T stays in registers as the B operand of O^T += V^T P^T;
+// the MFMA's k index runs over keys in the order the score layout leaves them
+// in each lane, and V^T is stored in LDS with the matching key permutation so
+// each lane's 8 keys are one 16-byte read.
+// Online softmax in base 2 with a lazy rescale: the running maximum m is only
+// raised (and O, l rescaled) when a tile's maximum exceeds m by more than 8,
+// so weights stay below 2^8 and most tiles skip the rescale.
+template <int D>
+struct Bf16Cfg {
+  static constexpr int BM = 128, BN = 64, NT = 256;
+  static constexpr int KSTR = D * 2 + 16;   // bytes per key row of the K tile (padded)
+  static constexpr int VSTR = BN * 2 + 16;  // bytes per dim row of the V^T tile (padded)
+  static constexpr int KT_BYTES = BN * KSTR;
+  static constexpr int VT_BYTES = D * VSTR;
+  static constexpr int STAGE = KT_BYTES + VT_BYTES;
+  static constexpr int CPR = D / 8;          // 16-byte chunks per key row
+  static constexpr int RPP = NT / CPR;       // K rows loaded per pass
+  static constexpr int KPASS = BN / RPP;     // K passes per tile
+  static constexpr int VITEMS = (BN / 4) * CPR;  // (4 keys x 8 dims) items per V tile
+};
+
+// Position of key k (0..63) in a V^T row: inside each group of 16 keys the
+// quads 4..7 and 8..11 trade places, so that lanes 0-31 find keys
+// {0-3, 8-11} and lanes 32-63 keys {4-7, 12-15} as 8 consecutive entries.
+__device__ __forceinline__ int vt_pos_of_quad(int kq) {
+  const int q = kq & 3;
+  const int sw = (q == 1) ? 2 : (q == 2) ? 1 : q;
+  return (kq >> 2) * 16 + sw * 4;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnArgs a) {
+  using C = Bf16Cfg<D>;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int w = logical_wg(a);
+  const int64_t I = (int64_t)a.units * a.T;
+  int64_t it = range_begin(w, I, a.P);
+  const int64_t it_end = range_begin(w + 1, I, a.P);
+
+  // this thread's load assignment inside a tile
+  const int k_row0 = tid / C::CPR, k_col = tid % C::CPR;
+  const bool v_active = tid < C::VITEMS;
+  const int v_kq = tid / C::CPR, v_dg = tid % C::CPR;
+
+  while (it < it_end) {
+    const int u = (int)(it / a.T);
+    const int t0 = (int)(it - (int64_t)u * a.T);
+    const int t1 = (int)((it_end - it) < (int64_t)(a.T - t0) ? t0 + (it_end - it) : a.T);
+    const int h = u / a.QT, qt = u - h * a.QT;
+    const int q0 = qt * C::BM + wave * 32;
+    const bool wave_rows = q0 < a.n;
+
+    // Q^T fragments (B operand): lane holds query q0+l32, dims 16kk+8hi .. +7
+    bf16x8_t qf[D / 16];
+    {
+      const int row = q0 + l32;
+      if (row < a.n) {
+        const __bf16* qp = static_cast<const __bf16*>(a.q) + ((int64_t)row * a.H + h) * D + 8 * hi;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * kk);
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) qf[kk] = bf16x8_t{};
+      }
+    }
+
+    f32x16_t o[D / 32];
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
+    float m_run = -INFINITY, l_run = 0.f;
+    int ri = 0;
+
+    uint4 kreg[C::KPASS];
+    uint4 vreg[4];
+
+    const HeadSrc ksrc = head_src(a.kc, a.kcur, a, h, D, 2, 2);
+    const HeadSrc vsrc = head_src(a.vc, a.vcur, a, h, D, 2, 2);
+
+    auto load_tile = [&](int tile) {
+      const int j0 = tile * C::BN;
+      ri = advance_run(a, ri, j0);
+      int jk[C::KPASS];
+#pragma unroll
+      for (int p = 0; p < C::KPASS; ++p) jk[p] = j0 + k_row0 + p * C::RPP;
+      load_rows<C::KPASS, C::BN>(a, ksrc, D, 2, 2, j0, ri, jk, k_col * 16, kreg);
+      if (v_active) {
+        int jv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) jv[e] = j0 + 4 * v_kq + e;
+        load_rows<4, C::BN>(a, vsrc, D, 2, 2, j0, ri, jv, v_dg * 16, vreg);
+      }
+    };
+
+    auto store_tile = [&](int st) {
+      unsigned char* Ks = smem + st * C::STAGE;
+      unsigned char* Vs = Ks + C::KT_BYTES;
+#pragma unroll
+      for (int p = 0; p < C::KPASS; ++p)
+        *reinterpret_cast<uint4*>(Ks + (k_row0 + p * C::RPP) * C::KSTR + k_col * 16) = kreg[p];
+      if (v_active) {
+        // vreg[e] holds key 4kq+e, dims 8dg..8dg+7 (two per dword). Write dims
+        // as rows of V^T: 4 keys (8 bytes) per dim row.
+        const int pos = vt_pos_of_quad(v_kq);
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+          const int d0 = 8 * v_dg + 2 * wd;
+          const uint32_t a0 = u4_get(vreg[0], wd), a1 = u4_get(vreg[1], wd);
+          const uint32_t a2 = u4_get(vreg[2], wd), a3 = u4_get(vreg[3], wd);
+          uint2 ev, od;
+          ev.x = (a0 & 0xffffu) | (a1 << 16);
+          ev.y = (a2 & 0xffffu) | (a3 << 16);
+          od.x = (a0 >> 16) | (a1 & 0xffff0000u);
+          od.y = (a2 >> 16) | (a3 & 0xffff0000u);
+          *reinterpret_cast<uint2*>(Vs + d0 * C::VSTR + pos * 2) = ev;
+          *reinterpret_cast<uint2*>(Vs + (d0 + 1) * C::VSTR + pos * 2) = od;
+        }
+      }
+    };
+
+    load_tile(t0);
+    store_tile(0);
+    __syncthreads();
+
+    for (int tile = t0; tile < t1; ++tile) {
+      const int st = (tile - t0) & 1;
+      const bool more = tile + 1 < t1;
+      if (more) load_tile(tile + 1);
+
+      if (wave_rows) {
+        const unsigned char* Ks = smem + st * C::STAGE;
+        const unsigned char* Vs = Ks + C::KT_BYTES;
+        f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const int cb = (16 * kk + 8 * hi) * 2;
+          const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(Ks + l32 * C::KSTR + cb);
+          const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(Ks + (32 + l32) * C::KSTR + cb);
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[kk], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[kk], s1, 0, 0, 0);
+        }
+        // keys past the last visible one (only in the final tile)
+        const int j0 = tile * C::BN;
+        if (j0 + C::BN > a.nk) {
+          const int lim = a.nk - j0;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kr = 8 * (r >> 2) + 4 * hi + (r & 3);
+            if (kr >= lim) s0[r] = -INFINITY;
+            if (32 + kr >= lim) s1[r] = -INFINITY;
+          }
+        }
+        float mx = s0[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s0[r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
+        mx = wave_swap32_max(mx);
+        const float mxs = mx * a.scale_log2;
+        const bool need = !(mxs <= m_run + 8.0f);
+        if (__any(need)) {
+          const float m_new = fmaxf(m_run, mxs);
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
+          l_run *= alpha;
+          m_run = m_new;
+        }
+        const float c = a.scale_log2;
+        f32x16_t p0, p1;
+        float ls = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          p0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], c, -m_run));
+          p1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], c, -m_run));
+          ls += p0[r] + p1[r];
+        }
+        l_run += ls;
+        bf16x8_t pf[4];
+        pf[0] = __builtin_convertvector(p0.lo, bf16x8_t);
+        pf[1] = __builtin_convertvector(p0.hi, bf16x8_t);
+        pf[2] = __builtin_convertvector(p1.lo, bf16x8_t);
+        pf[3] = __builtin_convertvector(p1.hi, bf16x8_t);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(
+                Vs + (32 * db + l32) * C::VSTR + (16 * kk + 8 * hi) * 2);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], o[db], 0, 0, 0);
+          }
+        }
+      }
+      if (more) store_tile(st ^ 1);
+      __syncthreads();
+    }
+
+    // epilogue: normalise, LSE (natural log), write final output or a partial
+    if (wave_rows) {
+      const float l_tot = wave_swap32_sum(l_run);
+      const float inv = 1.0f / l_tot;
+      const float lse_val = (m_run + log2f(l_tot)) * kLn2;
+      const int row = q0 + l32;
+      const bool whole = (t0 == 0) && (t1 == a.T);
+      if (row < a.n) {
+        if (whole) {
+          __bf16* op = static_cast<__bf16*>(a.o) + ((int64_t)row * a.H + h) * D;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              f32x4_t v4 = {o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+              v4 *= inv;
+              *reinterpret_cast<bf16x4_t*>(op + 32 * db + 8 * g + 4 * hi) =
+                  __builtin_convertvector(v4, bf16x4_t);
+            }
+          if (hi == 0 && a.lse) a.lse[(int64_t)h * a.n + row] = lse_val;
+        } else {
+          const int64_t jslot = (int64_t)w - first_wg_of((int64_t)u * a.T, I, a.P);
+          const int64_t prow = ((int64_t)u * a.jmax + jslot) * C::BM + wave * 32 + l32;
+          float* pp = a.part_o + prow * D;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              f32x4_t v4 = {o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+              v4 *= inv;
+              *reinterpret_cast<f32x4_t*>(pp + 32 * db + 8 * g + 4 * hi) = v4;
+            }
+          if (hi == 0) a.part_lse[prow] = lse_val;
+        }
+      }
+    }
+    it += t1 - t0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 attention on the vector ALUs (the fp32 configuration is small; this
+// kernel aims at exact agreement rather than throughput).
+// Work group: 128 threads, BM = 64 rows, two threads per row each owning half
+// of the head dimension; key tiles of 32 in LDS.
+template <int D>
+__global__ __launch_bounds__(128) void attn_f32_kernel(const AttnArgs a) {
+  constexpr int BM = 64, BN = 32, NT = 128, HALF = D / 2;
+  constexpr int CPR = D / 4;               // float4 per row
+  constexpr int NCH = BN * CPR / NT;       // float4 loads per thread per tile (K and V each)
+  __shared__ __attribute__((aligned(16))) float Ks[BN][D];
+  __shared__ __attribute__((aligned(16))) float Vs[BN][D];
+
+  const int tid = threadIdx.x;
+  const int rloc = tid >> 1, half = tid & 1;
+  const int w = logical_wg(a);
+  const int64_t I = (int64_t)a.units * a.T;
+  int64_t it = range_begin(w, I, a.P);
+  const int64_t it_end = range_begin(w + 1, I, a.P);
+
+  while (it < it_end) {
+    const int u = (int)(it / a.T);
+    const int t0 = (int)(it - (int64_t)u * a.T);
+    const int t1 = (int)((it_end - it) < (int64_t)(a.T - t0) ? t0 + (it_end - it) : a.T);
+    const int h = u / a.QT, qt = u - h * a.QT;
+    const int row = qt * BM + rloc;
+
+    float q[HALF], o[HALF];
+    {
+      const float* qp = static_cast<const float*>(a.q) + ((int64_t)min(row, a.n - 1) * a.H + h) * D +
+                        half * HALF;
+#pragma unroll
+      for (int c = 0; c < HALF; c += 4) {
+        f32x4_t v = *reinterpret_cast<const f32x4_t*>(qp + c);
+        q[c] = v[0], q[c + 1] = v[1], q[c + 2] = v[2], q[c + 3] = v[3];
+      }
+#pragma unroll
+      for (int c = 0; c < HALF; ++c) o[c] = 0.f;
+    }
+    float m_run = -INFINITY, l_run = 0.f;
+    int ri = 0;
+    const HeadSrc ksrc = head_src(a.kc, a.kcur, a, h, D, 4, 4);
+    const HeadSrc vsrc = head_src(a.vc, a.vcur, a, h, D, 4, 4);
+
+    for (int tile = t0; tile < t1; ++tile) {
+      const int j0 = tile * BN;
+      ri = advance_run(a, ri, j0);
+      int jr[NCH], cr[NCH];
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        jr[i] = j0 + (tid + NT * i) / CPR;
+        cr[i] = (tid + NT * i) % CPR;
+      }
+      // every thread's chunks share one column: NT is a multiple of CPR
+      uint4 kv[NCH], vv[NCH];
+      load_rows<NCH, BN>(a, ksrc, D, 4, 4, j0, ri, jr, cr[0] * 16, kv);
+      load_rows<NCH, BN>(a, vsrc, D, 4, 4, j0, ri, jr, cr[0] * 16, vv);
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int r = (tid + NT * i) / CPR;
+        *reinterpret_cast<uint4*>(&Ks[r][4 * cr[i]]) = kv[i];
+        *reinterpret_cast<uint4*>(&Vs[r][4 * cr[i]]) = vv[i];
+      }
+      __syncthreads();
+
+      float s[BN];
+#pragma unroll
+      for (int j = 0; j < BN; ++j) {
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < HALF; ++c) acc = fmaf(q[c], Ks[j][half * HALF + c], acc);
+        acc += __shfl_xor(acc, 1);
+        s[j] = (j0 + j < a.nk) ? acc * a.scale_log2 : -INFINITY;
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int j = 1; j < BN; ++j) mx = fmaxf(mx, s[j]);
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int c = 0; c < HALF; ++c) o[c] *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int j = 0; j < BN; ++j) {
+        const float p = exp2f(s[j] - m_run);
+        l_run += p;
+#pragma unroll
+        for (int c = 0; c < HALF; ++c) o[c] = fmaf(p, Vs[j][half * HALF + c], o[c]);
+      }
+      __syncthreads();
+    }
+
+    if (row < a.n) {
+      const float inv = 1.0f / l_run;
+      const float lse_val = (m_run + log2f(l_run)) * kLn2;
+      const bool whole = (t0 == 0) && (t1 == a.T);
+      float* dst;
+      if (whole) {
+        dst = static_cast<float*>(a.o) + ((int64_t)row * a.H + h) * D + half * HALF;
+        if (half == 0 && a.lse) a.lse[(int64_t)h * a.n + row] = lse_val;
+      } else {
+        const int64_t jslot = (int64_t)w - first_wg_of((int64_t)u * a.T, I, a.P);
+        const int64_t prow = ((int64_t)u * a.jmax + jslot) * BM + rloc;
+        dst = a.part_o + prow * D + half * HALF;
+        if (half == 0) a.part_lse[prow] = lse_val;
+      }
+#pragma unroll
+      for (int c = 0; c < HALF; c += 4) {
+        f32x4_t v = {o[c] * inv, o[c + 1] * inv, o[c + 2] * inv, o[c + 3] * inv};
+        *reinterpret_cast<f32x4_t*>(dst + c) = v;
+      }
+    }
+    it += t1 - t0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Log-sum-exp merge of the segments of every split unit:
+//   M = max_g LSE_g, w_g = exp(LSE_g - M) (0 for LSE_g = -inf),
+//   O = sum_g w_g O_g / sum_g w_g, LSE = M + ln sum_g w_g.
+// One work group covers 256 / (D/4) rows of one unit; each thread four dims.
+template <int D, typename OutT>
+__global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
+  constexpr int TPR = D / 4, RPB = 256 / TPR;
+  const int blocks_per_unit = (a.bm + RPB - 1) / RPB;
+  const int u = blockIdx.x / blocks_per_unit;
+  const int rb = blockIdx.x - u * blocks_per_unit;
+  const int64_t I = (int64_t)a.units * a.T;
+  const int64_t w0 = first_wg_of((int64_t)u * a.T, I, a.P);
+  const int64_t w1 = first_wg_of((int64_t)(u + 1) * a.T - 1, I, a.P);
+  const int pieces = (int)(w1 - w0 + 1);
+  if (pieces <= 1) return;  // written whole by the attention kernel
+  const int rloc = rb * RPB + threadIdx.x / TPR;
+  const int c4 = (threadIdx.x % TPR) * 4;
+  if (rloc >= a.bm) return;
+  const int h = u / a.QT, qt = u - h * a.QT;
+  const int row = qt * a.bm + rloc;
+  if (row >= a.n) return;
+  float M = -INFINITY;
+  for (int j = 0; j < pieces; ++j)
+    M = fmaxf(M, a.part_lse[((int64_t)u * a.jmax + j) * a.bm + rloc]);
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (M != -INFINITY) {
+    for (int j = 0; j < pieces; ++j) {
+      const int64_t prow = ((int64_t)u * a.jmax + j) * a.bm + rloc;
+      const float lj = a.part_lse[prow];
+      const float wj = (lj == -INFINITY) ? 0.f : expf(lj - M);
+      wsum += wj;
+      const f32x4_t oj = *reinterpret_cast<const f32x4_t*>(a.part_o + prow * D + c4);
+      acc += wj * oj;
+    }
+  }
+  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  acc *= inv;
+  OutT* op = static_cast<OutT*>(a.o) + ((int64_t)row * a.H + h) * D + c4;
+  if constexpr (sizeof(OutT) == 2) {
+    *reinterpret_cast<bf16x4_t*>(op) = __builtin_convertvector(acc, bf16x4_t);
+  } else {
+    *reinterpret_cast<f32x4_t*>(op) = acc;
+  }
+  if (c4 == 0 && a.lse) a.lse[(int64_t)h * a.n + row] = (M == -INFINITY) ? M : M + logf(wsum);
+}
+
+// ---------------------------------------------------------------------------
+// Fused K/V append: [n][H][d] -> the block's [H][n][d] rows (stride (S+R)*n*d
+// between heads), converting to the cache dtype. blockIdx.y selects K or V.
+// Each thread moves 8 elements.
+template <int D>
+__global__ __launch_bounds__(256) void append_copy_kernel(const AppendArgs a, int es) {
+  constexpr int G = D / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)a.n * a.H * G;
+  if (idx >= total) return;
+  const int g = (int)(idx % G);
+  const int64_t rh = idx / G;
+  const int h = (int)(rh % a.H);
+  const int r = (int)(rh / a.H);
+  const bool isv = blockIdx.y == 1;
+  const char* src = static_cast<const char*>(isv ? a.v : a.k) + (rh * D + g * 8) * es;
+  char* dst = static_cast<char*>(isv ? a.vdst : a.kdst) +
+              ((int64_t)h * a.head_stride_elems + (int64_t)r * D + g * 8) * es;
+  if (es == 2) {
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+  } else {
+    const uint4* s4 = reinterpret_cast<const uint4*>(src);
+    uint4* d4 = reinterpret_cast<uint4*>(dst);
+    d4[0] = s4[0];
+    d4[1] = s4[1];
+  }
+}
+
+// bf16 -> OCP e4m3 with the head's scale: code = round_to_nearest_even(x / s),
+// saturated to +-448 (NaN stays NaN).
+template <int D>
+__global__ __launch_bounds__(256) void append_fp8_kernel(const AppendArgs a) {
+  constexpr int G = D / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)a.n * a.H * G;
+  if (idx >= total) return;
+  const int g = (int)(idx % G);
+  const int64_t rh = idx / G;
+  const int h = (int)(rh % a.H);
+  const int r = (int)(rh / a.H);
+  const bool isv = blockIdx.y == 1;
+  const float s = isv ? a.v_scale[h] : a.k_scale[h];
+  const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(
+      static_cast<const __bf16*>(isv ? a.v : a.k) + rh * D + g * 8);
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float t = (float)x[i] / s;
+    y[i] = (fabsf(t) > 448.0f) ? copysignf(448.0f, t) : t;
+  }
+  int lo = 0, hi = 0;
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], lo, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], hi, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+  unsigned char* dst = static_cast<unsigned char*>(isv ? a.vdst : a.kdst) +
+                       ((int64_t)h * a.head_stride_elems + (int64_t)r * D + g * 8);
+  *reinterpret_cast<uint2*>(dst) = make_uint2((unsigned)lo, (unsigned)hi);
+}
+
+template <int D>
+int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
+  switch (p.kern) {
+    case Kern::BF16:
+      hipLaunchKernelGGL(attn_bf16_kernel<D>, dim3(p.wgs), dim3(256), 0, s, a);
+      break;
+    case Kern::F32:
+      hipLaunchKernelGGL(attn_f32_kernel<D>, dim3(p.wgs), dim3(128), 0, s, a);
+      break;
+    default:
+      return -1;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return (int)e;
+  if (p.merge) {
+    MergeArgs m;
+    m.part_o = a.part_o;
+    m.part_lse = a.part_lse;
+    m.o = a.o;
+    m.lse = a.lse;
+    m.n = a.n;
+    m.H = a.H;
+    m.T = a.T;
+    m.QT = a.QT;
+    m.units = a.units;
+    m.P = a.P;
+    m.jmax = a.jmax;
+    m.bm = p.bm;
+    constexpr int RPB = 256 / (D / 4);
+    const int blocks = a.units * ((p.bm + RPB - 1) / RPB);
+    if (p.kern == Kern::F32)
+      hipLaunchKernelGGL((merge_kernel<D, float>), dim3(blocks), dim3(256), 0, s, m);
+    else
+      hipLaunchKernelGGL((merge_kernel<D, __bf16>), dim3(blocks), dim3(256), 0, s, m);
+    e = hipGetLastError();
+    if (e != hipSuccess) return (int)e;
+  }
+  return 0;
+}
+
+}  // namespace
+
+int launch_attention(const Plan& p, const AttnArgs& a, int head_dim, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.kern == Kern::FP8) return -1;
+  if (head_dim == 64) return launch_attention_d<64>(p, a, s);
+  if (head_dim == 128) return launch_attention_d<128>(p, a, s);
+  return -1;
+}
+
+int launch_append(bca_dtype in, bca_dtype kv, int head_dim, const AppendArgs& a, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t total = (int64_t)a.n * a.H * (head_dim / 8);
+  const dim3 grid((unsigned)((total + 255) / 256), 2);
+  if (kv == BCA_FP8_E4M3) {
+    if (head_dim != 128 || in != BCA_BF16) return -1;
+    hipLaunchKernelGGL(append_fp8_kernel<128>, grid, dim3(256), 0, s, a);
+  } else {
+    const int es = kv == BCA_F32 ? 4 : 2;
+    if (head_dim == 64)
+      hipLaunchKernelGGL(append_copy_kernel<64>, grid, dim3(256), 0, s, a, es);
+    else
+      hipLaunchKernelGGL(append_copy_kernel<128>, grid, dim3(256), 0, s, a, es);
+  }
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? 0 : (int)e;
+}
+
+int device_compute_units() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return cus;
+}
+
+}  // namespace bca

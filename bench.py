@@ -1,0 +1,242 @@
+"""Benchmark of block-causal ring-KV chunk attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1|2|3|4]
+
+One step is one chunk of the chunk-wise autoregressive loop: for every denoise
+step and every layer one bca_attend (the chunk's queries over the current
+chunk plus the visible ring chunks), then one bca_append_chunk per layer that
+writes the chunk's K/V into its ring slot. Each layer has its own cache, so
+the K/V reads of a step come from HBM, not from the 256 MB Infinity Cache.
+
+Workloads (synthetic inputs, random values of the stated shapes):
+  1  WanToFight-shaped bf16: 12 heads, d 128, 1536 tokens per chunk, window of
+     the current + previous 2 chunks (4608 keys), ring of 2 slots, 30 layers x
+     4 denoise steps per chunk. The default and the reported line.
+  2  Matrix-Game-4.0-shaped bf16: 24 heads, d 128, 405 tokens per chunk,
+     reference chunk + last 20 chunks + current (8910 keys), 4 segments merged
+     by log-sum-exp, 30 layers x 1 step.
+  3  workload 1 streamed over 64 chunks (steps = 64): sustained time per chunk.
+  4  workload 2 with an fp8-e4m3 K/V cache (per-head scales).
+
+Prints one JSON line. `value` is algorithmic attention TFLOP/s over the whole
+step (4*H*n*N_k*d per chunk-layer, appends included in the time).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "block-causal attention TFLOP/s & µs per chunk-layer; % of MFMA peak"
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}  # MI355X dense MFMA, published
+PEAK_HBM_GBS = 8000.0
+
+CONFIGS = {
+    1: dict(workload="wantofight_bf16_chunk", H=12, d=128, n=1536, S=2, W=2, R=0, G=0, L=30,
+            steps_per_chunk=4, kv="bf16"),
+    2: dict(workload="matrixgame4_bf16_chunk", H=24, d=128, n=405, S=20, W=20, R=1, G=4, L=30,
+            steps_per_chunk=1, kv="bf16"),
+    3: dict(workload="wantofight_bf16_stream64", H=12, d=128, n=1536, S=2, W=2, R=0, G=0, L=30,
+            steps_per_chunk=4, kv="bf16"),
+    4: dict(workload="matrixgame4_fp8cache_chunk", H=24, d=128, n=405, S=20, W=20, R=1, G=4,
+            L=30, steps_per_chunk=1, kv="fp8"),
+}
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def gen(shape, g, outliers=False):
+    import torch
+    z = torch.randn(shape, generator=g, device="cuda", dtype=torch.float32)
+    if outliers:
+        u = torch.rand(shape, generator=g, device="cuda", dtype=torch.float32)
+        z = torch.where(u < 0.01, 8.0 * torch.sign(z), z)
+    return z.to(torch.bfloat16)
+
+
+def cpu_baseline(cache, cfg, q0, k0, v0, t):
+    """The oracle, untouched, on a bounded sample of the same workload: the
+    chunk-layer of layer 0 restricted to the first few heads (heads are
+    independent), scaled until the sample takes about 10 s of CPU work."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    H, d, n, W = cfg["H"], cfg["d"], cfg["n"], cfg["W"]
+    K, V = cache.blocks(0)
+    hist = {}
+    for s in range(cfg["S"]):
+        c = cache.slot_chunk(0, s)
+        if c >= 0:
+            hist[c] = (K[:, s].float().cpu().numpy(), V[:, s].float().cpu().numpy())
+    ref = None
+    if cfg["R"]:
+        ref = (K[:, cfg["S"]].float().cpu().numpy(), V[:, cfg["S"]].float().cpu().numpy())
+    if cfg["kv"] == "fp8":
+        # the fp8 cache holds codes; the oracle attends over the dequantised values
+        dec = oracle.e4m3_decode(np.arange(256, dtype=np.uint8))
+        scale = 8.0 / 448.0
+        hist = {c: (dec[K[:, s].cpu().numpy()] * scale, dec[V[:, s].cpu().numpy()] * scale)
+                for c, s in ((c, c % cfg["S"]) for c in hist)}
+        ref = (dec[K[:, cfg["S"]].cpu().numpy()] * scale, dec[V[:, cfg["S"]].cpu().numpy()] * scale)
+    qn, kn, vn = (x.float().cpu().numpy() for x in (q0, k0, v0))
+    n_vis_blocks = 1 + sum(1 for c in hist if t - W <= c <= t - 1) + (1 if cfg["R"] else 0)
+    nk = n_vis_blocks * n
+
+    def run(hs):
+        h_hist = {c: (kv[0][:hs].transpose(1, 0, 2), kv[1][:hs].transpose(1, 0, 2))
+                  for c, kv in hist.items()}
+        h_ref = None if ref is None else (ref[0][:hs].transpose(1, 0, 2),
+                                          ref[1][:hs].transpose(1, 0, 2))
+        t0 = time.perf_counter()
+        oracle.attend(qn[:, :hs], kn[:, :hs], vn[:, :hs], h_hist, t=t, W=W,
+                      scale=1 / math.sqrt(d), ref=h_ref, use_ref=bool(cfg["R"]))
+        return time.perf_counter() - t0
+
+    hs = 1
+    dt = run(hs)
+    if dt < 3.0 and H > 1:
+        hs = min(H, max(2, int(math.ceil(10.0 / max(dt, 1e-3)))))
+        dt = run(hs)
+    flops = 4.0 * hs * n * nk * d
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"layer 0 chunk-layer, {hs} of {H} heads x {n} query rows x {nk} keys "
+                      f"(fp64 dense-mask oracle, {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", type=int, default=1, choices=sorted(CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import attention_bca_attend_amd as bca
+
+    cfg = dict(CONFIGS[args.config])
+    steps = args.steps if args.steps is not None else (64 if args.config == 3 else 5)
+    H, d, n, S, W, R, G, L = (cfg[k] for k in ("H", "d", "n", "S", "W", "R", "G", "L"))
+    spc = cfg["steps_per_chunk"]
+    fp8 = cfg["kv"] == "fp8"
+    torch.cuda.set_device(0)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20261202)
+
+    log(f"config {args.config}: {cfg}")
+    cache = bca.Cache(L, H, d, n, S, has_ref=bool(R), kv_dtype=cfg["kv"])
+    if fp8:
+        for l in range(L):
+            cache.set_kv_scales(l, [8.0 / 448.0] * H, [8.0 / 448.0] * H)
+    # per-layer Q/K/V of the current chunk, resident in HBM
+    Q = [gen((n, H, d), g) for _ in range(L)]
+    Kc = [gen((n, H, d), g, outliers=fp8) for _ in range(L)]
+    Vc = [gen((n, H, d), g, outliers=fp8) for _ in range(L)]
+    O = torch.empty((n, H, d), dtype=torch.bfloat16, device="cuda")
+    LSE = torch.empty((H, n), dtype=torch.float32, device="cuda")
+    # fill the ring (chunks 0..S-1) and the reference
+    for l in range(L):
+        if R:
+            cache.append_chunk(l, 0, gen((n, H, d), g, fp8), gen((n, H, d), g, fp8), is_ref=True)
+        for c in range(S):
+            cache.append_chunk(l, c, gen((n, H, d), g, fp8), gen((n, H, d), g, fp8))
+    torch.cuda.synchronize()
+    t_chunk = S
+    spec0 = cache.spec(t_chunk, W, use_ref=bool(R), num_segments=G)
+    ws = cache.workspace(spec0)
+    plan = cache.plan(0, spec0)
+    nk = plan["visible_keys"]
+    flop_cl = 4.0 * H * n * nk * d
+    log(f"plan: {plan['workgroups']} work groups, {plan['kv_tiles']} key tiles, "
+        f"max segments {plan['max_pieces']}, merge {plan['merge']}, N_k {nk}")
+
+    events = []
+
+    def run_chunk(t, record):
+        spec = cache.spec(t, W, use_ref=bool(R), num_segments=G)
+        for _ in range(spc):
+            for l in range(L):
+                if record:
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                cache.attend(l, Q[l], Kc[l], Vc[l], spec, out=O, lse=LSE, workspace=ws)
+                if record:
+                    e1.record()
+                    events.append((e0, e1))
+        for l in range(L):
+            cache.append_chunk(l, t, Kc[l], Vc[l])
+
+    for _ in range(args.warmup):
+        run_chunk(t_chunk, False)
+        t_chunk += 1
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    per_chunk = []
+    start.record()
+    for i in range(steps):
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record()
+        run_chunk(t_chunk, True)
+        c1.record()
+        per_chunk.append((c0, c1))
+        t_chunk += 1
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / steps
+    attend_us = sum(a.elapsed_time(b) for a, b in events) / len(events) * 1e3
+    chunk_ms = [a.elapsed_time(b) for a, b in per_chunk]
+    n_attend = spc * L
+    flops_step = n_attend * flop_cl
+    tflops = flops_step / (ms_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[cfg["kv"]]
+    achieved = flop_cl / (attend_us * 1e-6) / 1e12
+    log(f"{steps} steps: {ms_step:.3f} ms/step, attend {attend_us:.2f} us, "
+        f"{tflops:.1f} TFLOP/s over the step, {achieved:.1f} TFLOP/s per attend")
+
+    result = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if not fp8 else "bf16 q / fp8-e4m3 kv", "data": "synthetic",
+        "config": {"workload": cfg["workload"], "heads": H, "head_dim": d, "chunk_tokens": n,
+                   "visible_keys": nk, "ring_slots": S, "history": W, "reference": bool(R),
+                   "segments": G if G else "auto", "layers": L,
+                   "denoise_steps_per_chunk": spc, "batch": 1},
+        "us_per_chunk_layer": round(ms_step * 1e3 / n_attend, 3),
+        "attend_us": round(attend_us, 3),
+        "pct_mfma_peak": round(100.0 * achieved / peak, 2),
+        "chunk_ms_min_max": [round(min(chunk_ms), 4), round(max(chunk_ms), 4)],
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "attn_bf16_kernel" + ("+merge_kernel" if plan["merge"] else "")},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(cache, cfg, Q[0], Kc[0], Vc[0], t_chunk)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

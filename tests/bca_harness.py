@@ -1,0 +1,85 @@
+"""Shared helpers of the GPU tests: seeded chunk sequences driven through the
+C ABI, and the oracle run on the same rounded inputs."""
+from __future__ import annotations
+
+import math
+import sys
+import time
+
+import numpy as np
+
+import oracle
+import synth
+
+TOL = {"fp32": 1e-5, "bf16": 1e-2, "fp8": 5e-2}
+
+
+def log(msg: str) -> None:
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x: np.ndarray, dtype: str):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    t = t.to(torch.bfloat16) if dtype in ("bf16", "fp8") else t
+    return t.cuda()
+
+
+def to_np(t) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+class Sequence:
+    """Drives one cache layer through chunk steps and keeps the committed
+    history the oracle needs (every chunk appended, keyed by id)."""
+
+    def __init__(self, cache, H, d, n, dtype, seed_layer=0, outlier_frac=0.0):
+        self.cache = cache
+        self.H, self.d, self.n = H, d, n
+        self.dtype = dtype  # "fp32" | "bf16" | "fp8" (bf16 inputs, fp8 cache)
+        self.in_dtype = "fp32" if dtype == "fp32" else "bf16"
+        self.seed_layer = seed_layer
+        self.outlier_frac = outlier_frac
+        self.history = {}
+        self.ref = None
+
+    def chunk(self, t, step=0):
+        return synth.qkv(self.n, self.H, self.d, self.seed_layer, t, step, dtype=self.in_dtype,
+                         outlier_frac=self.outlier_frac)
+
+    def append(self, layer, t, k, v, is_ref=False):
+        self.cache.append_chunk(layer, t, to_dev(k, self.dtype), to_dev(v, self.dtype),
+                                is_ref=is_ref)
+        if is_ref:
+            self.ref = (k.astype(np.float64), v.astype(np.float64))
+        else:
+            self.history[t] = (k.astype(np.float64), v.astype(np.float64))
+
+    def attend(self, layer, t, q, k, v, W, use_ref=False, G=0, scale=None):
+        spec = self.cache.spec(t, W, use_ref=use_ref, num_segments=G, scale=scale)
+        o, lse = self.cache.attend(layer, to_dev(q, self.dtype), to_dev(k, self.dtype),
+                                   to_dev(v, self.dtype), spec)
+        return to_np(o), to_np(lse), spec
+
+    def expected(self, t, q, k, v, W, use_ref=False, scale=None, history=None):
+        scale = 1.0 / math.sqrt(self.d) if scale is None else scale
+        hist = self.history if history is None else history
+        return oracle.attend(q, k, v, hist, t=t, W=W, scale=scale, ref=self.ref,
+                             use_ref=use_ref)
+
+
+def max_err(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    if a.shape != b.shape:
+        raise AssertionError(f"shape {a.shape} != {b.shape}")
+    both_nan = np.isnan(a) & np.isnan(b)
+    d = np.where(both_nan, 0.0, np.abs(a - b))
+    return float(np.nanmax(np.where(np.isnan(d), np.inf, d))) if d.size else 0.0
+
+
+def assert_close(got_o, got_lse, exp_o, exp_lse, tol, what=""):
+    eo, el = max_err(got_o, exp_o), max_err(got_lse, exp_lse)
+    log(f"{what}: max|dO| = {eo:.3e}, max|dLSE| = {el:.3e} (tol {tol})")
+    assert eo <= tol and el <= tol, f"{what}: O err {eo}, LSE err {el} > {tol}"

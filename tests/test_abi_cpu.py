@@ -1,0 +1,266 @@
+"""The C-ABI library on the host (no GPU): exports, descriptor arithmetic, the
+slot table, window resolution, work planning and every error path that is
+decided before a kernel is launched."""
+import ctypes
+import itertools
+import os
+import re
+
+import pytest
+
+import attention_bca_attend_amd as bca
+from attention_bca_attend_amd import BcaError
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bca.h")
+
+# a 256-byte aligned stand-in for device memory: creating a cache never touches it
+FAKE = 1 << 40
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bca_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    lib = ctypes.CDLL(bca.LIB_PATH)
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def desc(L=2, H=2, d=64, n=16, S=2, R=0, dt=bca.F32):
+    return bca.bca_cache_desc(L, H, d, n, S, R, dt)
+
+
+def make(**kw):
+    dsc = desc(**kw)
+    nb = bca.bca_cache_bytes(dsc)
+    return bca.bca_cache_create(dsc, FAKE, nb), nb
+
+
+def test_cache_bytes_formula():
+    # [L][K|V][H][S+R][n][d]
+    assert bca.bca_cache_bytes(desc(L=1, H=2, d=64, n=16, S=2, dt=bca.F32)) == 2 * 2 * 2 * 16 * 64 * 4
+    assert bca.bca_cache_bytes(desc(L=30, H=12, d=128, n=1536, S=2, dt=bca.BF16)) == \
+        30 * 2 * 12 * 2 * 1536 * 128 * 2
+    assert bca.bca_cache_bytes(desc(L=30, H=24, d=128, n=405, S=20, R=1, dt=bca.FP8_E4M3)) == \
+        30 * 2 * 24 * 21 * 405 * 128
+
+
+@pytest.mark.parametrize("field,value", [("num_layers", 0), ("num_heads", 0), ("head_dim", 96),
+                                         ("chunk_tokens", 0), ("ring_slots", 0),
+                                         ("ring_slots", 63), ("has_ref", 2), ("kv_dtype", 7)])
+def test_invalid_descriptor(field, value):
+    d = desc()
+    setattr(d, field, value)
+    assert bca.bca_cache_bytes(d) == 0
+    with pytest.raises(BcaError) as e:
+        bca.bca_cache_create(d, FAKE, 1 << 30)
+    assert e.value.status == -1
+
+
+def test_fp8_descriptor_limits():
+    assert bca.bca_cache_bytes(desc(H=65, d=128, dt=bca.FP8_E4M3)) == 0
+    assert bca.bca_cache_bytes(desc(H=8, d=64, dt=bca.FP8_E4M3)) == 0
+    assert bca.bca_cache_bytes(desc(H=8, d=128, dt=bca.FP8_E4M3)) > 0
+
+
+def test_create_checks_memory():
+    d = desc()
+    nb = bca.bca_cache_bytes(d)
+    for ptr, size in ((0, nb), (FAKE + 16, nb), (FAKE, nb - 1)):
+        with pytest.raises(BcaError) as e:
+            bca.bca_cache_create(d, ptr, size)
+        assert e.value.status == -1
+    h = bca.bca_cache_create(d, FAKE, nb)
+    assert bca.bca_cache_slot_chunk(h, 0, 0) == -1
+    bca.bca_cache_destroy(h)
+
+
+def test_slot_table_hooks_and_plan():
+    h, _ = make(S=3, R=1, dt=bca.BF16, d=128, n=100, H=3)
+    for s in range(4):
+        assert bca.bca_cache_slot_chunk(h, 1, s) == -1
+    bca.bca_cache_set_slot_chunk(h, 1, 0, 6)
+    bca.bca_cache_set_slot_chunk(h, 1, 1, 7)
+    bca.bca_cache_set_slot_chunk(h, 1, 2, 5)
+    bca.bca_cache_set_slot_chunk(h, 1, 3, 0)  # reference block
+    with pytest.raises(BcaError):
+        bca.bca_cache_set_slot_chunk(h, 1, 0, 7)  # 7 mod 3 != 0
+    spec = bca.bca_window_spec(8, 2, 1, 1, 0.1)
+    p = bca.bca_attend_plan(h, 1, spec)
+    assert p["visible_blocks"] == [0, 1, 3, -1]  # slots with 6 and 7, the reference, current
+    assert p["visible_chunk_ids"] == [6, 7, 0, -1]
+    assert p["visible_keys"] == 400
+    assert p["q_tiles"] == 1 and p["units"] == 3
+    assert p["workgroups"] == 3 and p["max_pieces"] == 1 and not p["merge"]
+    # without the reference
+    p = bca.bca_attend_plan(h, 1, bca.bca_window_spec(8, 2, 0, 1, 0.1))
+    assert p["visible_blocks"] == [0, 1, -1]
+    # other layers are empty
+    p = bca.bca_attend_plan(h, 0, bca.bca_window_spec(8, 2, 1, 1, 0.1))
+    assert p["visible_blocks"] == [-1]
+    bca.bca_cache_destroy(h)
+
+
+def _ring_model(S, commits):
+    """slot -> chunk id after appending `commits` in order (id mod S, newest wins)."""
+    ring = {}
+    for c in commits:
+        ring[c % S] = c
+    return ring
+
+
+def test_window_resolution_brute_force():
+    # Every ring of S <= 4 slots, every commit sequence of non-decreasing ids
+    # (with repeats) drawn from 0..7 of length <= 4, every W <= S and t <= 10: the
+    # visible set equals the committed ids in [t-W, t-1] whenever the window is
+    # resident, and the call is refused otherwise.
+    checked = 0
+    for S in range(1, 5):
+        h, _ = make(S=S, n=16, H=1, d=64)
+        seqs = [()]
+        for length in range(1, 5):
+            seqs += [s for s in itertools.combinations_with_replacement(range(8), length)]
+        for seq in seqs:
+            ring = _ring_model(S, seq)
+            for s in range(S):
+                bca.bca_cache_set_slot_chunk(h, 0, s, ring.get(s, -1))
+            newest = max(seq) if seq else -1
+            committed = set(seq)
+            for W in range(0, S + 1):
+                for t in range(0, 11):
+                    spec = bca.bca_window_spec(t, W, 0, 1, 0.125)
+                    if newest >= 0 and newest >= t - W + S:
+                        with pytest.raises(BcaError) as e:
+                            bca.bca_attend_plan(h, 0, spec)
+                        assert e.value.status == -2
+                        continue
+                    p = bca.bca_attend_plan(h, 0, spec)
+                    got = sorted(c for c in p["visible_chunk_ids"] if c >= 0)
+                    want = sorted(c for c in committed if t - W <= c <= t - 1)
+                    assert got == want, (S, seq, W, t)
+                    assert p["visible_keys"] == 16 * (len(want) + 1)
+                    checked += 1
+        bca.bca_cache_destroy(h)
+    assert checked > 10000
+
+
+def test_segment_planning():
+    h, _ = make(S=20, R=1, dt=bca.BF16, d=128, n=405, H=24, L=1)
+    for c in range(20, 40):
+        bca.bca_cache_set_slot_chunk(h, 0, c % 20, c)
+    bca.bca_cache_set_slot_chunk(h, 0, 20, 0)
+    for G in (1, 2, 4, 7):
+        p = bca.bca_attend_plan(h, 0, bca.bca_window_spec(40, 20, 1, G, 0.088))
+        assert p["visible_keys"] == 22 * 405
+        assert p["kv_tiles"] == -(-22 * 405 // 64)
+        assert p["units"] == 24 * 4
+        assert p["workgroups"] == p["units"] * G
+        assert p["max_pieces"] == G and p["merge"] == (G > 1)
+        ws = bca.bca_attend_workspace_bytes(h, bca.bca_window_spec(40, 20, 1, G, 0.088))
+        assert ws >= p["workspace_bytes"]
+        if G > 1:
+            assert p["workspace_bytes"] >= p["units"] * G * 128 * 129 * 4
+    # automatic split: never more work groups than tile iterations
+    p = bca.bca_attend_plan(h, 0, bca.bca_window_spec(40, 20, 1, 0, 0.088))
+    assert 1 <= p["workgroups"] <= p["units"] * p["kv_tiles"]
+    bca.bca_cache_destroy(h)
+
+
+def test_workspace_covers_every_occupancy():
+    h, _ = make(S=2, dt=bca.BF16, d=128, n=1536, H=12, L=1)
+    spec = bca.bca_window_spec(5, 2, 0, 0, 0.088)
+    ws = bca.bca_attend_workspace_bytes(h, spec)
+    for fill in range(3):
+        for s in range(2):
+            bca.bca_cache_set_slot_chunk(h, 0, s, -1)
+        for c in range(5 - fill, 5):
+            bca.bca_cache_set_slot_chunk(h, 0, c % 2, c)
+        assert bca.bca_attend_plan(h, 0, spec)["workspace_bytes"] <= ws
+    bca.bca_cache_destroy(h)
+
+
+def test_append_errors_before_launch():
+    h, _ = make(S=2, R=0, dt=bca.BF16, d=128, H=2, n=16)
+    P = FAKE
+    cases = [
+        (dict(layer=2), -1), (dict(layer=-1), -1), (dict(chunk_id=-1), -1),
+        (dict(is_ref=1), -1), (dict(k=0), -1), (dict(v=P + 8), -1),
+        (dict(in_dtype=bca.F32), -4), (dict(in_dtype=9), -1),
+    ]
+    for over, status in cases:
+        args = dict(layer=0, chunk_id=3, is_ref=0, k=P, v=P, in_dtype=bca.BF16)
+        args.update(over)
+        with pytest.raises(BcaError) as e:
+            bca.bca_append_chunk(h, args["layer"], args["chunk_id"], args["is_ref"], args["k"],
+                                 args["v"], args["in_dtype"], 0)
+        assert e.value.status == status, over
+    # out of order: a smaller id than the newest
+    bca.bca_cache_set_slot_chunk(h, 0, 1, 5)
+    with pytest.raises(BcaError) as e:
+        bca.bca_append_chunk(h, 0, 4, 0, P, P, bca.BF16, 0)
+    assert e.value.status == -2
+    assert bca.bca_cache_slot_chunk(h, 0, 0) == -1 and bca.bca_cache_slot_chunk(h, 0, 1) == 5
+    bca.bca_cache_destroy(h)
+
+
+def test_attend_errors_before_launch():
+    h, _ = make(S=2, R=0, dt=bca.BF16, d=128, H=2, n=300)
+    P = FAKE
+
+    def call(spec=None, layer=0, q=P, k=P, v=P, dt=bca.BF16, o=P, lse=0, ws=0, wsb=0):
+        spec = spec or bca.bca_window_spec(2, 2, 0, 1, 0.1)
+        bca.bca_attend(h, layer, spec, q, k, v, dt, o, lse, ws, wsb, 0)
+
+    cases = [
+        (dict(layer=3), -1),
+        (dict(spec=bca.bca_window_spec(-1, 2, 0, 1, 0.1)), -1),
+        (dict(spec=bca.bca_window_spec(2, 3, 0, 1, 0.1)), -1),       # W > S
+        (dict(spec=bca.bca_window_spec(2, 2, 1, 1, 0.1)), -1),       # no reference block
+        (dict(spec=bca.bca_window_spec(2, 2, 0, 65, 0.1)), -1),
+        (dict(spec=bca.bca_window_spec(2, 2, 0, 1, float("nan"))), -1),
+        (dict(dt=bca.F32), -4), (dict(dt=bca.FP8_E4M3), -4),
+        (dict(q=0), -1), (dict(o=P + 2), -1),
+        (dict(spec=bca.bca_window_spec(2, 2, 0, 4, 0.1)), -3),       # needs a workspace
+        (dict(spec=bca.bca_window_spec(2, 2, 0, 4, 0.1), ws=P, wsb=16), -3),
+    ]
+    for over, status in cases:
+        with pytest.raises(BcaError) as e:
+            call(**over)
+        assert e.value.status == status, over
+    # residency: newest ring id 9 with S = 2 cannot serve query chunk 5
+    bca.bca_cache_set_slot_chunk(h, 0, 1, 9)
+    with pytest.raises(BcaError) as e:
+        call(spec=bca.bca_window_spec(5, 2, 0, 1, 0.1))
+    assert e.value.status == -2
+    assert "overwritten" in bca.bca_last_error()
+    bca.bca_cache_destroy(h)
+
+
+def test_fp8_scales_validation_and_reset():
+    h, _ = make(S=2, R=1, dt=bca.FP8_E4M3, d=128, H=3)
+    bca.bca_cache_set_slot_chunk(h, 0, 0, 4)
+    bca.bca_cache_set_slot_chunk(h, 0, 2, 0)
+    bca.bca_cache_set_kv_scales(h, 0, [0.5, 1.0, 2.0], [1.0, 1.0, 1.0])
+    # new scales empty the layer: stored codes used the old ones
+    assert bca.bca_cache_slot_chunk(h, 0, 0) == -1 and bca.bca_cache_slot_chunk(h, 0, 2) == -1
+    for bad in ([0.0, 1, 1], [float("inf"), 1, 1], [-1.0, 1, 1]):
+        with pytest.raises(BcaError):
+            bca.bca_cache_set_kv_scales(h, 0, bad, [1, 1, 1])
+    with pytest.raises(BcaError):
+        bca.bca_cache_set_kv_scales(h, 5, [1, 1, 1], [1, 1, 1])
+    bca.bca_cache_destroy(h)
+    h2, _ = make(S=2, dt=bca.BF16, d=128)
+    with pytest.raises(BcaError):
+        bca.bca_cache_set_kv_scales(h2, 0, [1, 1], [1, 1])
+    bca.bca_cache_destroy(h2)
+
+
+def test_status_strings():
+    for code, name in bca.STATUS.items():
+        assert bca.bca_status_string(code) == name

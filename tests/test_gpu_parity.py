@@ -1,0 +1,289 @@
+"""GPU path (through the C ABI) against the CPU oracle on the same seeded inputs.
+
+Bars: mask and ring-slot indexing exact; O and LSE max-abs <= 1e-5 (fp32),
+<= 1e-2 (bf16 with fp32 accumulation), <= 5e-2 (fp8 K/V cache).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from bca_harness import TOL, Sequence, assert_close, log, to_dev, to_np
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import attention_bca_attend_amd  # noqa: F401  (fails loudly when libbca.so is missing)
+    yield
+
+
+def new_cache(L, H, d, n, S, R=False, dtype="bf16"):
+    import attention_bca_attend_amd as bca
+    return bca.Cache(L, H, d, n, S, has_ref=R, kv_dtype=dtype)
+
+
+# ---------------------------------------------------------------------------
+# configuration 0: tiny fp32, H 2, d 64, n 16, W 2, ring of 2 slots, 6 chunks
+@pytest.mark.parametrize("G", [0, 1, 2, 4, 7])
+def test_cfg0_fp32_sequence(G):
+    H, d, n, S, W = 2, 64, 16, 2, 2
+    cache = new_cache(1, H, d, n, S, dtype="fp32")
+    seq = Sequence(cache, H, d, n, "fp32")
+    for t in range(6):
+        q, k, v = seq.chunk(t)
+        o, lse, spec = seq.attend(0, t, q, k, v, W, G=G)
+        eo, el = seq.expected(t, q, k, v, W)
+        assert_close(o, lse, eo, el, TOL["fp32"], f"cfg0 G={G} t={t}")
+        seq.append(0, t, k, v)
+        assert cache.slot_chunk(0, t % S) == t
+
+
+def test_cfg0_q_zero_lse_counts_visible_keys():
+    H, d, n, S, W = 2, 64, 16, 2, 2
+    cache = new_cache(1, H, d, n, S, dtype="fp32")
+    seq = Sequence(cache, H, d, n, "fp32")
+    for t in range(6):
+        _, k, v = seq.chunk(t)
+        o, lse, _ = seq.attend(0, t, np.zeros((n, H, d), np.float32), k, v, W)
+        n_vis = [16, 32, 48, 48, 48, 48][t]
+        assert np.abs(lse - math.log(n_vis)).max() <= 1e-6, t
+        seq.append(0, t, k, v)
+
+
+def test_cfg0_one_hot_probe_is_exact():
+    # V row of token r of chunk c is e_{16 (c mod 4) + r}; with Q = 0 the output is
+    # exactly 1/N_visible on visible columns and exactly 0 elsewhere.
+    H, d, n, S, W = 2, 64, 16, 3, 2  # S = W + 1: a stale chunk stays resident
+    cache = new_cache(1, H, d, n, S, dtype="fp32")
+    seq = Sequence(cache, H, d, n, "fp32")
+    for t in range(7):
+        _, k, _ = seq.chunk(t)
+        v = np.zeros((n, H, d), np.float32)
+        for r in range(n):
+            v[r, :, 16 * (t % 4) + r] = 1.0
+        o, _, _ = seq.attend(0, t, np.zeros((n, H, d), np.float32), k, v, W)
+        vis = list(range(max(0, t - W), t)) + [t]
+        want = np.zeros(d)
+        for c in vis:
+            want[16 * (c % 4):16 * (c % 4) + 16] = 1.0 / (n * len(vis))
+        for c in range(4):
+            cols = slice(16 * c, 16 * c + 16)
+            if want[16 * c] == 0.0:
+                assert np.all(o[:, :, cols] == 0.0), (t, c)
+            else:
+                assert np.abs(o[:, :, cols] - want[16 * c]).max() <= 1e-7, (t, c)
+        seq.append(0, t, k, v)
+
+
+# ---------------------------------------------------------------------------
+# bf16 shapes: ragged chunks, small chunks, both head dims, segments, reference
+BF16_CASES = [
+    # H, d, n, S, W, R, G, chunks
+    (2, 128, 100, 2, 2, False, 1, 4),
+    (3, 128, 200, 3, 2, False, 0, 5),
+    (2, 64, 130, 2, 1, False, 3, 4),
+    (1, 128, 16, 4, 4, True, 2, 6),
+    (2, 128, 1, 3, 3, False, 1, 5),
+    (2, 64, 64, 2, 2, True, 7, 4),
+    (4, 128, 405, 5, 5, True, 4, 7),
+    (2, 128, 257, 1, 0, False, 2, 3),
+]
+
+
+@pytest.mark.parametrize("H,d,n,S,W,R,G,chunks", BF16_CASES)
+def test_bf16_sequences(H, d, n, S, W, R, G, chunks):
+    cache = new_cache(1, H, d, n, S, R=R, dtype="bf16")
+    seq = Sequence(cache, H, d, n, "bf16", seed_layer=H * 1000 + n)
+    if R:
+        _, rk, rv = seq.chunk(10_000)
+        seq.append(0, 0, rk, rv, is_ref=True)
+    for t in range(chunks):
+        q, k, v = seq.chunk(t)
+        o, lse, _ = seq.attend(0, t, q, k, v, W, use_ref=R, G=G)
+        eo, el = seq.expected(t, q, k, v, W, use_ref=R)
+        assert_close(o, lse, eo, el, TOL["bf16"], f"bf16 H{H} d{d} n{n} S{S} W{W} R{R} G{G} t={t}")
+        seq.append(0, t, k, v)
+
+
+def test_bf16_segments_agree_with_each_other():
+    H, d, n, S, W = 2, 128, 300, 3, 3
+    cache = new_cache(1, H, d, n, S)
+    seq = Sequence(cache, H, d, n, "bf16", seed_layer=7)
+    for t in range(3):
+        _, k, v = seq.chunk(t)
+        seq.append(0, t, k, v)
+    q, k, v = seq.chunk(3)
+    eo, el = seq.expected(3, q, k, v, W)
+    outs = {}
+    for G in (1, 2, 4, 7, 0):
+        o, lse, _ = seq.attend(0, 3, q, k, v, W, G=G)
+        assert_close(o, lse, eo, el, TOL["bf16"], f"split G={G}")
+        outs[G] = (o, lse)
+    # a split only reorders sums: different G differ by rounding only
+    for G in (2, 4, 7, 0):
+        assert np.abs(outs[G][0] - outs[1][0]).max() <= 4e-3
+
+
+def test_window_invariance_under_nan_in_stale_slots():
+    # S = W + 1 keeps chunk t-W-1 resident; filling it (and the slot of a chunk
+    # committed as id t itself) with NaN must leave O and LSE bit-identical.
+    H, d, n, S, W = 2, 128, 96, 3, 2
+    cache = new_cache(2, H, d, n, S)
+    seq = Sequence(cache, H, d, n, "bf16", seed_layer=3)
+    for t in range(4):
+        _, k, v = seq.chunk(t)
+        seq.append(0, t, k, v)
+        seq.append(1, t, k, v)
+    q, k, v = seq.chunk(4)
+    o1, l1, _ = seq.attend(0, 4, q, k, v, W)
+    K, V = cache.blocks(0)
+    stale = 1 % S  # chunk 1 = t - W - 1 lives in slot 1
+    assert cache.slot_chunk(0, stale) == 1
+    K[:, stale].fill_(float("nan"))
+    V[:, stale].fill_(float("inf"))
+    # layer 1 and other heads do not matter either
+    K1, V1 = cache.blocks(1)
+    K1.fill_(float("nan"))
+    o2, l2, _ = seq.attend(0, 4, q, k, v, W)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    assert np.isfinite(o2).all()
+    # a visible chunk does change it
+    K[:, 3 % S].add_(1.0)
+    o3, _, _ = seq.attend(0, 4, q, k, v, W)
+    assert not np.array_equal(o1, o3)
+
+
+def test_deterministic():
+    H, d, n, S, W = 3, 128, 333, 2, 2
+    cache = new_cache(1, H, d, n, S)
+    seq = Sequence(cache, H, d, n, "bf16", seed_layer=5)
+    for t in range(2):
+        _, k, v = seq.chunk(t)
+        seq.append(0, t, k, v)
+    q, k, v = seq.chunk(2)
+    for G in (0, 3):
+        a = seq.attend(0, 2, q, k, v, W, G=G)
+        b = seq.attend(0, 2, q, k, v, W, G=G)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------------------
+# append: cache bytes are the input rows, bit for bit (fp8: the oracle's codes)
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_append_bytes_exact(dtype):
+    H, d, n, S = 3, 64 if dtype == "fp32" else 128, 50, 3
+    cache = new_cache(2, H, d, n, S, R=True, dtype=dtype)
+    seq = Sequence(cache, H, d, n, dtype, seed_layer=9)
+    for t in range(7):
+        _, k, v = seq.chunk(t)
+        seq.append(1, t, k, v)
+        K, V = cache.blocks(1)
+        torch.cuda.synchronize()
+        kk = K[:, t % S].float().cpu().numpy()  # [H][n][d]
+        vv = V[:, t % S].float().cpu().numpy()
+        assert np.array_equal(kk, k.transpose(1, 0, 2)) and np.array_equal(vv, v.transpose(1, 0, 2))
+        for s in range(S):
+            want = max([c for c in range(t + 1) if c % S == s], default=-1)
+            assert cache.slot_chunk(1, s) == want
+    _, rk, rv = seq.chunk(99)
+    seq.append(1, 5, rk, rv, is_ref=True)
+    K, _ = cache.blocks(1)
+    assert np.array_equal(K[:, S].float().cpu().numpy(), rk.transpose(1, 0, 2))
+    assert cache.slot_chunk(1, S) == 5
+    # layer 0 untouched (the buffer was never written: only slot ids matter)
+    assert all(cache.slot_chunk(0, s) == -1 for s in range(S))
+
+
+def test_append_fp8_codes_match_oracle_quantiser():
+    import oracle
+    H, d, n, S = 4, 128, 40, 2
+    cache = new_cache(1, H, d, n, S, R=True, dtype="fp8")
+    ks = [0.011 * (h + 1) for h in range(H)]
+    vs = [8.0 / 448.0 + 0.003 * h for h in range(H)]
+    cache.set_kv_scales(0, ks, vs)
+    seq = Sequence(cache, H, d, n, "fp8", seed_layer=11, outlier_frac=0.01)
+    for t in range(3):
+        _, k, v = seq.chunk(t)
+        k = k * 3.0  # push some values past the saturation point
+        k = synth.round_bf16(k).reshape(k.shape)
+        seq.append(0, t, k, v)
+        K, V = cache.blocks(0)
+        torch.cuda.synchronize()
+        kc = K[:, t % S].cpu().numpy()
+        vc = V[:, t % S].cpu().numpy()
+        for h in range(H):
+            assert np.array_equal(kc[h], oracle.quant_e4m3(k[:, h, :], ks[h])), h
+            assert np.array_equal(vc[h], oracle.quant_e4m3(v[:, h, :], vs[h])), h
+
+
+def test_slot_table_over_64_chunks():
+    for S in (2, 20):
+        cache = new_cache(1, 1, 64, 8, S)
+        seq = Sequence(cache, 1, 64, 8, "bf16", seed_layer=S)
+        for t in range(64):
+            _, k, v = seq.chunk(t)
+            seq.append(0, t, k, v)
+            assert cache.slot_chunk(0, t % S) == t
+        for s in range(S):
+            assert cache.slot_chunk(0, s) == max(c for c in range(64) if c % S == s)
+
+
+# ---------------------------------------------------------------------------
+# full-size configurations (one chunk-layer each, whole output against the oracle)
+def test_cfg1_full_size():
+    H, d, n, S, W = 12, 128, 1536, 2, 2
+    cache = new_cache(1, H, d, n, S)
+    seq = Sequence(cache, H, d, n, "bf16", seed_layer=0)
+    for t in range(2):
+        _, k, v = seq.chunk(t)
+        seq.append(0, t, k, v)
+    q, k, v = seq.chunk(2)
+    log("cfg1: oracle ...")
+    eo, el = seq.expected(2, q, k, v, W)
+    for G in (0, 1):
+        o, lse, _ = seq.attend(0, 2, q, k, v, W, G=G)
+        assert_close(o, lse, eo, el, TOL["bf16"], f"cfg1 full size G={G}")
+
+
+def test_cfg2_full_size():
+    H, d, n, S, W = 24, 128, 405, 20, 20
+    cache = new_cache(1, H, d, n, S, R=True)
+    seq = Sequence(cache, H, d, n, "bf16", seed_layer=0)
+    _, rk, rv = seq.chunk(100_000)
+    seq.append(0, 0, rk, rv, is_ref=True)
+    # chunks 5..24 in the ring (slots wrapped), query chunk 25
+    for t in range(5, 25):
+        _, k, v = seq.chunk(t)
+        seq.append(0, t, k, v)
+    q, k, v = seq.chunk(25)
+    log("cfg2: oracle ...")
+    eo, el = seq.expected(25, q, k, v, W, use_ref=True)
+    for G in (4, 0):
+        o, lse, _ = seq.attend(0, 25, q, k, v, W, use_ref=True, G=G)
+        assert_close(o, lse, eo, el, TOL["bf16"], f"cfg2 full size G={G}")
+
+
+def test_cfg3_streaming_wraparound():
+    # config-1 shapes streamed: every chunk attends, then is appended; the ring of
+    # 2 slots wraps many times. The oracle checks a sample of chunks, including the
+    # first ones (ring not full) and late ones (after wraparound).
+    H, d, n, S, W = 12, 128, 1536, 2, 2
+    cache = new_cache(1, H, d, n, S)
+    seq = Sequence(cache, H, d, n, "bf16", seed_layer=1)
+    check = {0, 1, 2, 3, 17}
+    for t in range(18):
+        q, k, v = seq.chunk(t)
+        o, lse, _ = seq.attend(0, t, q, k, v, W, G=0)
+        if t in check:
+            hist = {c: seq.history[c] for c in range(max(0, t - 3), t)}
+            eo, el = seq.expected(t, q, k, v, W, history=hist)
+            assert_close(o, lse, eo, el, TOL["bf16"], f"cfg3 stream t={t}")
+        seq.append(0, t, k, v)
+        assert cache.slot_chunk(0, t % S) == t
+        seq.history.pop(t - 4, None)
