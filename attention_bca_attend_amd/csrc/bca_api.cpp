@@ -214,22 +214,22 @@ bca_status make_plan(const bca_cache* c, int32_t layer, const bca_window_spec* s
   p.vis_id[p.nvis++] = -1;
   p.nk = p.nvis * n;
 
-  // runs: consecutive physical blocks share one run
+  // runs of the cache part: consecutive physical blocks share one run
   p.nruns = 0;
-  for (int i = 0; i < p.nvis; ++i) {
-    int b = p.vis_block[i];
-    if (b >= 0 && p.nruns > 0 && p.runs[p.nruns - 1].phys >= 0 &&
-        p.runs[p.nruns - 1].phys + p.runs[p.nruns - 1].len == b * n) {
+  for (int i = 0; i + 1 < p.nvis; ++i) {
+    const int b = p.vis_block[i];
+    if (p.nruns > 0 && p.runs[p.nruns - 1].phys + p.runs[p.nruns - 1].len == b * n) {
       p.runs[p.nruns - 1].len += n;
       continue;
     }
     Run r;
     r.vstart = i * n;
     r.len = n;
-    r.phys = b >= 0 ? b * n : -1;
+    r.phys = b * n;
     r.pad_ = 0;
     p.runs[p.nruns++] = r;
   }
+  p.nk_cache = (p.nvis - 1) * n;
 
   // a3: work planning. Every query row of the chunk sees the same keys, so all
   // units (head, query tile) have the same number of key tiles T. The
@@ -243,7 +243,8 @@ bca_status make_plan(const bca_cache* c, int32_t layer, const bca_window_spec* s
   p.bm = ts.bm;
   p.bn = ts.bn;
   p.q_tiles = (n + p.bm - 1) / p.bm;
-  p.kv_tiles = (p.nk + p.bn - 1) / p.bn;
+  p.cache_tiles = (p.nk_cache + p.bn - 1) / p.bn;
+  p.kv_tiles = p.cache_tiles + (n + p.bn - 1) / p.bn;
   p.units = d.num_heads * p.q_tiles;
   p.wgs = (int32_t)choose_wgs(c, p.kern, p.units, p.kv_tiles, s->num_segments);
   p.jmax = pieces_bound(p.units, p.kv_tiles, p.wgs);
@@ -397,7 +398,7 @@ size_t bca_attend_workspace_bytes(const bca_cache* c, const bca_window_spec* s) 
   size_t worst = 0;
   const int max_blocks = S + c->d.has_ref + 1;
   for (int blocks = 1; blocks <= max_blocks; ++blocks) {
-    int64_t T = ((int64_t)blocks * n + ts.bn - 1) / ts.bn;
+    int64_t T = ((int64_t)(blocks - 1) * n + ts.bn - 1) / ts.bn + (n + ts.bn - 1) / ts.bn;
     int64_t P = choose_wgs(c, k, units, T, s->num_segments);
     int32_t jmax = pieces_bound(units, T, P);
     if (jmax > 1) worst = std::max(worst, partial_bytes(units, jmax, ts.bm, c->d.head_dim));
@@ -445,7 +446,8 @@ bca_status bca_attend(const bca_cache* c, int32_t layer, const bca_window_spec* 
   a.cache_head_elems = (int64_t)(d.ring_slots + d.has_ref) * d.chunk_tokens * d.head_dim;
   a.n = d.chunk_tokens;
   a.H = d.num_heads;
-  a.nk = p.nk;
+  a.nk_cache = p.nk_cache;
+  a.cache_tiles = p.cache_tiles;
   a.T = p.kv_tiles;
   a.QT = p.q_tiles;
   a.units = p.units;

@@ -13,15 +13,19 @@ constexpr int kMaxBlocks = 64;  // ring slots + reference + current chunk
 constexpr int kMaxHeadsFp8 = 64;
 constexpr int kMaxSegments = 64;
 
-// A maximal range of consecutive visible keys that sits at one base address.
-// Visible keys are numbered 0 .. nk-1 in "key order": visible ring slots in
-// physical order, then the reference block, then the current chunk. Runs of
-// the cache are ranges of the head's [(S+R)*n][d] matrix; the current chunk is
-// a run of its own with row stride H*d.
+// A maximal range of consecutive visible cache keys that sits at one base
+// address. Visible cache keys are numbered 0 .. nk_cache-1 in "key order":
+// visible ring slots in physical order, then the reference block. A run is a
+// range of the head's [(S+R)*n][d] cache matrix.
+//
+// Key tiles: the first cache_tiles tiles cover the visible cache keys (the
+// last one padded with masked keys), the remaining tiles cover the current
+// chunk (its own tensor, row stride H*d). No tile mixes the two, so each tile
+// is read through one buffer resource.
 struct Run {
   int32_t vstart;  // first key of the run in key order
   int32_t len;     // number of keys
-  int32_t phys;    // first row in the head's cache matrix, or -1 for the current chunk
+  int32_t phys;    // first row in the head's cache matrix
   int32_t pad_;
 };
 
@@ -50,7 +54,9 @@ struct Plan {
   int64_t vis_id[kMaxBlocks];
   int32_t nruns;
   Run runs[kMaxBlocks];
-  int32_t nk;                       // visible keys
+  int32_t nk;                       // visible keys (cache + current)
+  int32_t nk_cache;                 // visible cache keys
+  int32_t cache_tiles;              // key tiles over the cache keys
   int32_t bm, bn;
   int32_t q_tiles, kv_tiles, units; // units = H * q_tiles
   int32_t wgs;                      // work groups (P)
@@ -71,7 +77,7 @@ struct AttnArgs {
   float* part_o;      // [units][jmax][bm][d] fp32
   float* part_lse;    // [units][jmax][bm]
   int64_t cache_head_elems;  // (S+R)*n*d
-  int32_t n, H, nk, T, QT, units, P, jmax;
+  int32_t n, H, nk_cache, cache_tiles, T, QT, units, P, jmax;
   float scale;        // softmax scale
   float scale_log2;   // scale * log2(e)
   int32_t xcd_remap;  // 1: spread work-group ids so each XCD gets a contiguous range

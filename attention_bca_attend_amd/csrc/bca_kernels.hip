@@ -65,49 +65,51 @@ constexpr int kBufDword3 = 0x00020000;  // raw buffer, gfx9 family
 constexpr int kOob = 0x7ffffff0;
 
 struct HeadSrc {
-  __amdgpu_buffer_rsrc_t cache;  // this head's cache matrix
-  __amdgpu_buffer_rsrc_t cur;    // this head's rows of the current chunk
+  const char* cache;  // this head's cache matrix
+  const char* cur;    // this head's first row of the current chunk
+  int cache_bytes;
+  int cur_bytes;
 };
+
+// A pointer every lane agrees on, held in scalar registers.
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+}
 
 __device__ __forceinline__ HeadSrc head_src(const void* cache_base, const void* cur_base,
                                             const AttnArgs& a, int h, int D, int es_cache,
                                             int es_cur) {
   HeadSrc r;
-  const int64_t hc = (int64_t)h * a.cache_head_elems * es_cache;
-  r.cache = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(static_cast<const char*>(cache_base) + hc), (short)0,
-      (int)(a.cache_head_elems * es_cache), kBufDword3);
-  const int64_t hq = (int64_t)h * D * es_cur;
-  r.cur = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(static_cast<const char*>(cur_base) + hq), (short)0,
-      (int)(((int64_t)(a.n - 1) * a.H * D + D) * es_cur), kBufDword3);
+  r.cache = uniform_ptr(static_cast<const char*>(cache_base) +
+                        (int64_t)h * a.cache_head_elems * es_cache);
+  r.cache_bytes = (int)(a.cache_head_elems * es_cache);
+  r.cur = uniform_ptr(static_cast<const char*>(cur_base) + (int64_t)h * D * es_cur);
+  r.cur_bytes = (int)(((int64_t)(a.n - 1) * a.H * D + D) * es_cur);
   return r;
 }
 
-__device__ __forceinline__ uint4 buf16(__amdgpu_buffer_rsrc_t r, int off) {
+__device__ __forceinline__ uint4 buf16(const char* base, int bytes, int off) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(base), (short)0, bytes, kBufDword3);
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-// Loads 16 bytes at byte column `colb` of NR key rows (key numbers j[i]) of
-// the tile of BN keys starting at j0; `ri` is the run holding j0. Keys at or
-// beyond nk read as zeros.
+// Loads 16 bytes at byte column `colb` of NR cache-key rows (key numbers j[i]
+// in the cache part of the key order) of the tile of BN keys starting at j0;
+// `ri` is the run holding j0. Keys at or beyond nk_cache read as zeros.
 template <int NR, int BN>
-__device__ __forceinline__ void load_rows(const AttnArgs& a, const HeadSrc& src, int D,
-                                          int es_cache, int es_cur, int j0, int ri,
-                                          const int (&j)[NR], int colb, uint4 (&out)[NR]) {
+__device__ __forceinline__ void load_cache_rows(const AttnArgs& a, const HeadSrc& src, int D,
+                                                int es, int j0, int ri, const int (&j)[NR],
+                                                int colb, uint4 (&out)[NR]) {
   const Run R0 = a.runs[ri];
   if (j0 + BN <= R0.vstart + R0.len) {
-    // the whole tile lies in one run and every row is valid
-    if (R0.phys >= 0) {
 #pragma unroll
-      for (int i = 0; i < NR; ++i)
-        out[i] = buf16(src.cache, (R0.phys + j[i] - R0.vstart) * D * es_cache + colb);
-    } else {
-#pragma unroll
-      for (int i = 0; i < NR; ++i)
-        out[i] = buf16(src.cur, (j[i] - R0.vstart) * a.H * D * es_cur + colb);
-    }
+    for (int i = 0; i < NR; ++i)
+      out[i] = buf16(src.cache, src.cache_bytes, (R0.phys + j[i] - R0.vstart) * D * es + colb);
     return;
   }
 #pragma unroll
@@ -118,11 +120,8 @@ __device__ __forceinline__ void load_rows(const AttnArgs& a, const HeadSrc& src,
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
       const bool in = j[i] >= R.vstart && j[i] < R.vstart + R.len;
-      uint4 v;
-      if (R.phys >= 0)
-        v = buf16(src.cache, in ? (R.phys + j[i] - R.vstart) * D * es_cache + colb : kOob);
-      else
-        v = buf16(src.cur, in ? (j[i] - R.vstart) * a.H * D * es_cur + colb : kOob);
+      const uint4 v = buf16(src.cache, src.cache_bytes,
+                            in ? (R.phys + j[i] - R.vstart) * D * es + colb : kOob);
       out[i].x |= v.x;
       out[i].y |= v.y;
       out[i].z |= v.z;
@@ -148,77 +147,177 @@ __device__ __forceinline__ float wave_swap32_sum(float x) { return x + __shfl_xo
 // bf16 attention on MFMA.
 //
 // Work group: 256 threads = 4 waves; BM = 128 query rows (32 per wave); key
-// tiles of BN = 64, double-buffered in LDS.
-// Per wave and tile the scores are computed transposed, S^T = K Q^T, with
-// v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims from LDS, B = 16 dims x 32
-// queries held in registers for the whole unit). In the 32x32 result lane l
-// holds query l%32 and 16 keys, so a row's max and sum need one exchange with
-// lane l^32 only. P^T stays in registers as the B operand of O^T += V^T P^T;
-// the MFMA's k index runs over keys in the order the score layout leaves them
-// in each lane, and V^T is stored in LDS with the matching key permutation so
-// each lane's 8 keys are one 16-byte read.
-// Online softmax in base 2 with a lazy rescale: the running maximum m is only
-// raised (and O, l rescaled) when a tile's maximum exceeds m by more than 8,
-// so weights stay below 2^8 and most tiles skip the rescale.
+// tiles of BN = 64 keys, two LDS stages (K and V of a tile each BN x d bf16,
+// row-major as in memory). Tiles are fetched straight into LDS by buffer
+// loads with an LDS destination: lane L of a wave-wide 16-byte load lands at
+// M0 + 16 L, so each lane picks the global 16-byte chunk that belongs at its
+// slot. Rows are XOR-swizzled at 16-byte granularity so that both LDS read
+// patterns below are free of bank conflicts (K: 16 consecutive rows at one
+// column; V: 8 rows x 64 bytes per transposed read).
+//
+// Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
+// A = 32 keys x 16 dims (one 16-byte LDS read per lane), B = Q^T, held in
+// registers for the whole unit. In the 32x32 result lane l holds query l%32
+// and 16 keys, so a row's max and sum need one exchange with lane l^32.
+// O^T += V^T P^T reuses P^T from registers as the B operand; the MFMA's k
+// index runs over keys in the order the score layout leaves them in each lane
+// ({4h..4h+3, 8+4h..8+4h+3} of every 16 keys for lane half h). The A operand
+// V^T comes from row-major V with ds_read_b64_tr_b16: within each group of 16
+// lanes, source lane a+4k points at 4 consecutive dims of key key0+k and
+// result lane 4a+b receives those 4 keys at one dim.
+//
+// Online softmax in base 2 with a lazy rescale: the running maximum m moves
+// only when a tile's maximum exceeds it by more than 8 (a factor 256), so O and
+// l are rescaled on few tiles.
 template <int D>
 struct Bf16Cfg {
-  static constexpr int BM = 128, BN = 64, NT = 256;
-  static constexpr int KSTR = D * 2 + 16;   // bytes per key row of the K tile (padded)
-  static constexpr int VSTR = BN * 2 + 16;  // bytes per dim row of the V^T tile (padded)
-  static constexpr int KT_BYTES = BN * KSTR;
-  static constexpr int VT_BYTES = D * VSTR;
-  static constexpr int STAGE = KT_BYTES + VT_BYTES;
-  static constexpr int CPR = D / 8;          // 16-byte chunks per key row
-  static constexpr int RPP = NT / CPR;       // K rows loaded per pass
-  static constexpr int KPASS = BN / RPP;     // K passes per tile
-  static constexpr int VITEMS = (BN / 4) * CPR;  // (4 keys x 8 dims) items per V tile
+  static constexpr int BM = 128, BN = 64, NT = 256, NW = 4;
+  static constexpr int ROWB = D * 2;                   // bytes per key row
+  static constexpr int CPR = D / 8;                    // 16-byte chunks per row
+  static constexpr int TILE_BYTES = BN * ROWB;         // K (or V) of one tile
+  static constexpr int STAGE = 2 * TILE_BYTES;         // K then V
+  static constexpr int RPI = 1024 / ROWB;              // rows per wave-wide 16-byte load
+  static constexpr int IPW = TILE_BYTES / 1024 / NW;   // such loads per wave per tensor
 };
 
-// Position of key k (0..63) in a V^T row: inside each group of 16 keys the
-// quads 4..7 and 8..11 trade places, so that lanes 0-31 find keys
-// {0-3, 8-11} and lanes 32-63 keys {4-7, 12-15} as 8 consecutive entries.
-__device__ __forceinline__ int vt_pos_of_quad(int kq) {
-  const int q = kq & 3;
-  const int sw = (q == 1) ? 2 : (q == 2) ? 1 : q;
-  return (kq >> 2) * 16 + sw * 4;
+// Physical 16-byte chunk of logical chunk c in tile row r is c ^ swizzle(r).
+// K rows are read 16 at a time at one logical chunk: the swizzle spreads them
+// over all 16 chunk slots of a 256-byte bank line. V is read 4 rows x 64 bytes
+// per 32 lanes: the swizzle moves each of the 4 rows to a different 64-byte
+// quarter of the bank line.
+template <int D>
+__device__ __forceinline__ int k_swizzle(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swizzle(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+
+// One wave-wide 16-byte buffer load into LDS (lane L -> lds + 16 L).
+__device__ __forceinline__ void lds_load16(const char* base, int bytes, int off,
+                                           unsigned char* lds) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(base), (short)0, bytes, kBufDword3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
+}
+
+// Fetches K and V of key tile `tile` into one LDS stage (asynchronously; the
+// caller waits on vmcnt and synchronises the work group before reading).
+template <int D>
+__device__ __forceinline__ int bf16_fetch_tile(const AttnArgs& a, const HeadSrc& ks,
+                                               const HeadSrc& vs, int tile, int ri,
+                                               unsigned char* stage, int wave, int lane) {
+  using C = Bf16Cfg<D>;
+  const int lrow = lane / C::CPR, lchunk = lane % C::CPR;
+  if (tile < a.cache_tiles) {
+    const int j0 = tile * C::BN;
+    ri = advance_run(a, ri, j0);
+    const Run R0 = a.runs[ri];
+    const bool one_run = j0 + C::BN <= R0.vstart + R0.len;
+#pragma unroll
+    for (int q = 0; q < C::IPW; ++q) {
+      const int gi = wave * C::IPW + q;
+      const int r = gi * C::RPI + lrow;
+      const int j = j0 + r;
+      int phys = -1;
+      if (one_run) {
+        phys = R0.phys + j - R0.vstart;
+      } else {
+        for (int rr = ri; rr < a.nruns; ++rr) {
+          const Run R = a.runs[rr];
+          if (R.vstart >= j0 + C::BN) break;
+          if (j >= R.vstart && j < R.vstart + R.len) phys = R.phys + j - R.vstart;
+        }
+      }
+      const int koff = phys >= 0 ? phys * C::ROWB + ((lchunk ^ k_swizzle<D>(r)) << 4) : kOob;
+      const int voff = phys >= 0 ? phys * C::ROWB + ((lchunk ^ v_swizzle<D>(r)) << 4) : kOob;
+      lds_load16(ks.cache, ks.cache_bytes, koff, stage + gi * 1024);
+      lds_load16(vs.cache, vs.cache_bytes, voff, stage + C::TILE_BYTES + gi * 1024);
+    }
+  } else {
+    const int r0 = (tile - a.cache_tiles) * C::BN;
+#pragma unroll
+    for (int q = 0; q < C::IPW; ++q) {
+      const int gi = wave * C::IPW + q;
+      const int r = gi * C::RPI + lrow;
+      const int row = r0 + r;
+      const int rowoff = row * a.H * C::ROWB;
+      const int koff = row < a.n ? rowoff + ((lchunk ^ k_swizzle<D>(r)) << 4) : kOob;
+      const int voff = row < a.n ? rowoff + ((lchunk ^ v_swizzle<D>(r)) << 4) : kOob;
+      lds_load16(ks.cur, ks.cur_bytes, koff, stage + gi * 1024);
+      lds_load16(vs.cur, vs.cur_bytes, voff, stage + C::TILE_BYTES + gi * 1024);
+    }
+  }
+  return ri;
+}
+
+// Keys of `tile` that are real (the rest of the tile is padding).
+__device__ __forceinline__ int tile_valid(const AttnArgs& a, int tile, int bn) {
+  if (tile < a.cache_tiles) return min(bn, a.nk_cache - tile * bn);
+  return min(bn, a.n - (tile - a.cache_tiles) * bn);
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(
+    const AttnArgs a) {
   using C = Bf16Cfg<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * C::STAGE];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int w = logical_wg(a);
   const int64_t I = (int64_t)a.units * a.T;
   int64_t it = range_begin(w, I, a.P);
   const int64_t it_end = range_begin(w + 1, I, a.P);
 
-  // this thread's load assignment inside a tile
-  const int k_row0 = tid / C::CPR, k_col = tid % C::CPR;
-  const bool v_active = tid < C::VITEMS;
-  const int v_kq = tid / C::CPR, v_dg = tid % C::CPR;
+  // LDS read offsets (bytes within a stage) that stay fixed for the kernel.
+  // K: row l32 (+32 for the second key block), logical chunk 2kk+hi.
+  int koff[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk)
+    koff[kk] = l32 * C::ROWB + (((2 * kk + hi) ^ k_swizzle<D>(l32)) << 4);
+  // V (transposed reads): group g = lane/16, i = lane%16 = a + 4k; rows 4hi+k of
+  // each 8-key step, dims 32db + 16(g%2) + 4a .. +3.
+  int voff[D / 32];
+  {
+    const int g = lane >> 4, i = lane & 15, ai = i & 3, k = i >> 2;
+    const int c0 = 2 * (g & 1) + (ai >> 1);
+    const int kx = D == 128 ? k : (k >> 1);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+      voff[db] = C::TILE_BYTES + (4 * hi + k) * C::ROWB + ((4 * (db ^ kx) + c0) << 4) +
+                 (ai & 1) * 8;
+  }
 
   while (it < it_end) {
     const int u = (int)(it / a.T);
     const int t0 = (int)(it - (int64_t)u * a.T);
     const int t1 = (int)((it_end - it) < (int64_t)(a.T - t0) ? t0 + (it_end - it) : a.T);
-    const int h = u / a.QT, qt = u - h * a.QT;
+    const int h = __builtin_amdgcn_readfirstlane(u / a.QT);
+    const int qt = u - h * a.QT;
     const int q0 = qt * C::BM + wave * 32;
     const bool wave_rows = q0 < a.n;
+    const HeadSrc ksrc = head_src(a.kc, a.kcur, a, h, D, 2, 2);
+    const HeadSrc vsrc = head_src(a.vc, a.vcur, a, h, D, 2, 2);
 
-    // Q^T fragments (B operand): lane holds query q0+l32, dims 16kk+8hi .. +7
+    int ri = bf16_fetch_tile<D>(a, ksrc, vsrc, t0, 0, smem, wave, lane);
+
+    // Q^T fragments (B operand): lane holds query q0+l32, dims 16kk+8hi .. +7;
+    // rows past the chunk read as zeros (out-of-range buffer offsets)
+    const HeadSrc qsrc = head_src(a.q, a.q, a, h, D, 2, 2);
     bf16x8_t qf[D / 16];
     {
       const int row = q0 + l32;
-      if (row < a.n) {
-        const __bf16* qp = static_cast<const __bf16*>(a.q) + ((int64_t)row * a.H + h) * D + 8 * hi;
+      const int qoff = row < a.n ? (row * a.H * D + 8 * hi) * 2 : kOob;
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) qf[kk] = *reinterpret_cast<const bf16x8_t*>(qp + 16 * kk);
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) qf[kk] = bf16x8_t{};
+      for (int kk = 0; kk < D / 16; ++kk) {
+        const uint4 x = buf16(qsrc.cur, qsrc.cur_bytes, qoff + (row < a.n ? 32 * kk : 0));
+        qf[kk] = __builtin_bit_cast(bf16x8_t, x);
       }
     }
 
@@ -226,80 +325,27 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnArgs a) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
     float m_run = -INFINITY, l_run = 0.f;
-    int ri = 0;
-
-    uint4 kreg[C::KPASS];
-    uint4 vreg[4];
-
-    const HeadSrc ksrc = head_src(a.kc, a.kcur, a, h, D, 2, 2);
-    const HeadSrc vsrc = head_src(a.vc, a.vcur, a, h, D, 2, 2);
-
-    auto load_tile = [&](int tile) {
-      const int j0 = tile * C::BN;
-      ri = advance_run(a, ri, j0);
-      int jk[C::KPASS];
-#pragma unroll
-      for (int p = 0; p < C::KPASS; ++p) jk[p] = j0 + k_row0 + p * C::RPP;
-      load_rows<C::KPASS, C::BN>(a, ksrc, D, 2, 2, j0, ri, jk, k_col * 16, kreg);
-      if (v_active) {
-        int jv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) jv[e] = j0 + 4 * v_kq + e;
-        load_rows<4, C::BN>(a, vsrc, D, 2, 2, j0, ri, jv, v_dg * 16, vreg);
-      }
-    };
-
-    auto store_tile = [&](int st) {
-      unsigned char* Ks = smem + st * C::STAGE;
-      unsigned char* Vs = Ks + C::KT_BYTES;
-#pragma unroll
-      for (int p = 0; p < C::KPASS; ++p)
-        *reinterpret_cast<uint4*>(Ks + (k_row0 + p * C::RPP) * C::KSTR + k_col * 16) = kreg[p];
-      if (v_active) {
-        // vreg[e] holds key 4kq+e, dims 8dg..8dg+7 (two per dword). Write dims
-        // as rows of V^T: 4 keys (8 bytes) per dim row.
-        const int pos = vt_pos_of_quad(v_kq);
-#pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-          const int d0 = 8 * v_dg + 2 * wd;
-          const uint32_t a0 = u4_get(vreg[0], wd), a1 = u4_get(vreg[1], wd);
-          const uint32_t a2 = u4_get(vreg[2], wd), a3 = u4_get(vreg[3], wd);
-          uint2 ev, od;
-          ev.x = (a0 & 0xffffu) | (a1 << 16);
-          ev.y = (a2 & 0xffffu) | (a3 << 16);
-          od.x = (a0 >> 16) | (a1 & 0xffff0000u);
-          od.y = (a2 >> 16) | (a3 & 0xffff0000u);
-          *reinterpret_cast<uint2*>(Vs + d0 * C::VSTR + pos * 2) = ev;
-          *reinterpret_cast<uint2*>(Vs + (d0 + 1) * C::VSTR + pos * 2) = od;
-        }
-      }
-    };
-
-    load_tile(t0);
-    store_tile(0);
-    __syncthreads();
 
     for (int tile = t0; tile < t1; ++tile) {
       const int st = (tile - t0) & 1;
-      const bool more = tile + 1 < t1;
-      if (more) load_tile(tile + 1);
-
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (tile + 1 < t1)
+        ri = bf16_fetch_tile<D>(a, ksrc, vsrc, tile + 1, ri, smem + (st ^ 1) * C::STAGE, wave,
+                                lane);
       if (wave_rows) {
-        const unsigned char* Ks = smem + st * C::STAGE;
-        const unsigned char* Vs = Ks + C::KT_BYTES;
+        const unsigned char* S = smem + st * C::STAGE;
         f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-          const int cb = (16 * kk + 8 * hi) * 2;
-          const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(Ks + l32 * C::KSTR + cb);
-          const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(Ks + (32 + l32) * C::KSTR + cb);
+          const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(S + koff[kk]);
+          const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(S + koff[kk] + 32 * C::ROWB);
           s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[kk], s0, 0, 0, 0);
           s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[kk], s1, 0, 0, 0);
         }
-        // keys past the last visible one (only in the final tile)
-        const int j0 = tile * C::BN;
-        if (j0 + C::BN > a.nk) {
-          const int lim = a.nk - j0;
+        // padding keys of a partial tile
+        const int lim = tile_valid(a, tile, C::BN);
+        if (lim < C::BN) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kr = 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -307,11 +353,9 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnArgs a) {
             if (32 + kr >= lim) s1[r] = -INFINITY;
           }
         }
-        float mx = s0[0];
+        float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s0[r]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s1[r]);
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
         mx = wave_swap32_max(mx);
         const float mxs = mx * a.scale_log2;
         const bool need = !(mxs <= m_run + 8.0f);
@@ -325,32 +369,35 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(const AttnArgs a) {
         }
         const float c = a.scale_log2;
         f32x16_t p0, p1;
-        float ls = 0.f;
+        float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           p0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], c, -m_run));
           p1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], c, -m_run));
-          ls += p0[r] + p1[r];
+          ls0 += p0[r];
+          ls1 += p1[r];
         }
-        l_run += ls;
+        l_run += ls0 + ls1;
         bf16x8_t pf[4];
         pf[0] = __builtin_convertvector(p0.lo, bf16x8_t);
         pf[1] = __builtin_convertvector(p0.hi, bf16x8_t);
         pf[2] = __builtin_convertvector(p1.lo, bf16x8_t);
         pf[3] = __builtin_convertvector(p1.hi, bf16x8_t);
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
+        for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const bf16x8_t vf = *reinterpret_cast<const bf16x8_t*>(
-                Vs + (32 * db + l32) * C::VSTR + (16 * kk + 8 * hi) * 2);
+          for (int db = 0; db < D / 32; ++db) {
+            const unsigned char* vp = S + voff[db] + 16 * kk * C::ROWB;
+            const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
+            const bf16x4_t hi4 =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * C::ROWB));
+            const bf16x8_t vf = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], o[db], 0, 0, 0);
           }
         }
       }
-      if (more) store_tile(st ^ 1);
-      __syncthreads();
     }
+    __syncthreads();  // the next unit's first fetch reuses stage 0
 
     // epilogue: normalise, LSE (natural log), write final output or a partial
     if (wave_rows) {
@@ -438,22 +485,36 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(const AttnArgs a) {
 
     for (int tile = t0; tile < t1; ++tile) {
       const int j0 = tile * BN;
-      ri = advance_run(a, ri, j0);
+      const int lim = tile_valid(a, tile, BN);
       int jr[NCH], cr[NCH];
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
-        jr[i] = j0 + (tid + NT * i) / CPR;
+        jr[i] = (tid + NT * i) / CPR;  // row inside the tile
         cr[i] = (tid + NT * i) % CPR;
       }
       // every thread's chunks share one column: NT is a multiple of CPR
       uint4 kv[NCH], vv[NCH];
-      load_rows<NCH, BN>(a, ksrc, D, 4, 4, j0, ri, jr, cr[0] * 16, kv);
-      load_rows<NCH, BN>(a, vsrc, D, 4, 4, j0, ri, jr, cr[0] * 16, vv);
+      if (tile < a.cache_tiles) {
+        ri = advance_run(a, ri, j0);
+        int jc[NCH];
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) jc[i] = j0 + jr[i];
+        load_cache_rows<NCH, BN>(a, ksrc, D, 4, j0, ri, jc, cr[0] * 16, kv);
+        load_cache_rows<NCH, BN>(a, vsrc, D, 4, j0, ri, jc, cr[0] * 16, vv);
+      } else {
+        const int r0 = (tile - a.cache_tiles) * BN;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const int row = r0 + jr[i];
+          const int off = row < a.n ? row * a.H * D * 4 + cr[i] * 16 : kOob;
+          kv[i] = buf16(ksrc.cur, ksrc.cur_bytes, off);
+          vv[i] = buf16(vsrc.cur, vsrc.cur_bytes, off);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
-        const int r = (tid + NT * i) / CPR;
-        *reinterpret_cast<uint4*>(&Ks[r][4 * cr[i]]) = kv[i];
-        *reinterpret_cast<uint4*>(&Vs[r][4 * cr[i]]) = vv[i];
+        *reinterpret_cast<uint4*>(&Ks[jr[i]][4 * cr[i]]) = kv[i];
+        *reinterpret_cast<uint4*>(&Vs[jr[i]][4 * cr[i]]) = vv[i];
       }
       __syncthreads();
 
@@ -464,7 +525,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(const AttnArgs a) {
 #pragma unroll
         for (int c = 0; c < HALF; ++c) acc = fmaf(q[c], Ks[j][half * HALF + c], acc);
         acc += __shfl_xor(acc, 1);
-        s[j] = (j0 + j < a.nk) ? acc * a.scale_log2 : -INFINITY;
+        s[j] = (j < lim) ? acc * a.scale_log2 : -INFINITY;
       }
       float mx = s[0];
 #pragma unroll

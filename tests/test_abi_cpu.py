@@ -158,7 +158,7 @@ def test_segment_planning():
     for G in (1, 2, 4, 7):
         p = bca.bca_attend_plan(h, 0, bca.bca_window_spec(40, 20, 1, G, 0.088))
         assert p["visible_keys"] == 22 * 405
-        assert p["kv_tiles"] == -(-22 * 405 // 64)
+        assert p["kv_tiles"] == -(-21 * 405 // 64) + -(-405 // 64)
         assert p["units"] == 24 * 4
         assert p["workgroups"] == p["units"] * G
         assert p["max_pieces"] == G and p["merge"] == (G > 1)
