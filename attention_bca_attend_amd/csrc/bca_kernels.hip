@@ -63,6 +63,8 @@ __device__ __forceinline__ int logical_wg(const AttnArgs& a) {
 // is how rows beyond the last visible key become zero rows without a branch.
 constexpr int kBufDword3 = 0x00020000;  // raw buffer, gfx9 family
 constexpr int kOob = 0x7ffffff0;
+// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt 0 and nothing else
+constexpr int kVmcnt0 = 0x0F70;
 
 struct HeadSrc {
   const char* cache;  // this head's cache matrix
@@ -143,41 +145,67 @@ __device__ __forceinline__ uint32_t u4_get(const uint4& v, int i) {
 __device__ __forceinline__ float wave_swap32_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 __device__ __forceinline__ float wave_swap32_sum(float x) { return x + __shfl_xor(x, 32); }
 
+// The same pair reductions over lanes l and l^32 on the vector ALU:
+// v_permlane32_swap exchanges the upper half of one operand with the lower
+// half of the other, so with both operands x every lane ends up holding x of
+// itself and of its partner (in either order), which is all a max or a sum
+// needs.
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---------------------------------------------------------------------------
 // bf16 attention on MFMA.
 //
-// Work group: 256 threads = 4 waves; BM = 128 query rows (32 per wave); key
-// tiles of BN = 64 keys, two LDS stages (K and V of a tile each BN x d bf16,
-// row-major as in memory). Tiles are fetched straight into LDS by buffer
-// loads with an LDS destination: lane L of a wave-wide 16-byte load lands at
-// M0 + 16 L, so each lane picks the global 16-byte chunk that belongs at its
-// slot. Rows are XOR-swizzled at 16-byte granularity so that both LDS read
-// patterns below are free of bank conflicts (K: 16 consecutive rows at one
-// column; V: 8 rows x 64 bytes per transposed read).
+// Work group: 512 threads = 8 waves in two groups of 4. BM = 128 query rows:
+// wave w of either group owns rows 32(w%4) .. +31. Key tiles of BN = 64 keys;
+// group g computes keys 32g .. 32g+31 of every tile ("split-K" inside the work
+// group), and the two partial softmax states of a row are merged through LDS
+// at the end of the unit.
 //
-// Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
-// A = 32 keys x 16 dims (one 16-byte LDS read per lane), B = Q^T, held in
-// registers for the whole unit. In the 32x32 result lane l holds query l%32
-// and 16 keys, so a row's max and sum need one exchange with lane l^32.
-// O^T += V^T P^T reuses P^T from registers as the B operand; the MFMA's k
-// index runs over keys in the order the score layout leaves them in each lane
-// ({4h..4h+3, 8+4h..8+4h+3} of every 16 keys for lane half h). The A operand
-// V^T comes from row-major V with ds_read_b64_tr_b16: within each group of 16
-// lanes, source lane a+4k points at 4 consecutive dims of key key0+k and
-// result lane 4a+b receives those 4 keys at one dim.
+// Ping-pong: the groups run the same sequence -- QK(0) | SM(0) | PV(0)+QK(1) |
+// SM(1) | PV(1)+QK(2) | ... -- one phase apart, with a work-group barrier
+// between phases, so in every phase one group issues MFMAs (PV of one tile and
+// QK of the next) while the other runs the softmax on the vector ALUs of the
+// same SIMDs. The MFMA group raises its wave priority for its phase.
 //
-// Online softmax in base 2 with a lazy rescale: the running maximum m moves
-// only when a tile's maximum exceeds it by more than 8 (a factor 256), so O and
-// l are rescaled on few tiles.
+// Tiles reach LDS by buffer loads with an LDS destination (lane L of a
+// wave-wide 16-byte load lands at M0 + 16 L), four stages deep: tile r+2 is
+// requested at the start of phase 2r and first read at phase 2r+4. K and V stay
+// row-major; rows are XOR-swizzled at 16-byte granularity so both read
+// patterns below are free of bank conflicts.
+//
+// Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
+// (A = 32 keys x 16 dims from LDS, B = Q^T held in registers for the unit).
+// In the 32x32 result lane l holds query l%32 and 16 keys, so a row's max and
+// sum need one exchange with lane l^32. O^T += V^T P^T takes P^T from
+// registers as the B operand, its k index running over keys in the order the
+// score layout leaves them ({4h..4h+3, 8+4h..8+4h+3} of every 16 keys for
+// lane half h); V^T comes from row-major V through ds_read_b64_tr_b16 (within
+// each group of 16 lanes, source lane a+4k points at 4 consecutive dims of key
+// key0+k, and result lane 4a+b receives those 4 keys at one dim).
+//
+// Online softmax in base 2 with a lazy rescale: the running maximum moves only
+// when a tile exceeds it by more than 8 (a factor 256), so O and l are
+// rescaled on few tiles.
 template <int D>
 struct Bf16Cfg {
-  static constexpr int BM = 128, BN = 64, NT = 256, NW = 4;
-  static constexpr int ROWB = D * 2;                   // bytes per key row
-  static constexpr int CPR = D / 8;                    // 16-byte chunks per row
-  static constexpr int TILE_BYTES = BN * ROWB;         // K (or V) of one tile
-  static constexpr int STAGE = 2 * TILE_BYTES;         // K then V
-  static constexpr int RPI = 1024 / ROWB;              // rows per wave-wide 16-byte load
-  static constexpr int IPW = TILE_BYTES / 1024 / NW;   // such loads per wave per tensor
+  static constexpr int BM = 128, BN = 64, NT = 512, NW = 8, NSTAGE = 4;
+  static constexpr int ROWB = D * 2;                  // bytes per key row
+  static constexpr int CPR = D / 8;                   // 16-byte chunks per row
+  static constexpr int TILE_BYTES = BN * ROWB;        // K (or V) of one tile
+  static constexpr int STAGE = 2 * TILE_BYTES;        // K then V
+  static constexpr int RPI = 1024 / ROWB;             // rows per wave-wide 16-byte load
+  static constexpr int IPW = TILE_BYTES / 1024 / NW;  // such loads per wave per tensor
+  static constexpr int LOADS = 2 * IPW;               // per wave per tile
+  static constexpr int XREG = D / 2 + 2;              // floats per lane in the group merge
 };
 
 // Physical 16-byte chunk of logical chunk c in tile row r is c ^ swizzle(r).
@@ -197,62 +225,130 @@ __device__ __forceinline__ int v_swizzle(int r) {
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
 
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
 // One wave-wide 16-byte buffer load into LDS (lane L -> lds + 16 L).
+// Issued through inline assembly on purpose: the kernels wait for these
+// loads themselves (s_waitcnt vmcnt before the work-group barrier that
+// precedes each use), and the compiler, which cannot tell which LDS stage a
+// load writes, would otherwise wait for all of them before every LDS read.
+// base must be wave-uniform (it becomes a scalar buffer resource).
 __device__ __forceinline__ void lds_load16(const char* base, int bytes, int off,
                                            unsigned char* lds) {
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(base), (short)0, bytes, kBufDword3);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4_t rsrc;
+  rsrc[0] = (int)__builtin_amdgcn_readfirstlane((uint32_t)p);
+  rsrc[1] = (int)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xffffu);
+  rsrc[2] = bytes;
+  rsrc[3] = kBufDword3;
+  const unsigned lds_addr = __builtin_amdgcn_readfirstlane(
+      (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)(lds));
+  // m0 is reserved by the compiler: save it, point it at the LDS destination,
+  // restore it.
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(rsrc), "s"(lds_addr)
+      : "memory");
 }
 
-// Fetches K and V of key tile `tile` into one LDS stage (asynchronously; the
-// caller waits on vmcnt and synchronises the work group before reading).
+// Scalar state of the tile requests of one unit: the run that holds the next
+// cache tile, kept in registers and reloaded only when a tile crosses into
+// the next run.
+struct FetchRun {
+  int ri, vstart, vend, phys;
+};
+
+__device__ __forceinline__ FetchRun fetch_run_at(const AttnArgs& a, int ri) {
+  FetchRun f;
+  f.ri = ri;
+  f.vstart = a.runs[ri].vstart;
+  f.vend = f.vstart + a.runs[ri].len;
+  f.phys = a.runs[ri].phys;
+  return f;
+}
+
+// Per-lane constants of the request pattern: the tile row each of the lane's
+// IPW loads covers and its swizzled byte column for K and for V.
 template <int D>
-__device__ __forceinline__ int bf16_fetch_tile(const AttnArgs& a, const HeadSrc& ks,
-                                               const HeadSrc& vs, int tile, int ri,
-                                               unsigned char* stage, int wave, int lane) {
+struct FetchLane {
+  int r[Bf16Cfg<D>::IPW];
+  int kcol[Bf16Cfg<D>::IPW];
+  int vcol[Bf16Cfg<D>::IPW];
+};
+
+template <int D>
+__device__ __forceinline__ FetchLane<D> fetch_lane(int wave, int lane) {
   using C = Bf16Cfg<D>;
+  FetchLane<D> f;
   const int lrow = lane / C::CPR, lchunk = lane % C::CPR;
+#pragma unroll
+  for (int q = 0; q < C::IPW; ++q) {
+    const int r = (wave * C::IPW + q) * C::RPI + lrow;
+    f.r[q] = r;
+    f.kcol[q] = (lchunk ^ k_swizzle<D>(r)) << 4;
+    f.vcol[q] = (lchunk ^ v_swizzle<D>(r)) << 4;
+  }
+  return f;
+}
+
+// Requests K and V of key tile `tile` into one LDS stage; completion is
+// awaited with vmcnt before the work-group barrier that precedes its use.
+// Wave w's load q fills the 1 KB of the stage at (w IPW + q) KB.
+template <int D>
+__device__ __forceinline__ void bf16_fetch_tile(const AttnArgs& a, const HeadSrc& ks,
+                                                const HeadSrc& vs, int tile, FetchRun& fr,
+                                                const FetchLane<D>& fl, unsigned char* stage,
+                                                int wave) {
+  using C = Bf16Cfg<D>;
+  unsigned char* kdst = stage + wave * C::IPW * 1024;
+  unsigned char* vdst = kdst + C::TILE_BYTES;
   if (tile < a.cache_tiles) {
     const int j0 = tile * C::BN;
-    ri = advance_run(a, ri, j0);
-    const Run R0 = a.runs[ri];
-    const bool one_run = j0 + C::BN <= R0.vstart + R0.len;
+    while (j0 >= fr.vend && fr.ri + 1 < a.nruns) fr = fetch_run_at(a, fr.ri + 1);
+    if (j0 + C::BN <= fr.vend) {
+      // the whole tile lies in one run
+      const int base = fr.phys + j0 - fr.vstart;
 #pragma unroll
-    for (int q = 0; q < C::IPW; ++q) {
-      const int gi = wave * C::IPW + q;
-      const int r = gi * C::RPI + lrow;
-      const int j = j0 + r;
-      int phys = -1;
-      if (one_run) {
-        phys = R0.phys + j - R0.vstart;
-      } else {
-        for (int rr = ri; rr < a.nruns; ++rr) {
+      for (int q = 0; q < C::IPW; ++q) {
+        const int off = (base + fl.r[q]) * C::ROWB;
+        lds_load16(ks.cache, ks.cache_bytes, off + fl.kcol[q], kdst + q * 1024);
+        lds_load16(vs.cache, vs.cache_bytes, off + fl.vcol[q], vdst + q * 1024);
+      }
+    } else {
+      // the tile crosses run boundaries or ends in padding
+#pragma unroll
+      for (int q = 0; q < C::IPW; ++q) {
+        const int j = j0 + fl.r[q];
+        int phys = -1;
+        for (int rr = fr.ri; rr < a.nruns; ++rr) {
           const Run R = a.runs[rr];
           if (R.vstart >= j0 + C::BN) break;
           if (j >= R.vstart && j < R.vstart + R.len) phys = R.phys + j - R.vstart;
         }
+        const int koff = phys >= 0 ? phys * C::ROWB + fl.kcol[q] : kOob;
+        const int voff = phys >= 0 ? phys * C::ROWB + fl.vcol[q] : kOob;
+        lds_load16(ks.cache, ks.cache_bytes, koff, kdst + q * 1024);
+        lds_load16(vs.cache, vs.cache_bytes, voff, vdst + q * 1024);
       }
-      const int koff = phys >= 0 ? phys * C::ROWB + ((lchunk ^ k_swizzle<D>(r)) << 4) : kOob;
-      const int voff = phys >= 0 ? phys * C::ROWB + ((lchunk ^ v_swizzle<D>(r)) << 4) : kOob;
-      lds_load16(ks.cache, ks.cache_bytes, koff, stage + gi * 1024);
-      lds_load16(vs.cache, vs.cache_bytes, voff, stage + C::TILE_BYTES + gi * 1024);
     }
   } else {
     const int r0 = (tile - a.cache_tiles) * C::BN;
 #pragma unroll
     for (int q = 0; q < C::IPW; ++q) {
-      const int gi = wave * C::IPW + q;
-      const int r = gi * C::RPI + lrow;
-      const int row = r0 + r;
+      const int row = r0 + fl.r[q];
       const int rowoff = row * a.H * C::ROWB;
-      const int koff = row < a.n ? rowoff + ((lchunk ^ k_swizzle<D>(r)) << 4) : kOob;
-      const int voff = row < a.n ? rowoff + ((lchunk ^ v_swizzle<D>(r)) << 4) : kOob;
-      lds_load16(ks.cur, ks.cur_bytes, koff, stage + gi * 1024);
-      lds_load16(vs.cur, vs.cur_bytes, voff, stage + C::TILE_BYTES + gi * 1024);
+      const int koff = row < a.n ? rowoff + fl.kcol[q] : kOob;
+      const int voff = row < a.n ? rowoff + fl.vcol[q] : kOob;
+      lds_load16(ks.cur, ks.cur_bytes, koff, kdst + q * 1024);
+      lds_load16(vs.cur, vs.cur_bytes, voff, vdst + q * 1024);
     }
   }
-  return ri;
 }
 
 // Keys of `tile` that are real (the rest of the tile is padding).
@@ -261,54 +357,179 @@ __device__ __forceinline__ int tile_valid(const AttnArgs& a, int tile, int bn) {
   return min(bn, a.n - (tile - a.cache_tiles) * bn);
 }
 
+// Work-group barrier without the memory fences __syncthreads() adds (those
+// would wait for every outstanding tile fetch). LDS reads issued before it
+// have all been consumed by MFMAs or waited for explicitly.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// Per-wave state of one unit in the ping-pong kernel.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(
-    const AttnArgs a) {
+struct PPState {
+  f32x16_t o[D / 32];  // O^T accumulator: dims 32db + 8(e/4) + 4hi + e%4, query l%32
+  f32x16_t s, s2;      // S^T of the tile (two partial sums) between its QK and its softmax
+  bf16x8_t pf[2];      // P^T of the tile between its softmax and its PV
+  float m_run, l_run;  // running max (base 2, scaled) and this lane's partial sum
+};
+
+// One MFMA phase: PV of the tile in stage SV and/or QK of the tile in stage
+// SK, for this group's 32 keys. The 8 PV and D/16 QK MFMAs alternate (the QK
+// chain accumulates into one register block, so each of its MFMAs waits on the
+// previous one; the independent PV MFMA between them covers that latency), and
+// the LDS operands are requested two steps ahead. sched_barrier keeps the
+// compiler from sinking the requests next to their uses.
+template <int D, bool PV, bool QK>
+__device__ __forceinline__ void pp_gemm(PPState<D>& st, const unsigned char* SV,
+                                        const unsigned char* SK, const int (&koff)[D / 16],
+                                        const int (&voff)[D / 32],
+                                        const bf16x8_t (&qf)[D / 16]) {
   using C = Bf16Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * C::STAGE];
+  constexpr int NPV = PV ? 2 * (D / 32) : 0;  // PV MFMAs: (kk, db)
+  constexpr int NQK = QK ? D / 16 : 0;        // QK MFMAs: kk
+  constexpr int NSTEP = NPV > NQK ? NPV : NQK;
+  constexpr int AHEAD = 3;                    // steps between an LDS request and its use
+  bf16x8_t vf[NSTEP + AHEAD], kf[NSTEP + AHEAD];
+  auto load_v = [&](int i) {
+    if (i < NPV) {
+      const int kk = i / (D / 32), db = i % (D / 32);
+      const unsigned char* vp = SV + voff[db] + 16 * kk * C::ROWB;
+      const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
+      const bf16x4_t h4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * C::ROWB));
+      vf[i] = __builtin_shufflevector(lo, h4, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  };
+  auto load_k = [&](int i) {
+    if (i < NQK) kf[i] = *reinterpret_cast<const bf16x8_t*>(SK + koff[i]);
+  };
+  // two QK accumulators (even and odd k steps): consecutive QK MFMAs are
+  // independent, so none waits for the previous one's result
+  f32x16_t acc0 = f32x16_t{}, acc1 = f32x16_t{};
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) {
+    load_v(i);
+    load_k(i);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < NSTEP; ++i) {
+    if (i < NPV) {
+      const int db = i % (D / 32), kk = i / (D / 32);
+      st.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], st.pf[kk], st.o[db], 0, 0, 0);
+    }
+    if (i < NQK) {
+      if (i & 1)
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i], acc1, 0, 0, 0);
+      else
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i], acc0, 0, 0, 0);
+    }
+    load_v(i + AHEAD);
+    load_k(i + AHEAD);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (QK) {
+    st.s = acc0;
+    st.s2 = acc1;
+  }
+}
+
+// Online softmax of st.s (lim = real keys of this group's half of the tile).
+template <int D>
+__device__ __forceinline__ void pp_softmax(PPState<D>& st, int lim, int hi, float c) {
+  st.s += st.s2;
+  if (lim < 32) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int kr = 8 * (e >> 2) + 4 * hi + (e & 3);
+      if (kr >= lim) st.s[e] = -INFINITY;
+    }
+  }
+  // maximum over the 16 scores (a tree of 3-input maxima) and the partner lane
+  const f32x16_t v = st.s;
+  const float m0 = fmaxf(fmaxf(v[0], v[1]), v[2]), m1 = fmaxf(fmaxf(v[3], v[4]), v[5]);
+  const float m2 = fmaxf(fmaxf(v[6], v[7]), v[8]), m3 = fmaxf(fmaxf(v[9], v[10]), v[11]);
+  const float m4 = fmaxf(fmaxf(v[12], v[13]), v[14]);
+  const float mx = xhalf_max(fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), v[15])));
+  const float mxs = mx * c;
+  const bool need = !(mxs <= st.m_run + 8.0f);
+  if (__any(need)) {
+    const float m_new = fmaxf(st.m_run, mxs);
+    const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) st.o[db] *= alpha;
+    st.l_run *= alpha;
+    st.m_run = m_new;
+  }
+  // a half whose keys have all been padding so far keeps m = -inf
+  const float m_use = st.m_run == -INFINITY ? 0.f : st.m_run;
+  f32x16_t p;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(v[e], c, -m_use));
+  // sum as a tree (independent adds instead of one 16-long chain)
+  float t8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) t8[e] = p[e] + p[e + 8];
+  const float ls = ((t8[0] + t8[4]) + (t8[1] + t8[5])) + ((t8[2] + t8[6]) + (t8[3] + t8[7]));
+  st.l_run += ls;
+  st.pf[0] = __builtin_convertvector(p.lo, bf16x8_t);
+  st.pf[1] = __builtin_convertvector(p.hi, bf16x8_t);
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
+  using C = Bf16Cfg<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::NSTAGE * C::STAGE];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wv = wave & 3;
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int w = logical_wg(a);
   const int64_t I = (int64_t)a.units * a.T;
   int64_t it = range_begin(w, I, a.P);
   const int64_t it_end = range_begin(w + 1, I, a.P);
 
-  // LDS read offsets (bytes within a stage) that stay fixed for the kernel.
-  // K: row l32 (+32 for the second key block), logical chunk 2kk+hi.
+  // LDS read offsets within a stage for this group's key half.
+  // K: row 32 grp + l32, logical chunk 2kk + hi.
   int koff[D / 16];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk)
-    koff[kk] = l32 * C::ROWB + (((2 * kk + hi) ^ k_swizzle<D>(l32)) << 4);
-  // V (transposed reads): group g = lane/16, i = lane%16 = a + 4k; rows 4hi+k of
-  // each 8-key step, dims 32db + 16(g%2) + 4a .. +3.
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const int row = 32 * grp + l32;
+    koff[kk] = row * C::ROWB + (((2 * kk + hi) ^ k_swizzle<D>(row)) << 4);
+  }
+  // V (transposed reads): group g16 = lane/16, i = lane%16 = ai + 4k; rows
+  // 32 grp + 4 hi + k of each 8-key step, dims 32 db + 16 (g16%2) + 4 ai .. +3.
   int voff[D / 32];
   {
-    const int g = lane >> 4, i = lane & 15, ai = i & 3, k = i >> 2;
-    const int c0 = 2 * (g & 1) + (ai >> 1);
+    const int g16 = lane >> 4, i = lane & 15, ai = i & 3, k = i >> 2;
+    const int c0 = 2 * (g16 & 1) + (ai >> 1);
     const int kx = D == 128 ? k : (k >> 1);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
-      voff[db] = C::TILE_BYTES + (4 * hi + k) * C::ROWB + ((4 * (db ^ kx) + c0) << 4) +
-                 (ai & 1) * 8;
+      voff[db] = C::TILE_BYTES + (32 * grp + 4 * hi + k) * C::ROWB +
+                 ((4 * (db ^ kx) + c0) << 4) + (ai & 1) * 8;
   }
+  const float c = a.scale_log2;
+  const FetchLane<D> fl = fetch_lane<D>(wave, lane);
 
   while (it < it_end) {
     const int u = (int)(it / a.T);
     const int t0 = (int)(it - (int64_t)u * a.T);
     const int t1 = (int)((it_end - it) < (int64_t)(a.T - t0) ? t0 + (it_end - it) : a.T);
+    const int nt = t1 - t0;
     const int h = __builtin_amdgcn_readfirstlane(u / a.QT);
     const int qt = u - h * a.QT;
-    const int q0 = qt * C::BM + wave * 32;
+    const int q0 = qt * C::BM + wv * 32;
     const bool wave_rows = q0 < a.n;
     const HeadSrc ksrc = head_src(a.kc, a.kcur, a, h, D, 2, 2);
     const HeadSrc vsrc = head_src(a.vc, a.vcur, a, h, D, 2, 2);
 
-    int ri = bf16_fetch_tile<D>(a, ksrc, vsrc, t0, 0, smem, wave, lane);
+    FetchRun fr = fetch_run_at(a, 0);
+    bf16_fetch_tile<D>(a, ksrc, vsrc, t0, fr, fl, smem, wave);
+    if (nt > 1) bf16_fetch_tile<D>(a, ksrc, vsrc, t0 + 1, fr, fl, smem + C::STAGE, wave);
 
     // Q^T fragments (B operand): lane holds query q0+l32, dims 16kk+8hi .. +7;
-    // rows past the chunk read as zeros (out-of-range buffer offsets)
+    // rows past the chunk read as zeros (out-of-range buffer offsets).
     const HeadSrc qsrc = head_src(a.q, a.q, a, h, D, 2, 2);
     bf16x8_t qf[D / 16];
     {
@@ -320,90 +541,134 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         qf[kk] = __builtin_bit_cast(bf16x8_t, x);
       }
     }
+    // Wait for everything in flight (the first tiles and Q) with a wait the
+    // compiler sees: it then knows the Q registers are loaded and inserts no
+    // vector-memory waits in the loop, where the only loads in flight are the
+    // tile requests this kernel waits for itself.
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
 
-    f32x16_t o[D / 32];
+    PPState<D> st;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db) o[db] = f32x16_t{};
-    float m_run = -INFINITY, l_run = 0.f;
+    for (int db = 0; db < D / 32; ++db) st.o[db] = f32x16_t{};
+    st.s = f32x16_t{};
+    st.s2 = f32x16_t{};
+    st.pf[0] = bf16x8_t{};
+    st.pf[1] = bf16x8_t{};
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
 
-    for (int tile = t0; tile < t1; ++tile) {
-      const int st = (tile - t0) & 1;
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (tile + 1 < t1)
-        ri = bf16_fetch_tile<D>(a, ksrc, vsrc, tile + 1, ri, smem + (st ^ 1) * C::STAGE, wave,
-                                lane);
-      if (wave_rows) {
-        const unsigned char* S = smem + st * C::STAGE;
-        f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(S + koff[kk]);
-          const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(S + koff[kk] + 32 * C::ROWB);
-          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[kk], s0, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[kk], s1, 0, 0, 0);
-        }
-        // padding keys of a partial tile
-        const int lim = tile_valid(a, tile, C::BN);
-        if (lim < C::BN) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kr = 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (kr >= lim) s0[r] = -INFINITY;
-            if (32 + kr >= lim) s1[r] = -INFINITY;
-          }
-        }
-        float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-        mx = wave_swap32_max(mx);
-        const float mxs = mx * a.scale_log2;
-        const bool need = !(mxs <= m_run + 8.0f);
-        if (__any(need)) {
-          const float m_new = fmaxf(m_run, mxs);
-          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) o[db] *= alpha;
-          l_run *= alpha;
-          m_run = m_new;
-        }
-        const float c = a.scale_log2;
-        f32x16_t p0, p1;
-        float ls0 = 0.f, ls1 = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          p0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], c, -m_run));
-          p1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], c, -m_run));
-          ls0 += p0[r];
-          ls1 += p1[r];
-        }
-        l_run += ls0 + ls1;
-        bf16x8_t pf[4];
-        pf[0] = __builtin_convertvector(p0.lo, bf16x8_t);
-        pf[1] = __builtin_convertvector(p0.hi, bf16x8_t);
-        pf[2] = __builtin_convertvector(p1.lo, bf16x8_t);
-        pf[3] = __builtin_convertvector(p1.hi, bf16x8_t);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const unsigned char* vp = S + voff[db] + 16 * kk * C::ROWB;
-            const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
-            const bf16x4_t hi4 =
-                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * C::ROWB));
-            const bf16x8_t vf = __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kk], o[db], 0, 0, 0);
-          }
-        }
+    // Phase k: even phases 2r start by requesting tile r+2; odd phases 2q-1 end
+    // by waiting for this wave's requests of tile q (read from phase 2q on).
+    auto begin_phase = [&](int k) {
+      if ((k & 1) == 0 && (k >> 1) + 2 < nt) {
+        const int r = (k >> 1) + 2;
+        bf16_fetch_tile<D>(a, ksrc, vsrc, t0 + r, fr, fl, smem + (r & 3) * C::STAGE, wave);
       }
-    }
-    __syncthreads();  // the next unit's first fetch reuses stage 0
+    };
+    auto end_phase = [&](int k) {
+      const int q = (k + 1) >> 1;
+      if ((k & 1) == 1 && q < nt) {
+        if (q + 1 < nt)
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::LOADS) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      wg_barrier();
+    };
+    auto stage = [&](int r) -> const unsigned char* { return smem + (r & 3) * C::STAGE; };
 
-    // epilogue: normalise, LSE (natural log), write final output or a partial
-    if (wave_rows) {
-      const float l_tot = wave_swap32_sum(l_run);
+    wg_barrier();
+
+    if (grp == 0) {
+      // k = 2r: PV(r-1) + QK(r); k = 2r+1: softmax(r)
+      begin_phase(0);
+      if (wave_rows) {
+        __builtin_amdgcn_s_setprio(1);
+        pp_gemm<D, false, true>(st, nullptr, stage(0), koff, voff, qf);
+        __builtin_amdgcn_s_setprio(0);
+      }
+      end_phase(0);
+      begin_phase(1);
+      if (wave_rows) pp_softmax<D>(st, tile_valid(a, t0, C::BN), hi, c);
+      end_phase(1);
+      for (int r = 1; r < nt; ++r) {
+        begin_phase(2 * r);
+        if (wave_rows) {
+          __builtin_amdgcn_s_setprio(1);
+          pp_gemm<D, true, true>(st, stage(r - 1), stage(r), koff, voff, qf);
+          __builtin_amdgcn_s_setprio(0);
+        }
+        end_phase(2 * r);
+        begin_phase(2 * r + 1);
+        if (wave_rows) pp_softmax<D>(st, tile_valid(a, t0 + r, C::BN), hi, c);
+        end_phase(2 * r + 1);
+      }
+      begin_phase(2 * nt);
+      if (wave_rows) {
+        __builtin_amdgcn_s_setprio(1);
+        pp_gemm<D, true, false>(st, stage(nt - 1), nullptr, koff, voff, qf);
+        __builtin_amdgcn_s_setprio(0);
+      }
+      end_phase(2 * nt);
+      begin_phase(2 * nt + 1);
+      end_phase(2 * nt + 1);
+    } else {
+      // one phase later: k = 2r+1: PV(r-1) + QK(r); k = 2r+2: softmax(r)
+      begin_phase(0);
+      end_phase(0);
+      begin_phase(1);
+      if (wave_rows) {
+        __builtin_amdgcn_s_setprio(1);
+        pp_gemm<D, false, true>(st, nullptr, stage(0), koff, voff, qf);
+        __builtin_amdgcn_s_setprio(0);
+      }
+      end_phase(1);
+      for (int r = 1; r < nt; ++r) {
+        begin_phase(2 * r);
+        if (wave_rows) pp_softmax<D>(st, tile_valid(a, t0 + r - 1, C::BN) - 32, hi, c);
+        end_phase(2 * r);
+        begin_phase(2 * r + 1);
+        if (wave_rows) {
+          __builtin_amdgcn_s_setprio(1);
+          pp_gemm<D, true, true>(st, stage(r - 1), stage(r), koff, voff, qf);
+          __builtin_amdgcn_s_setprio(0);
+        }
+        end_phase(2 * r + 1);
+      }
+      begin_phase(2 * nt);
+      if (wave_rows) pp_softmax<D>(st, tile_valid(a, t0 + nt - 1, C::BN) - 32, hi, c);
+      end_phase(2 * nt);
+      begin_phase(2 * nt + 1);
+      if (wave_rows) {
+        __builtin_amdgcn_s_setprio(1);
+        pp_gemm<D, true, false>(st, stage(nt - 1), nullptr, koff, voff, qf);
+        __builtin_amdgcn_s_setprio(0);
+      }
+      end_phase(2 * nt + 1);
+    }
+
+    // merge the two key halves: group 1 publishes (O, m, l) per lane, group 0
+    // combines; both groups hold the same (row, dim) elements lane for lane.
+    float* xch = reinterpret_cast<float*>(smem) + (size_t)wv * C::XREG * 64 + lane;
+    if (grp == 1 && wave_rows) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) xch[(db * 16 + e) * 64] = st.o[db][e];
+      xch[(D / 2) * 64] = st.m_run;
+      xch[(D / 2 + 1) * 64] = st.l_run;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    wg_barrier();
+    if (grp == 0 && wave_rows) {
+      const float m1 = xch[(D / 2) * 64], l1 = xch[(D / 2 + 1) * 64];
+      const float M = fmaxf(st.m_run, m1);
+      const float a0 = st.m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m_run - M);
+      const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+      const float l_tot = xhalf_sum(st.l_run * a0 + l1 * a1);
       const float inv = 1.0f / l_tot;
-      const float lse_val = (m_run + log2f(l_tot)) * kLn2;
+      const float lse_val = (M + log2f(l_tot)) * kLn2;
+      const float s0 = a0 * inv, s1 = a1 * inv;
       const int row = q0 + l32;
       const bool whole = (t0 == 0) && (t1 == a.T);
       if (row < a.n) {
@@ -413,28 +678,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-              f32x4_t v4 = {o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
-              v4 *= inv;
+              f32x4_t v4;
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                v4[e] = st.o[db][4 * g + e] * s0 + xch[(db * 16 + 4 * g + e) * 64] * s1;
               *reinterpret_cast<bf16x4_t*>(op + 32 * db + 8 * g + 4 * hi) =
                   __builtin_convertvector(v4, bf16x4_t);
             }
           if (hi == 0 && a.lse) a.lse[(int64_t)h * a.n + row] = lse_val;
         } else {
           const int64_t jslot = (int64_t)w - first_wg_of((int64_t)u * a.T, I, a.P);
-          const int64_t prow = ((int64_t)u * a.jmax + jslot) * C::BM + wave * 32 + l32;
+          const int64_t prow = ((int64_t)u * a.jmax + jslot) * C::BM + wv * 32 + l32;
           float* pp = a.part_o + prow * D;
 #pragma unroll
           for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-              f32x4_t v4 = {o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
-              v4 *= inv;
+              f32x4_t v4;
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                v4[e] = st.o[db][4 * g + e] * s0 + xch[(db * 16 + 4 * g + e) * 64] * s1;
               *reinterpret_cast<f32x4_t*>(pp + 32 * db + 8 * g + 4 * hi) = v4;
             }
           if (hi == 0) a.part_lse[prow] = lse_val;
         }
       }
     }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    wg_barrier();  // the next unit's first requests reuse the LDS just read
     it += t1 - t0;
   }
 }
@@ -682,7 +953,7 @@ template <int D>
 int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
   switch (p.kern) {
     case Kern::BF16:
-      hipLaunchKernelGGL(attn_bf16_kernel<D>, dim3(p.wgs), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(attn_bf16_kernel<D>, dim3(p.wgs), dim3(512), 0, s, a);
       break;
     case Kern::F32:
       hipLaunchKernelGGL(attn_f32_kernel<D>, dim3(p.wgs), dim3(128), 0, s, a);
