@@ -72,6 +72,12 @@ def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with "
                           f"'python -m attention_bca_attend_amd.build'")
+    # torch ships its own build of the HIP runtime under the same soname
+    # (libamdhip64.so.7) as the system one libbca.so is linked against. Loading
+    # torch first makes libbca bind to the runtime already in the process;
+    # loaded the other way round the process would hold two HIP and two HSA
+    # runtimes driving one GPU, and torch's first device copy crashes.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     desc_p = ctypes.POINTER(bca_cache_desc)

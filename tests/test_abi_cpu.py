@@ -159,13 +159,14 @@ def test_segment_planning():
         p = bca.bca_attend_plan(h, 0, bca.bca_window_spec(40, 20, 1, G, 0.088))
         assert p["visible_keys"] == 22 * 405
         assert p["kv_tiles"] == -(-21 * 405 // 64) + -(-405 // 64)
-        assert p["units"] == 24 * 4
+        bm = -(-405 // p["q_tiles"])  # rows per query tile (a power of two >= this)
+        assert p["q_tiles"] in (1, 2, 4, 7) and p["units"] == 24 * p["q_tiles"]
         assert p["workgroups"] == p["units"] * G
         assert p["max_pieces"] == G and p["merge"] == (G > 1)
         ws = bca.bca_attend_workspace_bytes(h, bca.bca_window_spec(40, 20, 1, G, 0.088))
         assert ws >= p["workspace_bytes"]
         if G > 1:
-            assert p["workspace_bytes"] >= p["units"] * G * 128 * 129 * 4
+            assert p["workspace_bytes"] >= p["units"] * G * bm * 129 * 4
     # automatic split: never more work groups than tile iterations
     p = bca.bca_attend_plan(h, 0, bca.bca_window_spec(40, 20, 1, 0, 0.088))
     assert 1 <= p["workgroups"] <= p["units"] * p["kv_tiles"]
@@ -264,3 +265,22 @@ def test_fp8_scales_validation_and_reset():
 def test_status_strings():
     for code, name in bca.STATUS.items():
         assert bca.bca_status_string(code) == name
+
+
+def test_one_hip_runtime_per_process():
+    """Importing the package before torch must not map a second HIP or HSA
+    runtime next to the one torch brings (both drive the same GPU)."""
+    import subprocess
+    import sys
+    code = (
+        "import attention_bca_attend_amd, torch, re\n"
+        "libs = set()\n"
+        "for line in open('/proc/self/maps'):\n"
+        "    m = re.search(r'(/\\S*lib(amdhip64|hsa-runtime64)\\S*)', line)\n"
+        "    if m: libs.add((m.group(2), m.group(1)))\n"
+        "print(sorted(libs))\n"
+        "kinds = [k for k, _ in libs]\n"
+        "assert kinds.count('amdhip64') == 1 and kinds.count('hsa-runtime64') == 1, libs\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
