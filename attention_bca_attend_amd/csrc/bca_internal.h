@@ -40,7 +40,7 @@ struct TileShape {
 inline TileShape tile_shape(Kern k) {
   switch (k) {
     case Kern::F32: return {64, 32};
-    case Kern::BF16: return {128, 64};
+    case Kern::BF16: return {256, 64};
     case Kern::FP8: return {128, 64};
   }
   return {128, 64};

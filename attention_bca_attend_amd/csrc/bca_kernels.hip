@@ -164,17 +164,15 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 // ---------------------------------------------------------------------------
 // bf16 attention on MFMA.
 //
-// Work group: 512 threads = 8 waves in two groups of 4. BM = 128 query rows:
-// wave w of either group owns rows 32(w%4) .. +31. Key tiles of BN = 64 keys;
-// group g computes keys 32g .. 32g+31 of every tile ("split-K" inside the work
-// group), and the two partial softmax states of a row are merged through LDS
-// at the end of the unit.
+// Work group: 512 threads = 8 waves in two groups of 4. BM = 256 query rows:
+// wave w of group g owns rows 128g + 32(w%4) .. +31. Key tiles of BN = 64 keys.
 //
 // Ping-pong: the groups run the same sequence -- QK(0) | SM(0) | PV(0)+QK(1) |
 // SM(1) | PV(1)+QK(2) | ... -- one phase apart, with a work-group barrier
 // between phases, so in every phase one group issues MFMAs (PV of one tile and
-// QK of the next) while the other runs the softmax on the vector ALUs of the
-// same SIMDs. The MFMA group raises its wave priority for its phase.
+// QK of the next: 32 per wave) while the other runs the softmax on the vector
+// ALUs of the same SIMDs. The MFMA group raises its wave priority for its
+// phase. Every key tile in LDS serves all 256 rows.
 //
 // Tiles reach LDS by buffer loads with an LDS destination (lane L of a
 // wave-wide 16-byte load lands at M0 + 16 L), four stages deep: tile r+2 is
@@ -197,7 +195,7 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 // rescaled on few tiles.
 template <int D>
 struct Bf16Cfg {
-  static constexpr int BM = 128, BN = 64, NT = 512, NW = 8, NSTAGE = 4;
+  static constexpr int BM = 256, BN = 64, NT = 512, NW = 8, NSTAGE = 4;
   static constexpr int ROWB = D * 2;                  // bytes per key row
   static constexpr int CPR = D / 8;                   // 16-byte chunks per row
   static constexpr int TILE_BYTES = BN * ROWB;        // K (or V) of one tile
@@ -205,7 +203,6 @@ struct Bf16Cfg {
   static constexpr int RPI = 1024 / ROWB;             // rows per wave-wide 16-byte load
   static constexpr int IPW = TILE_BYTES / 1024 / NW;  // such loads per wave per tensor
   static constexpr int LOADS = 2 * IPW;               // per wave per tile
-  static constexpr int XREG = D / 2 + 2;              // floats per lane in the group merge
 };
 
 // Physical 16-byte chunk of logical chunk c in tile row r is c ^ swizzle(r).
@@ -368,27 +365,26 @@ __device__ __forceinline__ void wg_barrier() {
 template <int D>
 struct PPState {
   f32x16_t o[D / 32];  // O^T accumulator: dims 32db + 8(e/4) + 4hi + e%4, query l%32
-  f32x16_t s, s2;      // S^T of the tile (two partial sums) between its QK and its softmax
-  bf16x8_t pf[2];      // P^T of the tile between its softmax and its PV
+  f32x16_t s[2];       // S^T of the tile (keys 0-31, 32-63) between its QK and its softmax
+  bf16x8_t pf[4];      // P^T of the tile (16-key steps) between its softmax and its PV
   float m_run, l_run;  // running max (base 2, scaled) and this lane's partial sum
 };
 
 // One MFMA phase: PV of the tile in stage SV and/or QK of the tile in stage
-// SK, for this group's 32 keys. The 8 PV and D/16 QK MFMAs alternate (the QK
-// chain accumulates into one register block, so each of its MFMAs waits on the
-// previous one; the independent PV MFMA between them covers that latency), and
-// the LDS operands are requested two steps ahead. sched_barrier keeps the
-// compiler from sinking the requests next to their uses.
+// SK. The 16 PV and 16 QK MFMAs alternate; consecutive QK MFMAs go to the two
+// independent 32-key score blocks, and the LDS operands are requested AHEAD
+// steps before their use. sched_barrier keeps the compiler from sinking the
+// requests next to their uses.
 template <int D, bool PV, bool QK>
 __device__ __forceinline__ void pp_gemm(PPState<D>& st, const unsigned char* SV,
                                         const unsigned char* SK, const int (&koff)[D / 16],
                                         const int (&voff)[D / 32],
                                         const bf16x8_t (&qf)[D / 16]) {
   using C = Bf16Cfg<D>;
-  constexpr int NPV = PV ? 2 * (D / 32) : 0;  // PV MFMAs: (kk, db)
-  constexpr int NQK = QK ? D / 16 : 0;        // QK MFMAs: kk
+  constexpr int NPV = PV ? 4 * (D / 32) : 0;  // PV MFMAs: (kk 0..3, db)
+  constexpr int NQK = QK ? 2 * (D / 16) : 0;  // QK MFMAs: (kk, key block 0..1)
   constexpr int NSTEP = NPV > NQK ? NPV : NQK;
-  constexpr int AHEAD = 3;                    // steps between an LDS request and its use
+  constexpr int AHEAD = 3;
   bf16x8_t vf[NSTEP + AHEAD], kf[NSTEP + AHEAD];
   auto load_v = [&](int i) {
     if (i < NPV) {
@@ -400,10 +396,11 @@ __device__ __forceinline__ void pp_gemm(PPState<D>& st, const unsigned char* SV,
     }
   };
   auto load_k = [&](int i) {
-    if (i < NQK) kf[i] = *reinterpret_cast<const bf16x8_t*>(SK + koff[i]);
+    if (i < NQK) {
+      const int kk = i >> 1, kb = i & 1;
+      kf[i] = *reinterpret_cast<const bf16x8_t*>(SK + koff[kk] + kb * 32 * C::ROWB);
+    }
   };
-  // two QK accumulators (even and odd k steps): consecutive QK MFMAs are
-  // independent, so none waits for the previous one's result
   f32x16_t acc0 = f32x16_t{}, acc1 = f32x16_t{};
 #pragma unroll
   for (int i = 0; i < AHEAD; ++i) {
@@ -419,37 +416,42 @@ __device__ __forceinline__ void pp_gemm(PPState<D>& st, const unsigned char* SV,
     }
     if (i < NQK) {
       if (i & 1)
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i], acc1, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i >> 1], acc1, 0, 0, 0);
       else
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i], acc0, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i >> 1], acc0, 0, 0, 0);
     }
     load_v(i + AHEAD);
     load_k(i + AHEAD);
     __builtin_amdgcn_sched_barrier(0);
   }
   if (QK) {
-    st.s = acc0;
-    st.s2 = acc1;
+    st.s[0] = acc0;
+    st.s[1] = acc1;
   }
 }
 
-// Online softmax of st.s (lim = real keys of this group's half of the tile).
+// Online softmax of the tile's scores (lim = real keys of the tile).
 template <int D>
 __device__ __forceinline__ void pp_softmax(PPState<D>& st, int lim, int hi, float c) {
-  st.s += st.s2;
-  if (lim < 32) {
+  if (lim < 64) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int kr = 8 * (e >> 2) + 4 * hi + (e & 3);
-      if (kr >= lim) st.s[e] = -INFINITY;
+      if (kr >= lim) st.s[0][e] = -INFINITY;
+      if (32 + kr >= lim) st.s[1][e] = -INFINITY;
     }
   }
-  // maximum over the 16 scores (a tree of 3-input maxima) and the partner lane
-  const f32x16_t v = st.s;
-  const float m0 = fmaxf(fmaxf(v[0], v[1]), v[2]), m1 = fmaxf(fmaxf(v[3], v[4]), v[5]);
-  const float m2 = fmaxf(fmaxf(v[6], v[7]), v[8]), m3 = fmaxf(fmaxf(v[9], v[10]), v[11]);
-  const float m4 = fmaxf(fmaxf(v[12], v[13]), v[14]);
-  const float mx = xhalf_max(fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), v[15])));
+  // maximum over the 32 scores (a tree of 3-input maxima) and the partner lane
+  const f32x16_t v0 = st.s[0], v1 = st.s[1];
+  float m[11];
+#pragma unroll
+  for (int e = 0; e < 5; ++e) m[e] = fmaxf(fmaxf(v0[3 * e], v0[3 * e + 1]), v0[3 * e + 2]);
+#pragma unroll
+  for (int e = 0; e < 5; ++e) m[5 + e] = fmaxf(fmaxf(v1[3 * e], v1[3 * e + 1]), v1[3 * e + 2]);
+  m[10] = fmaxf(v0[15], v1[15]);
+  const float n0 = fmaxf(fmaxf(m[0], m[1]), m[2]), n1 = fmaxf(fmaxf(m[3], m[4]), m[5]);
+  const float n2 = fmaxf(fmaxf(m[6], m[7]), m[8]), n3 = fmaxf(m[9], m[10]);
+  const float mx = xhalf_max(fmaxf(fmaxf(n0, n1), fmaxf(n2, n3)));
   const float mxs = mx * c;
   const bool need = !(mxs <= st.m_run + 8.0f);
   if (__any(need)) {
@@ -460,19 +462,22 @@ __device__ __forceinline__ void pp_softmax(PPState<D>& st, int lim, int hi, floa
     st.l_run *= alpha;
     st.m_run = m_new;
   }
-  // a half whose keys have all been padding so far keeps m = -inf
   const float m_use = st.m_run == -INFINITY ? 0.f : st.m_run;
-  f32x16_t p;
+  f32x16_t p0, p1;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(v[e], c, -m_use));
-  // sum as a tree (independent adds instead of one 16-long chain)
+  for (int e = 0; e < 16; ++e) {
+    p0[e] = __builtin_amdgcn_exp2f(fmaf(v0[e], c, -m_use));
+    p1[e] = __builtin_amdgcn_exp2f(fmaf(v1[e], c, -m_use));
+  }
+  // sum as a tree (independent adds instead of one long chain)
   float t8[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) t8[e] = p[e] + p[e + 8];
-  const float ls = ((t8[0] + t8[4]) + (t8[1] + t8[5])) + ((t8[2] + t8[6]) + (t8[3] + t8[7]));
-  st.l_run += ls;
-  st.pf[0] = __builtin_convertvector(p.lo, bf16x8_t);
-  st.pf[1] = __builtin_convertvector(p.hi, bf16x8_t);
+  for (int e = 0; e < 8; ++e) t8[e] = (p0[e] + p0[e + 8]) + (p1[e] + p1[e + 8]);
+  st.l_run += ((t8[0] + t8[4]) + (t8[1] + t8[5])) + ((t8[2] + t8[6]) + (t8[3] + t8[7]));
+  st.pf[0] = __builtin_convertvector(p0.lo, bf16x8_t);
+  st.pf[1] = __builtin_convertvector(p0.hi, bf16x8_t);
+  st.pf[2] = __builtin_convertvector(p1.lo, bf16x8_t);
+  st.pf[3] = __builtin_convertvector(p1.hi, bf16x8_t);
 }
 
 template <int D>
@@ -482,23 +487,21 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave >> 2, wv = wave & 3;
+  const int grp = wave >> 2;
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int w = logical_wg(a);
   const int64_t I = (int64_t)a.units * a.T;
   int64_t it = range_begin(w, I, a.P);
   const int64_t it_end = range_begin(w + 1, I, a.P);
 
-  // LDS read offsets within a stage for this group's key half.
-  // K: row 32 grp + l32, logical chunk 2kk + hi.
+  // LDS read offsets within a stage. K: row l32 (+32 for keys 32-63), logical
+  // chunk 2kk + hi.
   int koff[D / 16];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    const int row = 32 * grp + l32;
-    koff[kk] = row * C::ROWB + (((2 * kk + hi) ^ k_swizzle<D>(row)) << 4);
-  }
+  for (int kk = 0; kk < D / 16; ++kk)
+    koff[kk] = l32 * C::ROWB + (((2 * kk + hi) ^ k_swizzle<D>(l32)) << 4);
   // V (transposed reads): group g16 = lane/16, i = lane%16 = ai + 4k; rows
-  // 32 grp + 4 hi + k of each 8-key step, dims 32 db + 16 (g16%2) + 4 ai .. +3.
+  // 4 hi + k of each 8-key step, dims 32 db + 16 (g16%2) + 4 ai .. +3.
   int voff[D / 32];
   {
     const int g16 = lane >> 4, i = lane & 15, ai = i & 3, k = i >> 2;
@@ -506,8 +509,8 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
     const int kx = D == 128 ? k : (k >> 1);
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
-      voff[db] = C::TILE_BYTES + (32 * grp + 4 * hi + k) * C::ROWB +
-                 ((4 * (db ^ kx) + c0) << 4) + (ai & 1) * 8;
+      voff[db] = C::TILE_BYTES + (4 * hi + k) * C::ROWB + ((4 * (db ^ kx) + c0) << 4) +
+                 (ai & 1) * 8;
   }
   const float c = a.scale_log2;
   const FetchLane<D> fl = fetch_lane<D>(wave, lane);
@@ -519,7 +522,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
     const int nt = t1 - t0;
     const int h = __builtin_amdgcn_readfirstlane(u / a.QT);
     const int qt = u - h * a.QT;
-    const int q0 = qt * C::BM + wv * 32;
+    const int q0 = qt * C::BM + (wave & 7) * 32;  // = 128 grp + 32 (wave % 4)
     const bool wave_rows = q0 < a.n;
     const HeadSrc ksrc = head_src(a.kc, a.kcur, a, h, D, 2, 2);
     const HeadSrc vsrc = head_src(a.vc, a.vcur, a, h, D, 2, 2);
@@ -550,10 +553,10 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
     PPState<D> st;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db) st.o[db] = f32x16_t{};
-    st.s = f32x16_t{};
-    st.s2 = f32x16_t{};
-    st.pf[0] = bf16x8_t{};
-    st.pf[1] = bf16x8_t{};
+    st.s[0] = f32x16_t{};
+    st.s[1] = f32x16_t{};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st.pf[e] = bf16x8_t{};
     st.m_run = -INFINITY;
     st.l_run = 0.f;
 
@@ -625,7 +628,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
       end_phase(1);
       for (int r = 1; r < nt; ++r) {
         begin_phase(2 * r);
-        if (wave_rows) pp_softmax<D>(st, tile_valid(a, t0 + r - 1, C::BN) - 32, hi, c);
+        if (wave_rows) pp_softmax<D>(st, tile_valid(a, t0 + r - 1, C::BN), hi, c);
         end_phase(2 * r);
         begin_phase(2 * r + 1);
         if (wave_rows) {
@@ -636,7 +639,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
         end_phase(2 * r + 1);
       }
       begin_phase(2 * nt);
-      if (wave_rows) pp_softmax<D>(st, tile_valid(a, t0 + nt - 1, C::BN) - 32, hi, c);
+      if (wave_rows) pp_softmax<D>(st, tile_valid(a, t0 + nt - 1, C::BN), hi, c);
       end_phase(2 * nt);
       begin_phase(2 * nt + 1);
       if (wave_rows) {
@@ -647,28 +650,11 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
       end_phase(2 * nt + 1);
     }
 
-    // merge the two key halves: group 1 publishes (O, m, l) per lane, group 0
-    // combines; both groups hold the same (row, dim) elements lane for lane.
-    float* xch = reinterpret_cast<float*>(smem) + (size_t)wv * C::XREG * 64 + lane;
-    if (grp == 1 && wave_rows) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) xch[(db * 16 + e) * 64] = st.o[db][e];
-      xch[(D / 2) * 64] = st.m_run;
-      xch[(D / 2 + 1) * 64] = st.l_run;
-    }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    wg_barrier();
-    if (grp == 0 && wave_rows) {
-      const float m1 = xch[(D / 2) * 64], l1 = xch[(D / 2 + 1) * 64];
-      const float M = fmaxf(st.m_run, m1);
-      const float a0 = st.m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m_run - M);
-      const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
-      const float l_tot = xhalf_sum(st.l_run * a0 + l1 * a1);
+    // epilogue: normalise, LSE (natural log), write final output or a partial
+    if (wave_rows) {
+      const float l_tot = xhalf_sum(st.l_run);
       const float inv = 1.0f / l_tot;
-      const float lse_val = (M + log2f(l_tot)) * kLn2;
-      const float s0 = a0 * inv, s1 = a1 * inv;
+      const float lse_val = (st.m_run + log2f(l_tot)) * kLn2;
       const int row = q0 + l32;
       const bool whole = (t0 == 0) && (t1 == a.T);
       if (row < a.n) {
@@ -678,34 +664,30 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
           for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-              f32x4_t v4;
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                v4[e] = st.o[db][4 * g + e] * s0 + xch[(db * 16 + 4 * g + e) * 64] * s1;
+              f32x4_t v4 = {st.o[db][4 * g], st.o[db][4 * g + 1], st.o[db][4 * g + 2],
+                            st.o[db][4 * g + 3]};
+              v4 *= inv;
               *reinterpret_cast<bf16x4_t*>(op + 32 * db + 8 * g + 4 * hi) =
                   __builtin_convertvector(v4, bf16x4_t);
             }
           if (hi == 0 && a.lse) a.lse[(int64_t)h * a.n + row] = lse_val;
         } else {
           const int64_t jslot = (int64_t)w - first_wg_of((int64_t)u * a.T, I, a.P);
-          const int64_t prow = ((int64_t)u * a.jmax + jslot) * C::BM + wv * 32 + l32;
+          const int64_t prow = ((int64_t)u * a.jmax + jslot) * C::BM + (wave & 7) * 32 + l32;
           float* pp = a.part_o + prow * D;
 #pragma unroll
           for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-              f32x4_t v4;
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                v4[e] = st.o[db][4 * g + e] * s0 + xch[(db * 16 + 4 * g + e) * 64] * s1;
+              f32x4_t v4 = {st.o[db][4 * g], st.o[db][4 * g + 1], st.o[db][4 * g + 2],
+                            st.o[db][4 * g + 3]};
+              v4 *= inv;
               *reinterpret_cast<f32x4_t*>(pp + 32 * db + 8 * g + 4 * hi) = v4;
             }
           if (hi == 0) a.part_lse[prow] = lse_val;
         }
       }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    wg_barrier();  // the next unit's first requests reuse the LDS just read
     it += t1 - t0;
   }
 }
