@@ -152,6 +152,13 @@ int64_t choose_wgs(const bca_cache* c, Kern k, int64_t units, int64_t T, int32_t
   return std::max<int64_t>(1, std::min(I, target));
 }
 
+// fp8 cache: the current chunk's K and V quantised to e4m3, [H][n][d] each,
+// 256-byte aligned regions.
+size_t fp8_stage_bytes(const bca_cache_desc& d) {
+  const size_t one = ((size_t)d.num_heads * d.chunk_tokens * d.head_dim + 255) & ~(size_t)255;
+  return 2 * one;
+}
+
 size_t partial_bytes(int64_t units, int64_t jmax, int bm, int d) {
   // part_o [units][jmax][bm][d] fp32, then part_lse [units][jmax][bm] fp32,
   // each region 256-byte aligned
@@ -250,6 +257,8 @@ bca_status make_plan(const bca_cache* c, int32_t layer, const bca_window_spec* s
   p.jmax = pieces_bound(p.units, p.kv_tiles, p.wgs);
   p.merge = p.jmax > 1 ? 1 : 0;
   p.ws_bytes = p.merge ? partial_bytes(p.units, p.jmax, p.bm, d.head_dim) : 0;
+  p.stage_off = p.ws_bytes;
+  if (p.kern == Kern::FP8) p.ws_bytes += fp8_stage_bytes(d);
   return BCA_OK;
 }
 
@@ -403,6 +412,7 @@ size_t bca_attend_workspace_bytes(const bca_cache* c, const bca_window_spec* s) 
     int32_t jmax = pieces_bound(units, T, P);
     if (jmax > 1) worst = std::max(worst, partial_bytes(units, jmax, ts.bm, c->d.head_dim));
   }
+  if (k == Kern::FP8) worst += fp8_stage_bytes(c->d);
   return worst;
 }
 
@@ -432,6 +442,13 @@ bca_status bca_attend(const bca_cache* c, int32_t layer, const bca_window_spec* 
   a.q = q;
   a.kcur = k_cur;
   a.vcur = v_cur;
+  if (p.kern == Kern::FP8) {
+    a.kcur_in = k_cur;
+    a.vcur_in = v_cur;
+    char* stage = static_cast<char*>(workspace) + p.stage_off;
+    a.kcur = stage;
+    a.vcur = stage + fp8_stage_bytes(d) / 2;
+  }
   char* layer_k = c->mem + 2 * (size_t)layer * half_layer_bytes(d);
   a.kc = layer_k;
   a.vc = layer_k + half_layer_bytes(d);

@@ -41,7 +41,7 @@ inline TileShape tile_shape(Kern k) {
   switch (k) {
     case Kern::F32: return {64, 32};
     case Kern::BF16: return {256, 64};
-    case Kern::FP8: return {128, 64};
+    case Kern::FP8: return {256, 64};
   }
   return {128, 64};
 }
@@ -62,14 +62,17 @@ struct Plan {
   int32_t wgs;                      // work groups (P)
   int32_t jmax;                     // partial slots reserved per unit
   int32_t merge;                    // 1: some unit is split over work groups
+  size_t stage_off;                 // fp8 cache: offset of the current-chunk staging copy
   size_t ws_bytes;                  // workspace this call needs
 };
 
 // Arguments of the attention kernels (passed by value as kernel arguments).
 struct AttnArgs {
   const void* q;      // [n][H][d]
-  const void* kcur;   // [n][H][d]
-  const void* vcur;   // [n][H][d]
+  const void* kcur;   // [n][H][d]; fp8 cache: the staging copy [H][n][d] e4m3
+  const void* vcur;   // [n][H][d]; fp8 cache: the staging copy [H][n][d] e4m3
+  const void* kcur_in;  // fp8 cache: the caller's bf16 K of the chunk [n][H][d]
+  const void* vcur_in;
   const void* kc;     // this layer's K blocks: [H][S+R][n][d]
   const void* vc;     // this layer's V blocks
   void* o;            // [n][H][d]

@@ -203,6 +203,14 @@ struct Bf16Cfg {
   static constexpr int RPI = 1024 / ROWB;             // rows per wave-wide 16-byte load
   static constexpr int IPW = TILE_BYTES / 1024 / NW;  // such loads per wave per tensor
   static constexpr int LOADS = 2 * IPW;               // per wave per tile
+  // fp8 cache: raw e4m3 tiles (row = d bytes) are staged in LDS three tiles
+  // ahead and converted to the bf16 layout above one tile ahead; three bf16
+  // stages and three raw slots.
+  static constexpr int NSTAGE8 = 3;
+  static constexpr int RAW_TILE = BN * D;             // raw K (or V) of one tile
+  static constexpr int RAW_STAGE = 2 * RAW_TILE;
+  static constexpr int RAW_IPW = RAW_TILE / 1024 / NW;  // raw loads per wave per tensor
+  static constexpr int LOADS8 = 2 * RAW_IPW;
 };
 
 // Physical 16-byte chunk of logical chunk c in tile row r is c ^ swizzle(r).
@@ -348,6 +356,84 @@ __device__ __forceinline__ void bf16_fetch_tile(const AttnArgs& a, const HeadSrc
   }
 }
 
+// fp8 cache: requests the raw e4m3 rows of K and V of key tile `tile` into
+// one raw LDS slot (row-major, d bytes per row). Lane L of wave w covers row
+// RAW_IPW w (1024 / d) + L / (d / 16), 16 bytes at column 16 (L % (d / 16)),
+// so the rows a wave requests are the rows it later converts. Cache rows come
+// from the head's fp8 cache matrix, current-chunk rows from the head's block
+// of the fp8 staging copy of the chunk ([H][n][d]); rows past the visible keys
+// or the chunk read as zeros.
+template <int D>
+__device__ __forceinline__ void fp8_fetch_raw(const AttnArgs& a, int h, int tile, FetchRun& fr,
+                                              unsigned char* slot, int wave, int lane) {
+  using C = Bf16Cfg<D>;
+  static_assert(C::RAW_IPW == 1, "one raw load per wave per tensor");
+  constexpr int RPL = 1024 / D;  // rows per wave-wide load
+  const int r = wave * RPL + lane / (D / 16);
+  const int col = 16 * (lane % (D / 16));
+  unsigned char* kdst = slot + wave * 1024;
+  unsigned char* vdst = kdst + C::RAW_TILE;
+  if (tile < a.cache_tiles) {
+    const HeadSrc ks = head_src(a.kc, a.kcur, a, h, D, 1, 1);
+    const HeadSrc vs = head_src(a.vc, a.vcur, a, h, D, 1, 1);
+    const int j0 = tile * C::BN;
+    while (j0 >= fr.vend && fr.ri + 1 < a.nruns) fr = fetch_run_at(a, fr.ri + 1);
+    int phys;
+    if (j0 + C::BN <= fr.vend) {
+      phys = fr.phys + j0 - fr.vstart + r;
+    } else {
+      const int j = j0 + r;
+      phys = -1;
+      for (int rr = fr.ri; rr < a.nruns; ++rr) {
+        const Run R = a.runs[rr];
+        if (R.vstart >= j0 + C::BN) break;
+        if (j >= R.vstart && j < R.vstart + R.len) phys = R.phys + j - R.vstart;
+      }
+    }
+    const int off = phys >= 0 ? phys * D + col : kOob;
+    lds_load16(ks.cache, ks.cache_bytes, off, kdst);
+    lds_load16(vs.cache, vs.cache_bytes, off, vdst);
+  } else {
+    // staging copy: head h's rows at a.kcur + h n d (row stride d)
+    const char* kb = uniform_ptr(static_cast<const char*>(a.kcur) + (int64_t)h * a.n * D);
+    const char* vb = uniform_ptr(static_cast<const char*>(a.vcur) + (int64_t)h * a.n * D);
+    const int row = (tile - a.cache_tiles) * C::BN + r;
+    const int off = row < a.n ? row * D + col : kOob;
+    lds_load16(kb, a.n * D, off, kdst);
+    lds_load16(vb, a.n * D, off, vdst);
+  }
+}
+
+// Converts the raw tile in `slot` to the bf16 stage layout (swizzled rows of
+// 2 d bytes; e4m3 values are exact in bf16). Thread t converts row t / (d/16),
+// 16 values at dims 16 (t % (d/16)) .., which its own wave requested.
+template <int D>
+__device__ __forceinline__ void fp8_convert(const unsigned char* slot, unsigned char* stage,
+                                            int tid) {
+  using C = Bf16Cfg<D>;
+  const int r = tid / (D / 16), j = tid % (D / 16);
+#pragma unroll
+  for (int tensor = 0; tensor < 2; ++tensor) {
+    const uint4 raw =
+        *reinterpret_cast<const uint4*>(slot + tensor * C::RAW_TILE + r * D + 16 * j);
+    const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t out[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w4[i], 1.0f, false));
+      out[2 * i + 1] = __builtin_bit_cast(
+          uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w4[i], 1.0f, true));
+    }
+    const int sw = tensor == 0 ? k_swizzle<D>(r) : v_swizzle<D>(r);
+    unsigned char* row = stage + tensor * C::TILE_BYTES + r * C::ROWB;
+    *reinterpret_cast<uint4*>(row + (((2 * j) ^ sw) << 4)) =
+        make_uint4(out[0], out[1], out[2], out[3]);
+    *reinterpret_cast<uint4*>(row + (((2 * j + 1) ^ sw) << 4)) =
+        make_uint4(out[4], out[5], out[6], out[7]);
+  }
+}
+
 // Keys of `tile` that are real (the rest of the tile is padding).
 __device__ __forceinline__ int tile_valid(const AttnArgs& a, int tile, int bn) {
   if (tile < a.cache_tiles) return min(bn, a.nk_cache - tile * bn);
@@ -480,10 +566,17 @@ __device__ __forceinline__ void pp_softmax(PPState<D>& st, int lim, int hi, floa
   st.pf[3] = __builtin_convertvector(p1.hi, bf16x8_t);
 }
 
-template <int D>
+// KV8: the cache holds fp8 e4m3 K/V with per-head scales (k_scale folded into
+// the softmax scale, v_scale into the output) and the current chunk comes as
+// an fp8 staging copy; tiles are converted to bf16 in LDS (see fp8_fetch_raw,
+// fp8_convert) and the MFMA work is the bf16 kernel's.
+template <int D, bool KV8>
 __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
   using C = Bf16Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::NSTAGE * C::STAGE];
+  constexpr int LDS_BYTES =
+      KV8 ? C::NSTAGE8 * C::STAGE + C::NSTAGE8 * C::RAW_STAGE : C::NSTAGE * C::STAGE;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
+  unsigned char* const raw = smem + C::NSTAGE8 * C::STAGE;  // fp8 raw slots (KV8)
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -512,7 +605,6 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
       voff[db] = C::TILE_BYTES + (4 * hi + k) * C::ROWB + ((4 * (db ^ kx) + c0) << 4) +
                  (ai & 1) * 8;
   }
-  const float c = a.scale_log2;
   const FetchLane<D> fl = fetch_lane<D>(wave, lane);
 
   while (it < it_end) {
@@ -526,10 +618,18 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
     const bool wave_rows = q0 < a.n;
     const HeadSrc ksrc = head_src(a.kc, a.kcur, a, h, D, 2, 2);
     const HeadSrc vsrc = head_src(a.vc, a.vcur, a, h, D, 2, 2);
+    // base-2 softmax scale; with an fp8 cache it includes the head's K scale
+    const float c = KV8 ? a.scale_log2 * a.k_scale[h] : a.scale_log2;
 
     FetchRun fr = fetch_run_at(a, 0);
-    bf16_fetch_tile<D>(a, ksrc, vsrc, t0, fr, fl, smem, wave);
-    if (nt > 1) bf16_fetch_tile<D>(a, ksrc, vsrc, t0 + 1, fr, fl, smem + C::STAGE, wave);
+    if constexpr (KV8) {
+      // raw tiles 0-2 (slots 0-2); tile 0 is converted once they are in
+      for (int r = 0; r < 3 && r < nt; ++r)
+        fp8_fetch_raw<D>(a, h, t0 + r, fr, raw + r * C::RAW_STAGE, wave, lane);
+    } else {
+      bf16_fetch_tile<D>(a, ksrc, vsrc, t0, fr, fl, smem, wave);
+      if (nt > 1) bf16_fetch_tile<D>(a, ksrc, vsrc, t0 + 1, fr, fl, smem + C::STAGE, wave);
+    }
 
     // Q^T fragments (B operand): lane holds query q0+l32, dims 16kk+8hi .. +7;
     // rows past the chunk read as zeros (out-of-range buffer offsets).
@@ -549,6 +649,10 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
     // vector-memory waits in the loop, where the only loads in flight are the
     // tile requests this kernel waits for itself.
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    if constexpr (KV8) {
+      fp8_convert<D>(raw, smem, tid);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
 
     PPState<D> st;
 #pragma unroll
@@ -560,25 +664,50 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
     st.m_run = -INFINITY;
     st.l_run = 0.f;
 
-    // Phase k: even phases 2r start by requesting tile r+2; odd phases 2q-1 end
-    // by waiting for this wave's requests of tile q (read from phase 2q on).
+    // bf16: even phases 2r start by requesting tile r+2; odd phases 2q-1 end by
+    // waiting for this wave's requests of tile q (read from phase 2q on).
+    // fp8: even phases 2r start by converting tile r+1 (raw slot and bf16
+    // stage (r+1) % 3) and requesting raw tile r+3; odd phases 2r-1 end by
+    // waiting for the raw requests of tile r+1; even phases end by waiting for
+    // the conversion's LDS writes.
     auto begin_phase = [&](int k) {
-      if ((k & 1) == 0 && (k >> 1) + 2 < nt) {
-        const int r = (k >> 1) + 2;
-        bf16_fetch_tile<D>(a, ksrc, vsrc, t0 + r, fr, fl, smem + (r & 3) * C::STAGE, wave);
+      if ((k & 1) != 0) return;
+      const int r = k >> 1;
+      if constexpr (KV8) {
+        if (r + 1 < nt)
+          fp8_convert<D>(raw + ((r + 1) % 3) * C::RAW_STAGE, smem + ((r + 1) % 3) * C::STAGE,
+                         tid);
+        if (r + 3 < nt)
+          fp8_fetch_raw<D>(a, h, t0 + r + 3, fr, raw + (r % 3) * C::RAW_STAGE, wave, lane);
+      } else {
+        if (r + 2 < nt)
+          bf16_fetch_tile<D>(a, ksrc, vsrc, t0 + r + 2, fr, fl, smem + ((r + 2) & 3) * C::STAGE,
+                             wave);
       }
     };
     auto end_phase = [&](int k) {
       const int q = (k + 1) >> 1;
-      if ((k & 1) == 1 && q < nt) {
-        if (q + 1 < nt)
-          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::LOADS) : "memory");
-        else
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if constexpr (KV8) {
+        if ((k & 1) == 1 && q + 1 < nt) {
+          if (q + 2 < nt)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::LOADS8) : "memory");
+          else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        if ((k & 1) == 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      } else {
+        if ((k & 1) == 1 && q < nt) {
+          if (q + 1 < nt)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::LOADS) : "memory");
+          else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
       }
       wg_barrier();
     };
-    auto stage = [&](int r) -> const unsigned char* { return smem + (r & 3) * C::STAGE; };
+    auto stage = [&](int r) -> const unsigned char* {
+      return smem + (KV8 ? r % 3 : r & 3) * C::STAGE;
+    };
 
     wg_barrier();
 
@@ -653,7 +782,8 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
     // epilogue: normalise, LSE (natural log), write final output or a partial
     if (wave_rows) {
       const float l_tot = xhalf_sum(st.l_run);
-      const float inv = 1.0f / l_tot;
+      // with an fp8 cache O is in units of the head's V scale
+      const float inv = (KV8 ? a.v_scale[h] : 1.0f) / l_tot;
       const float lse_val = (st.m_run + log2f(l_tot)) * kLn2;
       const int row = q0 + l32;
       const bool whole = (t0 == 0) && (t1 == a.T);
@@ -935,7 +1065,31 @@ template <int D>
 int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
   switch (p.kern) {
     case Kern::BF16:
-      hipLaunchKernelGGL(attn_bf16_kernel<D>, dim3(p.wgs), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((attn_bf16_kernel<D, false>), dim3(p.wgs), dim3(512), 0, s, a);
+      break;
+    case Kern::FP8:
+      if constexpr (D == 128) {
+        // quantise the current chunk into the staging copy first, exactly as
+        // appending it to the cache would
+        AppendArgs q;
+        q.k = a.kcur_in;
+        q.v = a.vcur_in;
+        q.kdst = const_cast<void*>(a.kcur);
+        q.vdst = const_cast<void*>(a.vcur);
+        q.head_stride_elems = (int64_t)a.n * D;
+        q.n = a.n;
+        q.H = a.H;
+        for (int i = 0; i < kMaxHeadsFp8; ++i) {
+          q.k_scale[i] = a.k_scale[i];
+          q.v_scale[i] = a.v_scale[i];
+        }
+        const int64_t total = (int64_t)a.n * a.H * (D / 8);
+        hipLaunchKernelGGL(append_fp8_kernel<D>, dim3((unsigned)((total + 255) / 256), 2),
+                           dim3(256), 0, s, q);
+        hipLaunchKernelGGL((attn_bf16_kernel<D, true>), dim3(p.wgs), dim3(512), 0, s, a);
+      } else {
+        return -1;
+      }
       break;
     case Kern::F32:
       hipLaunchKernelGGL(attn_f32_kernel<D>, dim3(p.wgs), dim3(128), 0, s, a);
@@ -975,7 +1129,6 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
 
 int launch_attention(const Plan& p, const AttnArgs& a, int head_dim, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (p.kern == Kern::FP8) return -1;
   if (head_dim == 64) return launch_attention_d<64>(p, a, s);
   if (head_dim == 128) return launch_attention_d<128>(p, a, s);
   return -1;

@@ -30,31 +30,66 @@ def to_np(t) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 
 
+_E4M3 = None
+
+
+def e4m3_table():
+    """Value of every e4m3 code, from the oracle's decoder."""
+    global _E4M3
+    if _E4M3 is None:
+        _E4M3 = oracle.e4m3_decode(np.arange(256, dtype=np.uint8))
+    return _E4M3
+
+
+def fp8_stored(x, scales):
+    """What an fp8 cache holds for x [n][H][d] (bf16 values), dequantised:
+    decode(quant(x / s_h)) * s_h per head, with the oracle's quantiser."""
+    tab = e4m3_table()
+    out = np.empty(x.shape, dtype=np.float64)
+    for h in range(x.shape[1]):
+        out[:, h, :] = tab[oracle.quant_e4m3(x[:, h, :], scales[h])] * scales[h]
+    return out
+
+
 class Sequence:
     """Drives one cache layer through chunk steps and keeps the committed
-    history the oracle needs (every chunk appended, keyed by id)."""
+    history the oracle needs (every chunk appended, keyed by id). With an fp8
+    cache and `scales` = (k_scale[H], v_scale[H]) set, `history`/`ref` hold
+    what the cache stores (dequantised) and `history_raw`/`ref_raw` the
+    appended values themselves."""
 
-    def __init__(self, cache, H, d, n, dtype, seed_layer=0, outlier_frac=0.0):
+    def __init__(self, cache, H, d, n, dtype, seed_layer=0, outlier_frac=0.0, scales=None):
         self.cache = cache
         self.H, self.d, self.n = H, d, n
         self.dtype = dtype  # "fp32" | "bf16" | "fp8" (bf16 inputs, fp8 cache)
         self.in_dtype = "fp32" if dtype == "fp32" else "bf16"
         self.seed_layer = seed_layer
         self.outlier_frac = outlier_frac
+        self.scales = scales
         self.history = {}
+        self.history_raw = {}
         self.ref = None
+        self.ref_raw = None
+        if scales is not None:
+            cache.set_kv_scales(0, scales[0], scales[1])
 
     def chunk(self, t, step=0):
         return synth.qkv(self.n, self.H, self.d, self.seed_layer, t, step, dtype=self.in_dtype,
                          outlier_frac=self.outlier_frac)
 
+    def stored(self, k, v):
+        if self.dtype == "fp8" and self.scales is not None:
+            return fp8_stored(k, self.scales[0]), fp8_stored(v, self.scales[1])
+        return k.astype(np.float64), v.astype(np.float64)
+
     def append(self, layer, t, k, v, is_ref=False):
         self.cache.append_chunk(layer, t, to_dev(k, self.dtype), to_dev(v, self.dtype),
                                 is_ref=is_ref)
+        raw = (k.astype(np.float64), v.astype(np.float64))
         if is_ref:
-            self.ref = (k.astype(np.float64), v.astype(np.float64))
+            self.ref, self.ref_raw = self.stored(k, v), raw
         else:
-            self.history[t] = (k.astype(np.float64), v.astype(np.float64))
+            self.history[t], self.history_raw[t] = self.stored(k, v), raw
 
     def attend(self, layer, t, q, k, v, W, use_ref=False, G=0, scale=None):
         spec = self.cache.spec(t, W, use_ref=use_ref, num_segments=G, scale=scale)
@@ -62,10 +97,19 @@ class Sequence:
                                    to_dev(v, self.dtype), spec)
         return to_np(o), to_np(lse), spec
 
-    def expected(self, t, q, k, v, W, use_ref=False, scale=None, history=None):
+    def expected(self, t, q, k, v, W, use_ref=False, scale=None, history=None, raw=False):
+        """The oracle on the same inputs. With an fp8 cache the chunk attends to
+        cache-precision keys and values, its own included (the kernel
+        quantises the current chunk as appending it would); raw=True uses the
+        unquantised values instead."""
         scale = 1.0 / math.sqrt(self.d) if scale is None else scale
+        if raw:
+            hist = self.history_raw if history is None else history
+            return oracle.attend(q, k, v, hist, t=t, W=W, scale=scale, ref=self.ref_raw,
+                                 use_ref=use_ref)
         hist = self.history if history is None else history
-        return oracle.attend(q, k, v, hist, t=t, W=W, scale=scale, ref=self.ref,
+        kk, vv = self.stored(k, v)
+        return oracle.attend(q, kk, vv, hist, t=t, W=W, scale=scale, ref=self.ref,
                              use_ref=use_ref)
 
 

@@ -284,3 +284,18 @@ def test_one_hip_runtime_per_process():
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
                        timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
+
+
+def test_fp8_cache_plan_needs_the_chunk_copy():
+    """An fp8 cache attends over the current chunk quantised into the
+    workspace, so even an unsplit plan needs 2 H n d bytes of workspace."""
+    H, d, n = 2, 128, 64
+    h, _ = make(S=2, dt=bca.FP8_E4M3, d=d, H=H, n=n, L=1)
+    spec = bca.bca_window_spec(0, 2, 0, 1, 0.088)
+    p = bca.bca_attend_plan(h, 0, spec)
+    assert p["merge"] == 0 and p["workspace_bytes"] >= 2 * H * n * d
+    assert bca.bca_attend_workspace_bytes(h, spec) >= p["workspace_bytes"]
+    with pytest.raises(BcaError) as e:
+        bca.bca_attend(h, 0, spec, FAKE, FAKE, FAKE, bca.BF16, FAKE, 0, 0, 0, 0)
+    assert e.value.status == -3
+    bca.bca_cache_destroy(h)

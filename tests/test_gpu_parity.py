@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import synth
-from bca_harness import TOL, Sequence, assert_close, log, to_dev, to_np
+from bca_harness import TOL, Sequence, assert_close, log, max_err, to_dev, to_np
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -220,6 +220,83 @@ def test_append_fp8_codes_match_oracle_quantiser():
         for h in range(H):
             assert np.array_equal(kc[h], oracle.quant_e4m3(k[:, h, :], ks[h])), h
             assert np.array_equal(vc[h], oracle.quant_e4m3(v[:, h, :], vs[h])), h
+
+
+# ---------------------------------------------------------------------------
+# fp8 e4m3 K/V cache with per-head scales: the cache holds decode(quant(x/s))*s
+# and the chunk attends at that precision, its own keys and values included.
+# The oracle attends over the same inputs the kernel does, the cache contents,
+# and the kernel is held to the fp8 bound (5e-2) and, tighter, to the error
+# its bf16 steps can make: P rounded to bf16 (relative 2^-9, at most
+# 2^-9 max|V| on O) and O rounded to bf16 (2^-9 |O| <= 2^-9 max|V|), so
+# 2^-8 max|V| in all (the data carry 8-sigma outliers, max|V| ~ 8), with the
+# bf16 bound as a floor. How far the quantised attention is from attention over
+# the unquantised values is e4m3's own error, not the kernel's: it is logged,
+# not asserted.
+def fp8_scales(H, kmax=8.0, vmax=8.0):
+    return ([kmax / 448.0 * (1.0 + 0.1 * h) for h in range(H)],
+            [vmax / 448.0 * (1.0 + 0.05 * h) for h in range(H)])
+
+
+def fp8_cache_tol(seq, v):
+    vmax = max([np.abs(v).max()] + [np.abs(b[1]).max() for b in seq.history.values()] +
+               ([np.abs(seq.ref[1]).max()] if seq.ref is not None else []))
+    return min(TOL["fp8"], max(TOL["bf16"], vmax * 2.0 ** -8 * 1.05))
+
+
+def log_quantisation_error(o, lse, ro, rl, what):
+    log(f"{what}: e4m3 quantisation moves O by {max_err(o, ro):.3e}, LSE by "
+        f"{max_err(lse, rl):.3e} against the unquantised values (reported, not asserted)")
+
+
+@pytest.mark.parametrize("G", [0, 1, 3])
+def test_fp8_sequence(G):
+    H, d, n, S, W = 4, 128, 100, 3, 2
+    cache = new_cache(1, H, d, n, S, R=True, dtype="fp8")
+    seq = Sequence(cache, H, d, n, "fp8", seed_layer=21, outlier_frac=0.01,
+                   scales=fp8_scales(H))
+    _, rk, rv = seq.chunk(90_000)
+    seq.append(0, 0, rk, rv, is_ref=True)
+    for t in range(1, 7):
+        q, k, v = seq.chunk(t)
+        use_ref = t % 2 == 0
+        o, lse, _ = seq.attend(0, t, q, k, v, W, use_ref=use_ref, G=G)
+        eo, el = seq.expected(t, q, k, v, W, use_ref=use_ref)
+        assert_close(o, lse, eo, el, fp8_cache_tol(seq, v), f"fp8 G={G} t={t} (cache precision)")
+        ro, rl = seq.expected(t, q, k, v, W, use_ref=use_ref, raw=True)
+        log_quantisation_error(o, lse, ro, rl, f"fp8 G={G} t={t}")
+        seq.append(0, t, k, v)
+
+
+def test_fp8_workspace_holds_the_chunk_copy():
+    H, d, n, S = 2, 128, 64, 2
+    cache = new_cache(1, H, d, n, S, dtype="fp8")
+    spec = cache.spec(0, 2, num_segments=1)
+    plan = cache.plan(0, spec)
+    # one work group per unit, yet the workspace is needed for the fp8 copy
+    assert plan["merge"] == 0 and plan["workspace_bytes"] >= 2 * H * n * d
+
+
+def test_cfg4_full_size():
+    # config-2 shapes over an fp8 cache with 1% outliers of 8 sigma
+    H, d, n, S, W = 24, 128, 405, 20, 20
+    cache = new_cache(1, H, d, n, S, R=True, dtype="fp8")
+    seq = Sequence(cache, H, d, n, "fp8", seed_layer=4, outlier_frac=0.01,
+                   scales=([8.0 / 448.0] * H, [8.0 / 448.0] * H))
+    _, rk, rv = seq.chunk(100_000)
+    seq.append(0, 0, rk, rv, is_ref=True)
+    for t in range(5, 25):
+        _, k, v = seq.chunk(t)
+        seq.append(0, t, k, v)
+    q, k, v = seq.chunk(25)
+    log("cfg4: oracle ...")
+    eo, el = seq.expected(25, q, k, v, W, use_ref=True)
+    ro, rl = seq.expected(25, q, k, v, W, use_ref=True, raw=True)
+    tol = fp8_cache_tol(seq, v)
+    for G in (4, 0):
+        o, lse, _ = seq.attend(0, 25, q, k, v, W, use_ref=True, G=G)
+        assert_close(o, lse, eo, el, tol, f"cfg4 full size G={G} (cache precision)")
+        log_quantisation_error(o, lse, ro, rl, f"cfg4 full size G={G}")
 
 
 def test_slot_table_over_64_chunks():
