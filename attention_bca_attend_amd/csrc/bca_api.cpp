@@ -145,10 +145,17 @@ int32_t pieces_bound(int64_t units, int64_t T, int64_t P) {
   return (int32_t)worst;
 }
 
+// Work groups of a launch. num_segments = G >= 1: every unit in G equal
+// segments. Automatic: when the units fit on the device, every unit in the
+// same number of equal segments, as many as fit (no work group then crosses
+// a unit boundary, and each unit has the fewest partial outputs to merge);
+// otherwise one range of tile iterations per resident work group
+// ("stream-K").
 int64_t choose_wgs(const bca_cache* c, Kern k, int64_t units, int64_t T, int32_t G) {
   const int64_t I = units * T;
   if (G >= 1) return units * std::min<int64_t>(G, T);
-  int64_t target = (int64_t)compute_units(c) * wgs_per_cu(k);
+  const int64_t target = (int64_t)compute_units(c) * wgs_per_cu(k);
+  if (units <= target) return units * std::min<int64_t>(T, target / units);
   return std::max<int64_t>(1, std::min(I, target));
 }
 
