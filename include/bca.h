@@ -149,7 +149,15 @@ size_t bca_attend_workspace_bytes(const bca_cache* cache, const bca_window_spec*
  * itself is therefore not visible.
  * o: device [n][H][d] in qkv_dtype. lse: device fp32 [H][n], may be NULL.
  * workspace: device, at least bca_attend_workspace_bytes(); may be NULL when
- * that is 0.
+ * that is 0. It holds the fp32 partial outputs of a split window and, on an
+ * FP8_E4M3 cache, the e4m3 copy of the current chunk's K and V ([H][n][d] each,
+ * quantised with the layer's per-head scales, so the chunk attends to itself
+ * through the same codec as the cached chunks); an FP8_E4M3 cache always
+ * needs one. Its content between calls is irrelevant; calls in flight at the
+ * same time need separate workspaces.
+ * FP8_E4M3 cache: the e4m3 keys and values are widened to bf16 exactly and
+ * contracted on the bf16 matrix cores; the K scale is folded into the softmax
+ * scale and the V scale into the output normalisation.
  * Errors: BCA_ERR_OUT_OF_ORDER when a chunk of the window may already have been
  * overwritten (the layer's newest ring id >= t - W + S).
  * The visible set is resolved on the host from the slot table's chunk ids each
