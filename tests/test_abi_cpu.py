@@ -186,6 +186,20 @@ def test_workspace_covers_every_occupancy():
     bca.bca_cache_destroy(h)
 
 
+def test_workspace_only_for_split_units():
+    """An unsplit bf16 plan needs no workspace; a split one holds the fp32
+    partial outputs and LSEs of every piece."""
+    h, _ = make(S=2, dt=bca.BF16, d=128, n=1536, H=12, L=1)
+    for c in range(3, 5):
+        bca.bca_cache_set_slot_chunk(h, 0, c % 2, c)
+    p1 = bca.bca_attend_plan(h, 0, bca.bca_window_spec(5, 2, 0, 1, 0.088))
+    assert p1["merge"] == 0 and p1["workspace_bytes"] == 0
+    p3 = bca.bca_attend_plan(h, 0, bca.bca_window_spec(5, 2, 0, 3, 0.088))
+    partial = p3["units"] * 3 * 256 * (128 + 1) * 4
+    assert p3["merge"] == 1 and p3["workspace_bytes"] >= partial
+    bca.bca_cache_destroy(h)
+
+
 def test_append_errors_before_launch():
     h, _ = make(S=2, R=0, dt=bca.BF16, d=128, H=2, n=16)
     P = FAKE

@@ -173,6 +173,23 @@ def test_deterministic():
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+def test_stream_k_ranges_cross_units():
+    """More units than work groups: ranges of tile iterations cross unit
+    boundaries, so one work group finishes the end of one unit and starts the
+    next, and units are split at uneven points."""
+    H, d, n, S, W = 130, 64, 257, 1, 1
+    cache = new_cache(1, H, d, n, S)
+    seq = Sequence(cache, H, d, n, "bf16", seed_layer=8)
+    _, k0, v0 = seq.chunk(0)
+    seq.append(0, 0, k0, v0)
+    q, k, v = seq.chunk(1)
+    plan = cache.plan(0, cache.spec(1, W))
+    assert plan["units"] > plan["workgroups"] and plan["merge"] == 1, plan
+    o, lse, _ = seq.attend(0, 1, q, k, v, W)
+    eo, el = seq.expected(1, q, k, v, W)
+    assert_close(o, lse, eo, el, TOL["bf16"], f"stream-K {plan['units']} units")
+
+
 # ---------------------------------------------------------------------------
 # append: cache bytes are the input rows, bit for bit (fp8: the oracle's codes)
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
