@@ -138,14 +138,7 @@ __device__ __forceinline__ int advance_run(const AttnArgs& a, int ri, int j0) {
   return ri;
 }
 
-__device__ __forceinline__ uint32_t u4_get(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
-__device__ __forceinline__ float wave_swap32_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
-__device__ __forceinline__ float wave_swap32_sum(float x) { return x + __shfl_xor(x, 32); }
-
-// The same pair reductions over lanes l and l^32 on the vector ALU:
+// Max and sum over the lane pair l, l^32 (the two halves of a row's keys):
 // v_permlane32_swap exchanges the upper half of one operand with the lower
 // half of the other, so with both operands x every lane ends up holding x of
 // itself and of its partner (in either order), which is all a max or a sum
@@ -203,14 +196,6 @@ struct Bf16Cfg {
   static constexpr int RPI = 1024 / ROWB;             // rows per wave-wide 16-byte load
   static constexpr int IPW = TILE_BYTES / 1024 / NW;  // such loads per wave per tensor
   static constexpr int LOADS = 2 * IPW;               // per wave per tile
-  // fp8 cache: raw e4m3 tiles (row = d bytes) are staged in LDS three tiles
-  // ahead and converted to the bf16 layout above one tile ahead; three bf16
-  // stages and three raw slots.
-  static constexpr int NSTAGE8 = 3;
-  static constexpr int RAW_TILE = BN * D;             // raw K (or V) of one tile
-  static constexpr int RAW_STAGE = 2 * RAW_TILE;
-  static constexpr int RAW_IPW = RAW_TILE / 1024 / NW;  // raw loads per wave per tensor
-  static constexpr int LOADS8 = 2 * RAW_IPW;
 };
 
 // Physical 16-byte chunk of logical chunk c in tile row r is c ^ swizzle(r).
@@ -356,84 +341,6 @@ __device__ __forceinline__ void bf16_fetch_tile(const AttnArgs& a, const HeadSrc
   }
 }
 
-// fp8 cache: requests the raw e4m3 rows of K and V of key tile `tile` into
-// one raw LDS slot (row-major, d bytes per row). Lane L of wave w covers row
-// RAW_IPW w (1024 / d) + L / (d / 16), 16 bytes at column 16 (L % (d / 16)),
-// so the rows a wave requests are the rows it later converts. Cache rows come
-// from the head's fp8 cache matrix, current-chunk rows from the head's block
-// of the fp8 staging copy of the chunk ([H][n][d]); rows past the visible keys
-// or the chunk read as zeros.
-template <int D>
-__device__ __forceinline__ void fp8_fetch_raw(const AttnArgs& a, int h, int tile, FetchRun& fr,
-                                              unsigned char* slot, int wave, int lane) {
-  using C = Bf16Cfg<D>;
-  static_assert(C::RAW_IPW == 1, "one raw load per wave per tensor");
-  constexpr int RPL = 1024 / D;  // rows per wave-wide load
-  const int r = wave * RPL + lane / (D / 16);
-  const int col = 16 * (lane % (D / 16));
-  unsigned char* kdst = slot + wave * 1024;
-  unsigned char* vdst = kdst + C::RAW_TILE;
-  if (tile < a.cache_tiles) {
-    const HeadSrc ks = head_src(a.kc, a.kcur, a, h, D, 1, 1);
-    const HeadSrc vs = head_src(a.vc, a.vcur, a, h, D, 1, 1);
-    const int j0 = tile * C::BN;
-    while (j0 >= fr.vend && fr.ri + 1 < a.nruns) fr = fetch_run_at(a, fr.ri + 1);
-    int phys;
-    if (j0 + C::BN <= fr.vend) {
-      phys = fr.phys + j0 - fr.vstart + r;
-    } else {
-      const int j = j0 + r;
-      phys = -1;
-      for (int rr = fr.ri; rr < a.nruns; ++rr) {
-        const Run R = a.runs[rr];
-        if (R.vstart >= j0 + C::BN) break;
-        if (j >= R.vstart && j < R.vstart + R.len) phys = R.phys + j - R.vstart;
-      }
-    }
-    const int off = phys >= 0 ? phys * D + col : kOob;
-    lds_load16(ks.cache, ks.cache_bytes, off, kdst);
-    lds_load16(vs.cache, vs.cache_bytes, off, vdst);
-  } else {
-    // staging copy: head h's rows at a.kcur + h n d (row stride d)
-    const char* kb = uniform_ptr(static_cast<const char*>(a.kcur) + (int64_t)h * a.n * D);
-    const char* vb = uniform_ptr(static_cast<const char*>(a.vcur) + (int64_t)h * a.n * D);
-    const int row = (tile - a.cache_tiles) * C::BN + r;
-    const int off = row < a.n ? row * D + col : kOob;
-    lds_load16(kb, a.n * D, off, kdst);
-    lds_load16(vb, a.n * D, off, vdst);
-  }
-}
-
-// Converts the raw tile in `slot` to the bf16 stage layout (swizzled rows of
-// 2 d bytes; e4m3 values are exact in bf16). Thread t converts row t / (d/16),
-// 16 values at dims 16 (t % (d/16)) .., which its own wave requested.
-template <int D>
-__device__ __forceinline__ void fp8_convert(const unsigned char* slot, unsigned char* stage,
-                                            int tid) {
-  using C = Bf16Cfg<D>;
-  const int r = tid / (D / 16), j = tid % (D / 16);
-#pragma unroll
-  for (int tensor = 0; tensor < 2; ++tensor) {
-    const uint4 raw =
-        *reinterpret_cast<const uint4*>(slot + tensor * C::RAW_TILE + r * D + 16 * j);
-    const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
-    uint32_t out[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      out[2 * i] = __builtin_bit_cast(
-          uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w4[i], 1.0f, false));
-      out[2 * i + 1] = __builtin_bit_cast(
-          uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w4[i], 1.0f, true));
-    }
-    const int sw = tensor == 0 ? k_swizzle<D>(r) : v_swizzle<D>(r);
-    unsigned char* row = stage + tensor * C::TILE_BYTES + r * C::ROWB;
-    *reinterpret_cast<uint4*>(row + (((2 * j) ^ sw) << 4)) =
-        make_uint4(out[0], out[1], out[2], out[3]);
-    *reinterpret_cast<uint4*>(row + (((2 * j + 1) ^ sw) << 4)) =
-        make_uint4(out[4], out[5], out[6], out[7]);
-  }
-}
-
 // Keys of `tile` that are real (the rest of the tile is padding).
 __device__ __forceinline__ int tile_valid(const AttnArgs& a, int tile, int bn) {
   if (tile < a.cache_tiles) return min(bn, a.nk_cache - tile * bn);
@@ -566,17 +473,10 @@ __device__ __forceinline__ void pp_softmax(PPState<D>& st, int lim, int hi, floa
   st.pf[3] = __builtin_convertvector(p1.hi, bf16x8_t);
 }
 
-// KV8: the cache holds fp8 e4m3 K/V with per-head scales (k_scale folded into
-// the softmax scale, v_scale into the output) and the current chunk comes as
-// an fp8 staging copy; tiles are converted to bf16 in LDS (see fp8_fetch_raw,
-// fp8_convert) and the MFMA work is the bf16 kernel's.
-template <int D, bool KV8>
+template <int D>
 __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
   using C = Bf16Cfg<D>;
-  constexpr int LDS_BYTES =
-      KV8 ? C::NSTAGE8 * C::STAGE + C::NSTAGE8 * C::RAW_STAGE : C::NSTAGE * C::STAGE;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[LDS_BYTES];
-  unsigned char* const raw = smem + C::NSTAGE8 * C::STAGE;  // fp8 raw slots (KV8)
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::NSTAGE * C::STAGE];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -618,18 +518,11 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
     const bool wave_rows = q0 < a.n;
     const HeadSrc ksrc = head_src(a.kc, a.kcur, a, h, D, 2, 2);
     const HeadSrc vsrc = head_src(a.vc, a.vcur, a, h, D, 2, 2);
-    // base-2 softmax scale; with an fp8 cache it includes the head's K scale
-    const float c = KV8 ? a.scale_log2 * a.k_scale[h] : a.scale_log2;
+    const float c = a.scale_log2;  // base-2 softmax scale
 
     FetchRun fr = fetch_run_at(a, 0);
-    if constexpr (KV8) {
-      // raw tiles 0-2 (slots 0-2); tile 0 is converted once they are in
-      for (int r = 0; r < 3 && r < nt; ++r)
-        fp8_fetch_raw<D>(a, h, t0 + r, fr, raw + r * C::RAW_STAGE, wave, lane);
-    } else {
-      bf16_fetch_tile<D>(a, ksrc, vsrc, t0, fr, fl, smem, wave);
-      if (nt > 1) bf16_fetch_tile<D>(a, ksrc, vsrc, t0 + 1, fr, fl, smem + C::STAGE, wave);
-    }
+    bf16_fetch_tile<D>(a, ksrc, vsrc, t0, fr, fl, smem, wave);
+    if (nt > 1) bf16_fetch_tile<D>(a, ksrc, vsrc, t0 + 1, fr, fl, smem + C::STAGE, wave);
 
     // Q^T fragments (B operand): lane holds query q0+l32, dims 16kk+8hi .. +7;
     // rows past the chunk read as zeros (out-of-range buffer offsets).
@@ -649,10 +542,6 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
     // vector-memory waits in the loop, where the only loads in flight are the
     // tile requests this kernel waits for itself.
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
-    if constexpr (KV8) {
-      fp8_convert<D>(raw, smem, tid);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    }
 
     PPState<D> st;
 #pragma unroll
@@ -664,50 +553,25 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
     st.m_run = -INFINITY;
     st.l_run = 0.f;
 
-    // bf16: even phases 2r start by requesting tile r+2; odd phases 2q-1 end by
+    // Even phases 2r start by requesting tile r+2; odd phases 2q-1 end by
     // waiting for this wave's requests of tile q (read from phase 2q on).
-    // fp8: even phases 2r start by converting tile r+1 (raw slot and bf16
-    // stage (r+1) % 3) and requesting raw tile r+3; odd phases 2r-1 end by
-    // waiting for the raw requests of tile r+1; even phases end by waiting for
-    // the conversion's LDS writes.
     auto begin_phase = [&](int k) {
-      if ((k & 1) != 0) return;
       const int r = k >> 1;
-      if constexpr (KV8) {
-        if (r + 1 < nt)
-          fp8_convert<D>(raw + ((r + 1) % 3) * C::RAW_STAGE, smem + ((r + 1) % 3) * C::STAGE,
-                         tid);
-        if (r + 3 < nt)
-          fp8_fetch_raw<D>(a, h, t0 + r + 3, fr, raw + (r % 3) * C::RAW_STAGE, wave, lane);
-      } else {
-        if (r + 2 < nt)
-          bf16_fetch_tile<D>(a, ksrc, vsrc, t0 + r + 2, fr, fl, smem + ((r + 2) & 3) * C::STAGE,
-                             wave);
-      }
+      if ((k & 1) == 0 && r + 2 < nt)
+        bf16_fetch_tile<D>(a, ksrc, vsrc, t0 + r + 2, fr, fl, smem + ((r + 2) & 3) * C::STAGE,
+                           wave);
     };
     auto end_phase = [&](int k) {
       const int q = (k + 1) >> 1;
-      if constexpr (KV8) {
-        if ((k & 1) == 1 && q + 1 < nt) {
-          if (q + 2 < nt)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::LOADS8) : "memory");
-          else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
-        if ((k & 1) == 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      } else {
-        if ((k & 1) == 1 && q < nt) {
-          if (q + 1 < nt)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::LOADS) : "memory");
-          else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
+      if ((k & 1) == 1 && q < nt) {
+        if (q + 1 < nt)
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::LOADS) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
       wg_barrier();
     };
-    auto stage = [&](int r) -> const unsigned char* {
-      return smem + (KV8 ? r % 3 : r & 3) * C::STAGE;
-    };
+    auto stage = [&](int r) -> const unsigned char* { return smem + (r & 3) * C::STAGE; };
 
     wg_barrier();
 
@@ -782,9 +646,493 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
     // epilogue: normalise, LSE (natural log), write final output or a partial
     if (wave_rows) {
       const float l_tot = xhalf_sum(st.l_run);
-      // with an fp8 cache O is in units of the head's V scale
-      const float inv = (KV8 ? a.v_scale[h] : 1.0f) / l_tot;
+      const float inv = 1.0f / l_tot;
       const float lse_val = (st.m_run + log2f(l_tot)) * kLn2;
+      const int row = q0 + l32;
+      const bool whole = (t0 == 0) && (t1 == a.T);
+      if (row < a.n) {
+        if (whole) {
+          __bf16* op = static_cast<__bf16*>(a.o) + ((int64_t)row * a.H + h) * D;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              f32x4_t v4 = {st.o[db][4 * g], st.o[db][4 * g + 1], st.o[db][4 * g + 2],
+                            st.o[db][4 * g + 3]};
+              v4 *= inv;
+              *reinterpret_cast<bf16x4_t*>(op + 32 * db + 8 * g + 4 * hi) =
+                  __builtin_convertvector(v4, bf16x4_t);
+            }
+          if (hi == 0 && a.lse) a.lse[(int64_t)h * a.n + row] = lse_val;
+        } else {
+          const int64_t jslot = (int64_t)w - first_wg_of((int64_t)u * a.T, I, a.P);
+          const int64_t prow = ((int64_t)u * a.jmax + jslot) * C::BM + (wave & 7) * 32 + l32;
+          float* pp = a.part_o + prow * D;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              f32x4_t v4 = {st.o[db][4 * g], st.o[db][4 * g + 1], st.o[db][4 * g + 2],
+                            st.o[db][4 * g + 3]};
+              v4 *= inv;
+              *reinterpret_cast<f32x4_t*>(pp + 32 * db + 8 * g + 4 * hi) = v4;
+            }
+          if (hi == 0) a.part_lse[prow] = lse_val;
+        }
+      }
+    }
+    it += t1 - t0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp8 e4m3 cache on the fp8 matrix cores (v_mfma_f32_32x32x64_f8f6f4).
+//
+// Same work decomposition, ping-pong schedule and softmax as the bf16 kernel;
+// what changes is the data in LDS and the products:
+//   - K and V tiles stay e4m3 in LDS (rows of d bytes, 16-byte chunks
+//     XOR-swizzled per row), loaded straight from the cache (or from the
+//     e4m3 copy of the current chunk) by the direct-to-LDS loads;
+//   - Q is scaled once per unit by one factor per query row (448 / amax) and
+//     written as two e4m3 terms, hi = e4m3(x) and lo = e4m3(x - hi) (about
+//     eight significant bits together); the row's scale, the head's K scale
+//     and the softmax scale make one per-lane constant, because a lane owns
+//     one query row of S^T;
+//   - S^T = K Q^T: per 32-key block and 64-dim step one 32x32x64 MFMA per
+//     Q term, both into the same accumulator. In
+//     that instruction byte j of A in lane m + 32h meets byte j of B in lane
+//     n + 32h, so any consistent assignment of dims to (h, j) works: here
+//     dims 64 ks + 32 h + j, i.e. 32 contiguous bytes of a row per lane;
+//   - P is produced scaled by 2^4 (the exponent's +4 costs nothing) under a
+//     running maximum that lags the true one by at most 4, so 0 <= P <= 2^8,
+//     and written as two e4m3 terms like Q (one e4m3 term alone moves O by
+//     several 1e-2 on data with 8-sigma outliers);
+//   - O^T += V^T P^T: the MFMA's key index (h, j) with j = 16 kb + 4 a + b
+//     is key 32 kb + 8 a + 4 h + b, the order in which the score layout
+//     leaves a lane's 32 keys, so P^T is the lane's own scores in order;
+//     V^T comes from transposing 8-bit LDS reads (ds_read_b64_tr_b8: within
+//     16 lanes, lane i takes byte i % 8 of the 8 bytes addressed by lane
+//     2r + (i >= 8), r = 0..7), four per 32-dim block.
+// O is in units of the head's V scale; the output normalisation applies it.
+template <int D>
+struct F8Cfg {
+  static constexpr int BM = 256, BN = 64, NSTAGE = 4;
+  static constexpr int ROWB = D;                // bytes per key row
+  static constexpr int CPR = D / 16;            // 16-byte chunks per row
+  static constexpr int TILE_BYTES = BN * ROWB;  // K (or V) of one tile
+  static constexpr int STAGE = 2 * TILE_BYTES;  // K then V
+  static constexpr int RPL = 1024 / ROWB;       // rows per wave-wide 16-byte load
+  static constexpr int LOADS = 2;               // requests per wave per tile (K, V)
+  static constexpr int KS = D / 64;             // 64-dim steps of a score block
+  static_assert(BN == 8 * RPL, "each of the 8 waves requests RPL rows of K and of V");
+};
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2;
+
+// Physical 16-byte chunk of logical chunk c in row r is c ^ swizzle(r). K:
+// the 32 rows one read instruction gathers spread over 8 chunk positions. V:
+// the 8 rows one transposing read gathers (keys base + {0..3, 8..11}) take
+// 8 different chunk positions.
+__device__ __forceinline__ int f8_kswz(int r) { return r & 7; }
+__device__ __forceinline__ int f8_vswz(int r) { return (r & 3) | (((r >> 3) & 1) << 2); }
+
+// Requests the e4m3 rows of K and V of key tile `tile` into one stage. Lane L
+// of wave w covers tile row RPL w + L / CPR and stage chunk L % CPR, which
+// holds the row's logical chunk (L % CPR) ^ swizzle(row).
+// This head's K and V sources: cache matrices and the rows of the e4m3 copy
+// of the chunk ([H][n][d], row stride d).
+struct F8Src {
+  const char *kc, *vc, *kcur, *vcur;
+  int cache_bytes, cur_bytes;
+};
+
+template <int D>
+__device__ __forceinline__ F8Src f8_src(const AttnArgs& a, int h) {
+  F8Src f;
+  f.kc = uniform_ptr(static_cast<const char*>(a.kc) + (int64_t)h * a.cache_head_elems);
+  f.vc = uniform_ptr(static_cast<const char*>(a.vc) + (int64_t)h * a.cache_head_elems);
+  f.kcur = uniform_ptr(static_cast<const char*>(a.kcur) + (int64_t)h * a.n * D);
+  f.vcur = uniform_ptr(static_cast<const char*>(a.vcur) + (int64_t)h * a.n * D);
+  f.cache_bytes = (int)a.cache_head_elems;
+  f.cur_bytes = a.n * D;
+  return f;
+}
+
+template <int D>
+__device__ __forceinline__ void f8_fetch_tile(const AttnArgs& a, const F8Src& src, int tile,
+                                              FetchRun& fr, unsigned char* stage, int wave,
+                                              int lane) {
+  using C = F8Cfg<D>;
+  const int r = wave * C::RPL + lane / C::CPR;
+  const int c = lane % C::CPR;
+  const int kcol = (c ^ f8_kswz(r)) << 4, vcol = (c ^ f8_vswz(r)) << 4;
+  unsigned char* kdst = stage + wave * 1024;
+  unsigned char* vdst = kdst + C::TILE_BYTES;
+  if (tile < a.cache_tiles) {
+    const int j0 = tile * C::BN;
+    while (j0 >= fr.vend && fr.ri + 1 < a.nruns) fr = fetch_run_at(a, fr.ri + 1);
+    int phys;
+    if (j0 + C::BN <= fr.vend) {
+      phys = fr.phys + j0 - fr.vstart + r;
+    } else {
+      const int j = j0 + r;
+      phys = -1;
+      for (int rr = fr.ri; rr < a.nruns; ++rr) {
+        const Run R = a.runs[rr];
+        if (R.vstart >= j0 + C::BN) break;
+        if (j >= R.vstart && j < R.vstart + R.len) phys = R.phys + j - R.vstart;
+      }
+    }
+    lds_load16(src.kc, src.cache_bytes, phys >= 0 ? phys * D + kcol : kOob, kdst);
+    lds_load16(src.vc, src.cache_bytes, phys >= 0 ? phys * D + vcol : kOob, vdst);
+  } else {
+    // rows past the chunk lie past the resource and read as zeros
+    const int row = (tile - a.cache_tiles) * C::BN + r;
+    lds_load16(src.kcur, src.cur_bytes, row * D + kcol, kdst);
+    lds_load16(src.vcur, src.cur_bytes, row * D + vcol, vdst);
+  }
+}
+
+// Four floats (within the e4m3 range) as two e4m3 words: [0] = hi =
+// e4m3(x), [1] = lo = e4m3(x - hi), bytes in argument order.
+__device__ __forceinline__ i32x2_t split_e4m3x4(float a, float b, float c, float d) {
+  int x = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  x = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, x, true);
+  const f32x2_t ab = __builtin_amdgcn_cvt_pk_f32_fp8(x, false);
+  const f32x2_t cd = __builtin_amdgcn_cvt_pk_f32_fp8(x, true);
+  int y = __builtin_amdgcn_cvt_pk_fp8_f32(a - ab[0], b - ab[1], 0, false);
+  y = __builtin_amdgcn_cvt_pk_fp8_f32(c - cd[0], d - cd[1], y, true);
+  return i32x2_t{x, y};
+}
+
+template <int D>
+struct F8State {
+  f32x16_t o[D / 32];  // O^T accumulator (layout of the bf16 kernel)
+  f32x16_t s[2];       // S^T of the tile, keys 0-31 and 32-63
+  i32x8_t pf[2];       // P^T of the tile (x 2^8) as e4m3 hi and lo terms, between softmax and PV
+  float m_run, l_run;  // running maximum (base 2) and this lane's partial sum (x 2^8)
+};
+
+// One MFMA phase of the fp8 kernel: PV of the tile in stage SV (per 32-dim
+// block, one MFMA per P term) and/or QK of the tile in stage SK (per key block
+// and 64-dim step, one MFMA per Q term). Step i issues PV hi, QK hi, PV lo,
+// QK lo with the operands loaded one step ahead.
+template <int D, bool PV, bool QK>
+__device__ __forceinline__ void f8_gemm(F8State<D>& st, const unsigned char* SV,
+                                        const unsigned char* SK, const int (&koff)[2 * (D / 64)],
+                                        const int (&voff)[D / 32],
+                                        const i32x8_t (&qf)[2][D / 64]) {
+  using C = F8Cfg<D>;
+  constexpr int NPV = PV ? D / 32 : 0;
+  constexpr int NQK = QK ? 2 * C::KS : 0;
+  constexpr int NSTEP = NPV > NQK ? NPV : NQK;
+  i32x8_t vf[NSTEP + 1], kf[NSTEP + 1];
+  auto load_v = [&](int i) {
+    if (i < NPV) {
+      const unsigned char* vp = SV + voff[i];
+      i32x2_t t4[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        t4[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vp + 2048 * t));
+      vf[i] = i32x8_t{t4[0][0], t4[0][1], t4[1][0], t4[1][1],
+                      t4[2][0], t4[2][1], t4[3][0], t4[3][1]};
+    }
+  };
+  auto load_k = [&](int i) {
+    if (i < NQK) {
+      // step i: key block i % 2, dim step i / 2
+      const int kb = i & 1, ks = i >> 1;
+      const unsigned char* kp = SK + kb * 32 * C::ROWB;
+      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(kp + koff[2 * ks]);
+      const i32x4_t h4 = *reinterpret_cast<const i32x4_t*>(kp + koff[2 * ks + 1]);
+      kf[i] = i32x8_t{lo[0], lo[1], lo[2], lo[3], h4[0], h4[1], h4[2], h4[3]};
+    }
+  };
+  f32x16_t acc0 = f32x16_t{}, acc1 = f32x16_t{};
+  load_v(0);
+  load_k(0);
+  __builtin_amdgcn_sched_barrier(0);
+  auto mf = [](const i32x8_t& x, const i32x8_t& y, const f32x16_t& c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, 0, 0, 0, 0);
+  };
+#pragma unroll
+  for (int i = 0; i < NSTEP; ++i) {
+    load_v(i + 1);
+    load_k(i + 1);
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+      if (i < NPV) st.o[i] = mf(vf[i], st.pf[part], st.o[i]);
+      if (i < NQK) {
+        if (i & 1)
+          acc1 = mf(kf[i], qf[part][i >> 1], acc1);
+        else
+          acc0 = mf(kf[i], qf[part][i >> 1], acc0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (QK) {
+    st.s[0] = acc0;
+    st.s[1] = acc1;
+  }
+}
+
+// Online softmax of the fp8 kernel's tile, c per lane (the query row's scale
+// included). The running maximum moves only when a tile exceeds it by more
+// than 4; P is scaled by 2^4, so P <= 2^8 stays within e4m3 and values down
+// to 2^-13 of the row's maximum keep a normal e4m3 representation.
+template <int D>
+__device__ __forceinline__ void f8_softmax(F8State<D>& st, int lim, int hi, float c) {
+  if (lim < 64) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int kr = 8 * (e >> 2) + 4 * hi + (e & 3);
+      if (kr >= lim) st.s[0][e] = -INFINITY;
+      if (32 + kr >= lim) st.s[1][e] = -INFINITY;
+    }
+  }
+  const f32x16_t v0 = st.s[0], v1 = st.s[1];
+  float m[11];
+#pragma unroll
+  for (int e = 0; e < 5; ++e) m[e] = fmaxf(fmaxf(v0[3 * e], v0[3 * e + 1]), v0[3 * e + 2]);
+#pragma unroll
+  for (int e = 0; e < 5; ++e) m[5 + e] = fmaxf(fmaxf(v1[3 * e], v1[3 * e + 1]), v1[3 * e + 2]);
+  m[10] = fmaxf(v0[15], v1[15]);
+  const float n0 = fmaxf(fmaxf(m[0], m[1]), m[2]), n1 = fmaxf(fmaxf(m[3], m[4]), m[5]);
+  const float n2 = fmaxf(fmaxf(m[6], m[7]), m[8]), n3 = fmaxf(m[9], m[10]);
+  // c > 0, so the maximum of the scaled scores is c times the maximum score
+  const float mxs = xhalf_max(fmaxf(fmaxf(n0, n1), fmaxf(n2, n3)) * c);
+  if (__any(!(mxs <= st.m_run + 4.0f))) {
+    const float m_new = fmaxf(st.m_run, mxs);
+    const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) st.o[db] *= alpha;
+    st.l_run *= alpha;
+    st.m_run = m_new;
+  }
+  // P x 2^4 = 2^(s c - m + 4): at most 2^8
+  const float off = st.m_run == -INFINITY ? 4.f : 4.f - st.m_run;
+  f32x16_t p0, p1;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    p0[e] = __builtin_amdgcn_exp2f(fmaf(v0[e], c, off));
+    p1[e] = __builtin_amdgcn_exp2f(fmaf(v1[e], c, off));
+  }
+  float t8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) t8[e] = (p0[e] + p0[e + 8]) + (p1[e] + p1[e + 8]);
+  st.l_run += ((t8[0] + t8[4]) + (t8[1] + t8[5])) + ((t8[2] + t8[6]) + (t8[3] + t8[7]));
+  // byte j = 16 kb + e of P^T holds key block kb's score e
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const i32x2_t s0 = split_e4m3x4(p0[4 * w], p0[4 * w + 1], p0[4 * w + 2], p0[4 * w + 3]);
+    const i32x2_t s1 = split_e4m3x4(p1[4 * w], p1[4 * w + 1], p1[4 * w + 2], p1[4 * w + 3]);
+    st.pf[0][w] = s0[0];
+    st.pf[1][w] = s0[1];
+    st.pf[0][4 + w] = s1[0];
+    st.pf[1][4 + w] = s1[1];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
+  using C = F8Cfg<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::NSTAGE * C::STAGE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
+  const int w = logical_wg(a);
+  const int64_t I = (int64_t)a.units * a.T;
+  int64_t it = range_begin(w, I, a.P);
+  const int64_t it_end = range_begin(w + 1, I, a.P);
+
+  // K operand: key row l32 (+32 per key block), 32 bytes at dims 64 ks + 32 hi
+  int koff[2 * C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      koff[2 * ks + x] = l32 * C::ROWB + (((4 * ks + 2 * hi + x) ^ f8_kswz(l32)) << 4);
+  // V^T operand of dim block db: lane 16 g + 2 r + s supplies the address of
+  // key 8 (r / 4) + 4 hi + r % 4 (+ 16 t for read t), dims 32 db + 16 (g % 2)
+  // + 8 s .. + 7
+  int voff[D / 32];
+  {
+    const int ii = lane & 15, g2 = (lane >> 4) & 1, r = ii >> 1, sx = ii & 1;
+    const int key = 8 * (r >> 2) + 4 * hi + (r & 3);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+      voff[db] = C::TILE_BYTES + key * C::ROWB + (((2 * db + g2) ^ f8_vswz(key)) << 4) + 8 * sx;
+  }
+
+  while (it < it_end) {
+    const int u = (int)(it / a.T);
+    const int t0 = (int)(it - (int64_t)u * a.T);
+    const int t1 = (int)((it_end - it) < (int64_t)(a.T - t0) ? t0 + (it_end - it) : a.T);
+    const int nt = t1 - t0;
+    const int h = __builtin_amdgcn_readfirstlane(u / a.QT);
+    const int qt = u - h * a.QT;
+    const int q0 = qt * C::BM + (wave & 7) * 32;
+    const bool wave_rows = q0 < a.n;
+
+    FetchRun fr = fetch_run_at(a, 0);
+    const F8Src src = f8_src<D>(a, h);
+    f8_fetch_tile<D>(a, src, t0, fr, smem, wave, lane);
+    if (nt > 1) f8_fetch_tile<D>(a, src, t0 + 1, fr, smem + C::STAGE, wave, lane);
+
+    // Q: lane holds row q0 + l32, dims 64 ks + 32 hi .. + 31 (bf16); rows
+    // past the chunk read as zeros. Quantised with the row's scale amax/448.
+    const HeadSrc qsrc = head_src(a.q, a.q, a, h, D, 2, 2);
+    i32x8_t qf[2][C::KS];
+    float c;
+    {
+      const int row = q0 + l32;
+      uint4 raw[4 * C::KS];
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          raw[4 * ks + x] = buf16(qsrc.cur, qsrc.cur_bytes,
+                                  row < a.n ? (row * a.H * D + 64 * ks + 32 * hi + 8 * x) * 2
+                                            : kOob);
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      float amax = 0.f;
+#pragma unroll
+      for (int x = 0; x < 4 * C::KS; ++x) {
+        const bf16x8_t v = __builtin_bit_cast(bf16x8_t, raw[x]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[e]));
+      }
+      amax = xhalf_max(amax);
+      const float qs = amax > 0.f ? amax * (1.0f / 448.0f) : 1.0f;
+      const float qinv = amax > 0.f ? 448.0f / amax : 1.0f;
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const bf16x8_t v = __builtin_bit_cast(bf16x8_t, raw[4 * ks + x]);
+          float f[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] = fminf(fmaxf((float)v[e] * qinv, -448.f), 448.f);
+          const i32x2_t lo4 = split_e4m3x4(f[0], f[1], f[2], f[3]);
+          const i32x2_t hi4 = split_e4m3x4(f[4], f[5], f[6], f[7]);
+          qf[0][ks][2 * x] = lo4[0];
+          qf[1][ks][2 * x] = lo4[1];
+          qf[0][ks][2 * x + 1] = hi4[0];
+          qf[1][ks][2 * x + 1] = hi4[1];
+        }
+      // base-2 scale of the raw products: softmax scale, K scale, Q row scale
+      c = a.scale_log2 * a.k_scale[h] * qs;
+    }
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+
+    F8State<D> st;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) st.o[db] = f32x16_t{};
+    st.s[0] = f32x16_t{};
+    st.s[1] = f32x16_t{};
+    st.pf[0] = i32x8_t{};
+    st.pf[1] = i32x8_t{};
+    st.m_run = -INFINITY;
+    st.l_run = 0.f;
+
+    // Even phases 2r start by requesting tile r+2; odd phases 2q-1 end by
+    // waiting for this wave's requests of tile q (read from phase 2q on).
+    auto begin_phase = [&](int k) {
+      if ((k & 1) == 0 && (k >> 1) + 2 < nt)
+        f8_fetch_tile<D>(a, src, t0 + (k >> 1) + 2, fr, smem + (((k >> 1) + 2) & 3) * C::STAGE,
+                         wave, lane);
+    };
+    auto end_phase = [&](int k) {
+      const int q = (k + 1) >> 1;
+      if ((k & 1) == 1 && q < nt) {
+        if (q + 1 < nt)
+          asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C::LOADS) : "memory");
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      wg_barrier();
+    };
+    auto stage = [&](int r) -> const unsigned char* { return smem + (r & 3) * C::STAGE; };
+
+    wg_barrier();
+
+    if (grp == 0) {
+      begin_phase(0);
+      if (wave_rows) {
+        __builtin_amdgcn_s_setprio(1);
+        f8_gemm<D, false, true>(st, nullptr, stage(0), koff, voff, qf);
+        __builtin_amdgcn_s_setprio(0);
+      }
+      end_phase(0);
+      begin_phase(1);
+      if (wave_rows) f8_softmax<D>(st, tile_valid(a, t0, C::BN), hi, c);
+      end_phase(1);
+      for (int r = 1; r < nt; ++r) {
+        begin_phase(2 * r);
+        if (wave_rows) {
+          __builtin_amdgcn_s_setprio(1);
+          f8_gemm<D, true, true>(st, stage(r - 1), stage(r), koff, voff, qf);
+          __builtin_amdgcn_s_setprio(0);
+        }
+        end_phase(2 * r);
+        begin_phase(2 * r + 1);
+        if (wave_rows) f8_softmax<D>(st, tile_valid(a, t0 + r, C::BN), hi, c);
+        end_phase(2 * r + 1);
+      }
+      begin_phase(2 * nt);
+      if (wave_rows) {
+        __builtin_amdgcn_s_setprio(1);
+        f8_gemm<D, true, false>(st, stage(nt - 1), nullptr, koff, voff, qf);
+        __builtin_amdgcn_s_setprio(0);
+      }
+      end_phase(2 * nt);
+      begin_phase(2 * nt + 1);
+      end_phase(2 * nt + 1);
+    } else {
+      begin_phase(0);
+      end_phase(0);
+      begin_phase(1);
+      if (wave_rows) {
+        __builtin_amdgcn_s_setprio(1);
+        f8_gemm<D, false, true>(st, nullptr, stage(0), koff, voff, qf);
+        __builtin_amdgcn_s_setprio(0);
+      }
+      end_phase(1);
+      for (int r = 1; r < nt; ++r) {
+        begin_phase(2 * r);
+        if (wave_rows) f8_softmax<D>(st, tile_valid(a, t0 + r - 1, C::BN), hi, c);
+        end_phase(2 * r);
+        begin_phase(2 * r + 1);
+        if (wave_rows) {
+          __builtin_amdgcn_s_setprio(1);
+          f8_gemm<D, true, true>(st, stage(r - 1), stage(r), koff, voff, qf);
+          __builtin_amdgcn_s_setprio(0);
+        }
+        end_phase(2 * r + 1);
+      }
+      begin_phase(2 * nt);
+      if (wave_rows) f8_softmax<D>(st, tile_valid(a, t0 + nt - 1, C::BN), hi, c);
+      end_phase(2 * nt);
+      begin_phase(2 * nt + 1);
+      if (wave_rows) {
+        __builtin_amdgcn_s_setprio(1);
+        f8_gemm<D, true, false>(st, stage(nt - 1), nullptr, koff, voff, qf);
+        __builtin_amdgcn_s_setprio(0);
+      }
+      end_phase(2 * nt + 1);
+    }
+
+    // epilogue: P carried 2^4 (in l and in O alike); O is in V-scale units
+    if (wave_rows) {
+      const float l_tot = xhalf_sum(st.l_run);
+      const float inv = a.v_scale[h] / l_tot;
+      const float lse_val = (st.m_run - 4.0f + log2f(l_tot)) * kLn2;
       const int row = q0 + l32;
       const bool whole = (t0 == 0) && (t1 == a.T);
       if (row < a.n) {
@@ -1065,7 +1413,7 @@ template <int D>
 int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
   switch (p.kern) {
     case Kern::BF16:
-      hipLaunchKernelGGL((attn_bf16_kernel<D, false>), dim3(p.wgs), dim3(512), 0, s, a);
+      hipLaunchKernelGGL(attn_bf16_kernel<D>, dim3(p.wgs), dim3(512), 0, s, a);
       break;
     case Kern::FP8:
       if constexpr (D == 128) {
@@ -1086,7 +1434,7 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
         const int64_t total = (int64_t)a.n * a.H * (D / 8);
         hipLaunchKernelGGL(append_fp8_kernel<D>, dim3((unsigned)((total + 255) / 256), 2),
                            dim3(256), 0, s, q);
-        hipLaunchKernelGGL((attn_bf16_kernel<D, true>), dim3(p.wgs), dim3(512), 0, s, a);
+        hipLaunchKernelGGL(attn_fp8_kernel<D>, dim3(p.wgs), dim3(512), 0, s, a);
       } else {
         return -1;
       }

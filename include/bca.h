@@ -155,9 +155,12 @@ size_t bca_attend_workspace_bytes(const bca_cache* cache, const bca_window_spec*
  * through the same codec as the cached chunks); an FP8_E4M3 cache always
  * needs one. Its content between calls is irrelevant; calls in flight at the
  * same time need separate workspaces.
- * FP8_E4M3 cache: the e4m3 keys and values are widened to bf16 exactly and
- * contracted on the bf16 matrix cores; the K scale is folded into the softmax
- * scale and the V scale into the output normalisation.
+ * FP8_E4M3 cache: both products run on the fp8 matrix cores with K and V as
+ * stored; Q (scaled per query row) and the softmax weights P are each written
+ * as two e4m3 terms (value and rounding residual), which keeps the result
+ * within 5e-2 of attention over the stored K/V on data with 8-sigma outliers.
+ * The K scale and the row's Q scale fold into the softmax scale, the V scale
+ * into the output normalisation.
  * Errors: BCA_ERR_OUT_OF_ORDER when a chunk of the window may already have been
  * overwritten (the layer's newest ring id >= t - W + S).
  * The visible set is resolved on the host from the slot table's chunk ids each

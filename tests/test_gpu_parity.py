@@ -242,23 +242,20 @@ def test_append_fp8_codes_match_oracle_quantiser():
 # ---------------------------------------------------------------------------
 # fp8 e4m3 K/V cache with per-head scales: the cache holds decode(quant(x/s))*s
 # and the chunk attends at that precision, its own keys and values included.
-# The oracle attends over the same inputs the kernel does, the cache contents,
-# and the kernel is held to the fp8 bound (5e-2) and, tighter, to the error
-# its bf16 steps can make: P rounded to bf16 (relative 2^-9, at most
-# 2^-9 max|V| on O) and O rounded to bf16 (2^-9 |O| <= 2^-9 max|V|), so
-# 2^-8 max|V| in all (the data carry 8-sigma outliers, max|V| ~ 8), with the
-# bf16 bound as a floor. How far the quantised attention is from attention over
-# the unquantised values is e4m3's own error, not the kernel's: it is logged,
-# not asserted.
+# The oracle attends over the same inputs the kernel does, the cache contents.
+# The kernel contracts on the fp8 matrix cores, so Q (per query row) and P
+# (scaled by 2^8) are rounded to e4m3 as well: each rounding is relative
+# 2^-4 at most, and their effect on O averages over the keys of a row. The
+# bar is the fp8 bound, 5e-2. How far the quantised attention is from
+# attention over the unquantised values is e4m3's own error, not the
+# kernel's: it is logged, not asserted.
 def fp8_scales(H, kmax=8.0, vmax=8.0):
     return ([kmax / 448.0 * (1.0 + 0.1 * h) for h in range(H)],
             [vmax / 448.0 * (1.0 + 0.05 * h) for h in range(H)])
 
 
 def fp8_cache_tol(seq, v):
-    vmax = max([np.abs(v).max()] + [np.abs(b[1]).max() for b in seq.history.values()] +
-               ([np.abs(seq.ref[1]).max()] if seq.ref is not None else []))
-    return min(TOL["fp8"], max(TOL["bf16"], vmax * 2.0 ** -8 * 1.05))
+    return TOL["fp8"]
 
 
 def log_quantisation_error(o, lse, ro, rl, what):
