@@ -282,6 +282,23 @@ def test_fp8_sequence(G):
         seq.append(0, t, k, v)
 
 
+def test_fp8_stream_k_ranges_cross_units():
+    """The fp8 kernel with more units than work groups (64 heads x 5 query
+    tiles): ranges of tile iterations cross unit boundaries."""
+    H, d, n, S, W = 64, 128, 1025, 1, 1
+    cache = new_cache(1, H, d, n, S, dtype="fp8")
+    seq = Sequence(cache, H, d, n, "fp8", seed_layer=31, outlier_frac=0.01,
+                   scales=fp8_scales(H))
+    _, k0, v0 = seq.chunk(0)
+    seq.append(0, 0, k0, v0)
+    q, k, v = seq.chunk(1)
+    plan = cache.plan(0, cache.spec(1, W))
+    assert plan["units"] > plan["workgroups"] and plan["merge"] == 1, plan
+    o, lse, _ = seq.attend(0, 1, q, k, v, W)
+    eo, el = seq.expected(1, q, k, v, W)
+    assert_close(o, lse, eo, el, fp8_cache_tol(seq, v), f"fp8 stream-K {plan['units']} units")
+
+
 def test_fp8_workspace_holds_the_chunk_copy():
     H, d, n, S = 2, 128, 64, 2
     cache = new_cache(1, H, d, n, S, dtype="fp8")
