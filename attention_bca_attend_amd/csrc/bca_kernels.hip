@@ -1,9 +1,13 @@
 // bca_kernels.hip — gfx950 kernels of block-causal ring-KV chunk attention.
 //
-//   attn_bf16_kernel  bf16 flash attention on MFMA (v_mfma_f32_32x32x16_bf16)
-//   attn_f32_kernel   fp32 flash attention on the vector ALUs
-//   merge_kernel      log-sum-exp merge of segment partials
-//   append_kernel     fused K/V write of one chunk into its ring slot
+//   attn_bf16_kernel   bf16 flash attention on MFMA (v_mfma_f32_32x32x16_bf16)
+//   attn_fp8_kernel    e4m3-cache flash attention on the fp8 MFMA
+//                      (v_mfma_f32_32x32x64_f8f6f4)
+//   attn_f32_kernel    fp32 flash attention on the vector ALUs
+//   merge_kernel       log-sum-exp merge of segment partials
+//   append_copy_kernel fused K/V write of one chunk into its ring slot
+//   append_fp8_kernel  the same with e4m3 quantisation (also the e4m3 copy of
+//                      the current chunk that the fp8 kernel reads)
 //
 // What is computed follows "WanToFight" (xllm-io review), section 3 model
 // components table (block-causal attention: bidirectional in the chunk, causal
@@ -17,10 +21,12 @@
 // sees are the same for every row of the chunk (the mask is block-causal), so
 // the host lists the visible keys as "runs" of consecutive rows and every
 // (head, query tile) unit has the same number T of key tiles. The units*T tile
-// iterations are cut into P consecutive, equal ranges, one per work group
-// ("stream-K"); a unit whose tiles span several ranges is computed as several
-// segments, each written as a normalised partial output plus its LSE, and
-// merge_kernel combines them. A unit computed whole writes the final output.
+// iterations are cut into P consecutive, equal ranges, one per work group; a
+// unit whose tiles span several ranges is computed as several segments, each
+// written as a normalised partial output plus its LSE, and merge_kernel
+// combines them. A unit computed whole writes the final output. (With P a
+// multiple of the unit count every unit gets the same number of equal
+// segments; otherwise ranges cross unit boundaries, "stream-K" style.)
 #include <hip/hip_runtime.h>
 
 #include "bca_internal.h"
