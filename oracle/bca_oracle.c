@@ -23,6 +23,11 @@
  *        cache" (recent window plus a reference frame; the window is split into
  *        intervals whose partial outputs are merged by log-sum-exp) and
  *        "technical novelty" (7 intervals, 8-bit K/V per interval).
+ *  [RoPE] The pages name rotary position embedding only as a step fused into
+ *        the path ("Matrix-Game 4.0" summary, experimental results: a RoPE
+ *        fusion kernel; "WorldPlay2" summary, inference optimisations: QKRoPE).
+ *        The reading here is the common one-dimensional rotary embedding with
+ *        interleaved pairs (see bca_oracle_rope).
  *  [OCP] OCP 8-bit Floating Point Specification (OFP8), format E4M3: bias 7,
  *        no infinities, S.1111.111 is NaN, largest finite 448, subnormals
  *        m/8 * 2^-6. (External document: the pages only say "FP8".)
@@ -341,4 +346,33 @@ void bca_oracle_quant_e4m3(const float* x, long count, float scale, uint8_t* out
     float y = x[i] / scale;
     out[i] = bca_oracle_e4m3_encode(y);
   }
+}
+
+/*
+ * Rotary position embedding of one chunk's vectors [RoPE]. x and y are
+ * [n][H][d] (d even); token r of the chunk has position pos0 + r. Each pair of
+ * dimensions (2i, 2i+1), i = 0 .. d/2 - 1, is rotated by the angle
+ *     theta = position * base^(-2i/d)
+ * as (x0, x1) -> (x0 cos theta - x1 sin theta, x0 sin theta + x1 cos theta),
+ * the same for every head. Position 0 leaves x unchanged, lengths are kept,
+ * and the inner product of a query at position m with a key at position k
+ * depends on m - k only. Returns 0, or -1 for an invalid argument.
+ */
+int bca_oracle_rope(int n, int H, int d, const double* x, int64_t pos0, double base, double* y) {
+  if (n < 0 || H < 1 || d < 2 || (d & 1) || !(base > 0.0)) return -1;
+  for (int r = 0; r < n; ++r) {
+    const double pos = (double)(pos0 + r);
+    for (int h = 0; h < H; ++h) {
+      const double* xi = x + ((size_t)r * H + h) * d;
+      double* yi = y + ((size_t)r * H + h) * d;
+      for (int i = 0; i < d / 2; ++i) {
+        const double theta = pos * pow(base, -2.0 * i / d);
+        const double c = cos(theta), s = sin(theta);
+        const double x0 = xi[2 * i], x1 = xi[2 * i + 1];
+        yi[2 * i] = x0 * c - x1 * s;
+        yi[2 * i + 1] = x0 * s + x1 * c;
+      }
+    }
+  }
+  return 0;
 }

@@ -69,6 +69,8 @@ class OracleLib:
         lib.bca_oracle_threads.restype = ctypes.c_int
         lib.bca_oracle_set_threads.argtypes = [ctypes.c_int]
         lib.bca_oracle_set_threads.restype = None
+        lib.bca_oracle_rope.argtypes = [ctypes.c_int] * 3 + [P, ctypes.c_int64, ctypes.c_double, P]
+        lib.bca_oracle_rope.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -152,6 +154,16 @@ class OracleLib:
         flat = [self.lib.bca_oracle_e4m3_encode(float(v)) for v in a.reshape(-1)]
         return np.array(flat, dtype=np.uint8).reshape(a.shape)
 
+    def rope(self, x, pos0: int, base: float) -> np.ndarray:
+        """Rotary position embedding of x [n][H][d]; token r at position pos0 + r."""
+        a = _f64(x)
+        n, H, d = a.shape
+        y = np.empty_like(a)
+        rc = self.lib.bca_oracle_rope(n, H, d, _ptr(a), int(pos0), float(base), _ptr(y))
+        if rc != 0:
+            raise RuntimeError(f"bca_oracle_rope failed ({rc})")
+        return y
+
     def quant_e4m3(self, x, scale: float) -> np.ndarray:
         """codes = encode(fp32(x / scale)) for a float32 array."""
         a = np.ascontiguousarray(x, dtype=np.float32)
@@ -198,6 +210,10 @@ def e4m3_decode(*a, **k):
 
 def e4m3_encode(*a, **k):
     return default().e4m3_encode(*a, **k)
+
+
+def rope(*a, **k):
+    return default().rope(*a, **k)
 
 
 def quant_e4m3(*a, **k):

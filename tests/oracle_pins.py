@@ -17,7 +17,9 @@ What pins what:
 * reductions to an independent library routine
   (torch.nn.functional.scaled_dot_product_attention in float64 on the CPU);
 * large logits (max subtraction);
-* OCP E4M3 codec against torch.float8_e4m3fn and the spec's rounding rules.
+* OCP E4M3 codec against torch.float8_e4m3fn and the spec's rounding rules;
+* rotary embedding: identity at position 0, lengths, composition, dependence
+  on the position difference only, and an independent implementation.
 """
 from __future__ import annotations
 
@@ -322,7 +324,43 @@ def pin_e4m3_codec(lib):
     assert np.array_equal(q, lib.e4m3_encode((x / 60.0).astype(np.float32) / s))
 
 
+def pin_rope(lib):
+    """Rotary embedding: position 0 is the identity, every pair keeps its
+    length, rotations compose (position a then b equals a + b), query-key
+    products depend only on the position difference, and at base 10000 the
+    result equals an independent implementation of the interleaved-pair form
+    (transformers' GPT-J rotary helpers, float32 angles)."""
+    rng = np.random.default_rng(7)
+    H, d = 3, 16
+    x = rng.standard_normal((5, H, d))
+    y0 = lib.rope(x[:1], 0, 500.0)
+    assert np.array_equal(y0, x[:1]), "position 0 must leave x unchanged"
+    y = lib.rope(x, 37, 500.0)
+    nx = x[..., 0::2] ** 2 + x[..., 1::2] ** 2
+    ny = y[..., 0::2] ** 2 + y[..., 1::2] ** 2
+    assert np.allclose(ny, nx, rtol=1e-12, atol=0), "pairs must keep their length"
+    one = x[2:3]
+    a, b = 11, 29
+    assert np.allclose(lib.rope(lib.rope(one, a, 500.0), b, 500.0), lib.rope(one, a + b, 500.0),
+                       rtol=0, atol=1e-12), "rotations must compose"
+    q, k = rng.standard_normal((1, H, d)), rng.standard_normal((1, H, d))
+    for m, kp, shift in ((5, 2, 40), (0, 9, 123), (300, 300, 7)):
+        d0 = np.einsum("nhd,nhd->h", lib.rope(q, m, 500.0), lib.rope(k, kp, 500.0))
+        d1 = np.einsum("nhd,nhd->h", lib.rope(q, m + shift, 500.0), lib.rope(k, kp + shift, 500.0))
+        assert np.allclose(d0, d1, rtol=0, atol=1e-10), "q.k must depend on m - k only"
+    import torch
+    from transformers.models.gptj.modeling_gptj import (apply_rotary_pos_emb,
+                                                        create_sinusoidal_positions)
+    n = 24
+    xs = rng.standard_normal((n, H, d)).astype(np.float32)
+    table = create_sinusoidal_positions(n, d)  # [n][d]: sin | cos, float32
+    sin, cos = table[None, :, : d // 2], table[None, :, d // 2:]
+    ref = apply_rotary_pos_emb(torch.from_numpy(xs)[None], sin, cos)[0].double().numpy()
+    got = lib.rope(xs.astype(np.float64), 0, 10000.0)
+    assert np.abs(got - ref).max() <= 2e-5, "differs from the interleaved-pair rotary form"
+
+
 ALL_PINS = [pin_hand_cases, pin_q_zero_closed_form, pin_one_hot_probe, pin_window_invariance,
             pin_split_merge, pin_merge_closed_forms, pin_constant_and_affine_v,
             pin_reduces_to_library_attention, pin_token_level_sliding_window, pin_large_logits,
-            pin_e4m3_codec]
+            pin_e4m3_codec, pin_rope]

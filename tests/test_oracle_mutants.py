@@ -36,6 +36,12 @@ MUTANTS = [
      "mag = ldexp(1.0 + (double)m / 8.0, e - 8);"),
     ("e4m3_no_saturation", "if (a >= 448.0) return (uint8_t)(sign | 0x7E);",
      "if (a >= 464.0) return (uint8_t)(sign | 0x7F);"),
+    ("rope_second_sign", "yi[2 * i + 1] = x0 * s + x1 * c;", "yi[2 * i + 1] = -x0 * s + x1 * c;"),
+    ("rope_frequency_exponent", "pow(base, -2.0 * i / d)", "pow(base, -1.0 * i / d)"),
+    ("rope_position_off_by_one", "const double pos = (double)(pos0 + r);",
+     "const double pos = (double)(pos0 + r + 1);"),
+    ("rope_pairs_split_halves", "const double x0 = xi[2 * i], x1 = xi[2 * i + 1];",
+     "const double x0 = xi[i], x1 = xi[i + d / 2];"),
 ]
 
 
