@@ -19,6 +19,7 @@ __all__ = [
     "F32", "BF16", "FP8_E4M3", "BcaError", "bca_cache_desc", "bca_window_spec",
     "bca_plan_info", "bca_cache_bytes", "bca_cache_create", "bca_cache_destroy",
     "bca_cache_set_kv_scales", "bca_append_chunk", "bca_attend_workspace_bytes", "bca_attend",
+    "bca_append_chunk_rope", "bca_attend_rope_workspace_bytes", "bca_attend_rope",
     "bca_cache_slot_chunk", "bca_cache_set_slot_chunk", "bca_attend_plan", "bca_status_string",
     "bca_last_error", "Cache", "LIB_PATH", "load_library",
 ]
@@ -96,6 +97,13 @@ def load_library(path: str = LIB_PATH):
     lib.bca_attend_workspace_bytes.restype = SZ
     lib.bca_attend.argtypes = [P, I32, spec_p, P, P, P, I32, P, P, P, SZ, P]
     lib.bca_attend.restype = I32
+    D64 = ctypes.c_double
+    lib.bca_append_chunk_rope.argtypes = [P, I32, I64, I32, P, P, I32, D64, I64, P]
+    lib.bca_append_chunk_rope.restype = I32
+    lib.bca_attend_rope_workspace_bytes.argtypes = [P, spec_p]
+    lib.bca_attend_rope_workspace_bytes.restype = SZ
+    lib.bca_attend_rope.argtypes = [P, I32, spec_p, P, P, P, I32, D64, I64, P, P, P, SZ, P]
+    lib.bca_attend_rope.restype = I32
     lib.bca_cache_slot_chunk.argtypes = [P, I32, I32, ctypes.POINTER(I64)]
     lib.bca_cache_slot_chunk.restype = I32
     lib.bca_cache_set_slot_chunk.argtypes = [P, I32, I32, I64]
@@ -177,6 +185,29 @@ def bca_attend(handle: int, layer: int, spec, q: int, k_cur: int, v_cur: int, qk
                            ctypes.c_void_p(q), ctypes.c_void_p(k_cur), ctypes.c_void_p(v_cur),
                            qkv_dtype, ctypes.c_void_p(o), ctypes.c_void_p(lse),
                            ctypes.c_void_p(workspace), workspace_bytes, ctypes.c_void_p(stream)))
+
+
+def bca_append_chunk_rope(handle: int, layer: int, chunk_id: int, is_ref: int, k: int, v: int,
+                          in_dtype: int, rope_base: float, pos0: int, stream: int = 0) -> None:
+    _check(_lib.bca_append_chunk_rope(ctypes.c_void_p(handle), layer, chunk_id, int(is_ref),
+                                      ctypes.c_void_p(k), ctypes.c_void_p(v), in_dtype,
+                                      float(rope_base), int(pos0), ctypes.c_void_p(stream)))
+
+
+def bca_attend_rope_workspace_bytes(handle: int, spec) -> int:
+    return int(_lib.bca_attend_rope_workspace_bytes(ctypes.c_void_p(handle),
+                                                    ctypes.byref(_spec(spec))))
+
+
+def bca_attend_rope(handle: int, layer: int, spec, q: int, k_cur: int, v_cur: int,
+                    qkv_dtype: int, rope_base: float, pos0: int, o: int, lse: int,
+                    workspace: int, workspace_bytes: int, stream: int = 0) -> None:
+    _check(_lib.bca_attend_rope(ctypes.c_void_p(handle), layer, ctypes.byref(_spec(spec)),
+                                ctypes.c_void_p(q), ctypes.c_void_p(k_cur),
+                                ctypes.c_void_p(v_cur), qkv_dtype, float(rope_base), int(pos0),
+                                ctypes.c_void_p(o), ctypes.c_void_p(lse),
+                                ctypes.c_void_p(workspace), workspace_bytes,
+                                ctypes.c_void_p(stream)))
 
 
 def bca_cache_slot_chunk(handle: int, layer: int, slot: int) -> int:
@@ -278,10 +309,17 @@ class Cache:
             return torch.cuda.current_stream().cuda_stream
         return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
-    def append_chunk(self, layer: int, chunk_id: int, k, v, is_ref: bool = False, stream=None):
+    def append_chunk(self, layer: int, chunk_id: int, k, v, is_ref: bool = False, stream=None,
+                     rope=None):
+        """rope = (base, pos0): K is rotated on its way in (bca_append_chunk_rope)."""
         self._check_qkv(k, v)
-        bca_append_chunk(self.handle, layer, chunk_id, int(bool(is_ref)), k.data_ptr(),
-                         v.data_ptr(), _DT[self.qkv_dtype], self._stream(stream))
+        if rope is None:
+            bca_append_chunk(self.handle, layer, chunk_id, int(bool(is_ref)), k.data_ptr(),
+                             v.data_ptr(), _DT[self.qkv_dtype], self._stream(stream))
+        else:
+            bca_append_chunk_rope(self.handle, layer, chunk_id, int(bool(is_ref)), k.data_ptr(),
+                                  v.data_ptr(), _DT[self.qkv_dtype], rope[0], rope[1],
+                                  self._stream(stream))
 
     def spec(self, q_chunk_id: int, history: int, use_ref: bool = False, num_segments: int = 0,
              scale: float | None = None) -> bca_window_spec:
@@ -289,10 +327,11 @@ class Cache:
             scale = 1.0 / math.sqrt(self.desc.head_dim)
         return bca_window_spec(q_chunk_id, history, int(bool(use_ref)), num_segments, scale)
 
-    def workspace(self, spec):
+    def workspace(self, spec, rope: bool = False):
         import torch
-        key = (spec.history, spec.num_segments)
-        nbytes = bca_attend_workspace_bytes(self.handle, spec)
+        key = (spec.history, spec.num_segments, bool(rope))
+        nbytes = (bca_attend_rope_workspace_bytes if rope else bca_attend_workspace_bytes)(
+            self.handle, spec)
         ws = self._ws.get(key)
         if ws is None or ws.numel() < nbytes:
             ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.mem.device)
@@ -303,8 +342,9 @@ class Cache:
         return bca_attend_plan(self.handle, layer, spec)
 
     def attend(self, layer: int, q, k_cur, v_cur, spec, out=None, lse=None, workspace=None,
-               stream=None):
-        """Returns (o [n][H][d], lse [H][n] fp32)."""
+               stream=None, rope=None):
+        """Returns (o [n][H][d], lse [H][n] fp32). rope = (base, pos0): Q and k_cur are
+        rotated first (bca_attend_rope)."""
         import torch
         self._check_qkv(q, k_cur, v_cur)
         if out is None:
@@ -313,8 +353,14 @@ class Cache:
             lse = torch.empty((self.desc.num_heads, self.desc.chunk_tokens), dtype=torch.float32,
                               device=q.device)
         if workspace is None:
-            workspace = self.workspace(spec)
-        bca_attend(self.handle, layer, spec, q.data_ptr(), k_cur.data_ptr(), v_cur.data_ptr(),
-                   _DT[self.qkv_dtype], out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
-                   workspace.numel(), self._stream(stream))
+            workspace = self.workspace(spec, rope=rope is not None)
+        if rope is None:
+            bca_attend(self.handle, layer, spec, q.data_ptr(), k_cur.data_ptr(), v_cur.data_ptr(),
+                       _DT[self.qkv_dtype], out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+                       workspace.numel(), self._stream(stream))
+        else:
+            bca_attend_rope(self.handle, layer, spec, q.data_ptr(), k_cur.data_ptr(),
+                            v_cur.data_ptr(), _DT[self.qkv_dtype], rope[0], rope[1],
+                            out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+                            workspace.numel(), self._stream(stream))
         return out, lse

@@ -340,9 +340,26 @@ bca_status bca_cache_set_kv_scales(bca_cache* c, int32_t layer, const float* k_s
   return BCA_OK;
 }
 
-bca_status bca_append_chunk(bca_cache* c, int32_t layer, int64_t chunk_id, int32_t is_ref,
-                            const void* k, const void* v, int32_t in_dtype,
-                            bca_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Rotary embedding parameters of one call (bca_append_chunk_rope / bca_attend_rope).
+struct RopeArg {
+  double log2_base;
+  int64_t pos0;
+};
+
+bca_status check_rope(double base, int64_t pos0) {
+  if (!std::isfinite(base) || !(base > 0.0))
+    return fail(BCA_ERR_INVALID_ARG, "rope_base must be finite and > 0");
+  if (pos0 < 0) return fail(BCA_ERR_INVALID_ARG, "rope position must be >= 0");
+  return BCA_OK;
+}
+
+bca_status append_impl(bca_cache* c, int32_t layer, int64_t chunk_id, int32_t is_ref,
+                       const void* k, const void* v, int32_t in_dtype, bca_stream_t stream,
+                       const RopeArg* rope) {
   if (!c) return fail(BCA_ERR_INVALID_ARG, "cache is NULL");
   if (!layer_ok(c, layer))
     return fail(BCA_ERR_INVALID_ARG, "layer %d out of range [0, %d)", layer, c->d.num_layers);
@@ -385,6 +402,11 @@ bca_status bca_append_chunk(bca_cache* c, int32_t layer, int64_t chunk_id, int32
       a.k_scale[h] = c->k_scale[(size_t)layer * d.num_heads + h];
       a.v_scale[h] = c->v_scale[(size_t)layer * d.num_heads + h];
     }
+  if (rope) {
+    a.rope = 1;
+    a.rope_log2_base = rope->log2_base;
+    a.rope_pos0 = rope->pos0;
+  }
   int err = launch_append((bca_dtype)in_dtype, (bca_dtype)kv, d.head_dim, a, (void*)stream);
   if (err != 0) return fail(BCA_ERR_HIP, "append kernel launch failed (hip error %d)", err);
   if (is_ref) {
@@ -396,6 +418,25 @@ bca_status bca_append_chunk(bca_cache* c, int32_t layer, int64_t chunk_id, int32
   }
   g_err.clear();
   return BCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bca_status bca_append_chunk(bca_cache* c, int32_t layer, int64_t chunk_id, int32_t is_ref,
+                            const void* k, const void* v, int32_t in_dtype,
+                            bca_stream_t stream) {
+  return append_impl(c, layer, chunk_id, is_ref, k, v, in_dtype, stream, nullptr);
+}
+
+bca_status bca_append_chunk_rope(bca_cache* c, int32_t layer, int64_t chunk_id, int32_t is_ref,
+                                 const void* k, const void* v, int32_t in_dtype,
+                                 double rope_base, int64_t pos0, bca_stream_t stream) {
+  bca_status st = check_rope(rope_base, pos0);
+  if (st != BCA_OK) return st;
+  const RopeArg r{std::log2(rope_base), pos0};
+  return append_impl(c, layer, chunk_id, is_ref, k, v, in_dtype, stream, &r);
 }
 
 size_t bca_attend_workspace_bytes(const bca_cache* c, const bca_window_spec* s) {
@@ -423,10 +464,21 @@ size_t bca_attend_workspace_bytes(const bca_cache* c, const bca_window_spec* s) 
   return worst;
 }
 
-bca_status bca_attend(const bca_cache* c, int32_t layer, const bca_window_spec* s,
-                      const void* q, const void* k_cur, const void* v_cur, int32_t qkv_dtype,
-                      void* o, float* lse, void* workspace, size_t workspace_bytes,
-                      bca_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace for the rotated copies of Q and K of the current chunk.
+size_t rope_stage_bytes(const bca_cache_desc& d, int32_t qkv_dtype) {
+  return 2 * align256((size_t)d.chunk_tokens * d.num_heads * d.head_dim * elem_size(qkv_dtype));
+}
+
+bca_status attend_impl(const bca_cache* c, int32_t layer, const bca_window_spec* s,
+                       const void* q, const void* k_cur, const void* v_cur, int32_t qkv_dtype,
+                       void* o, float* lse, void* workspace, size_t workspace_bytes,
+                       bca_stream_t stream, const RopeArg* rope) {
   Plan p;
   bca_status st = make_plan(c, layer, s, qkv_dtype, p);
   if (st != BCA_OK) return st;
@@ -435,15 +487,36 @@ bca_status bca_attend(const bca_cache* c, int32_t layer, const bca_window_spec* 
   if (!aligned(q, 16) || !aligned(k_cur, 16) || !aligned(v_cur, 16) || !aligned(o, 16) ||
       (lse && !aligned(lse, 4)))
     return fail(BCA_ERR_INVALID_ARG, "q, k_cur, v_cur and o must be 16-byte aligned");
-  if (p.ws_bytes > 0) {
-    if (!workspace) return fail(BCA_ERR_WORKSPACE, "workspace of %zu bytes required", p.ws_bytes);
+  const bca_cache_desc& d = c->d;
+  // the rotated copies of Q and K follow the plan's own workspace regions
+  const size_t rope_off = align256(p.ws_bytes);
+  const size_t need = rope ? rope_off + rope_stage_bytes(d, qkv_dtype) : p.ws_bytes;
+  if (need > 0) {
+    if (!workspace) return fail(BCA_ERR_WORKSPACE, "workspace of %zu bytes required", need);
     if (!aligned(workspace, 256))
       return fail(BCA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    if (workspace_bytes < p.ws_bytes)
+    if (workspace_bytes < need)
       return fail(BCA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
-                  p.ws_bytes);
+                  need);
   }
-  const bca_cache_desc& d = c->d;
+  if (rope) {
+    RopeStageArgs r;
+    std::memset(&r, 0, sizeof r);
+    char* qr = static_cast<char*>(workspace) + rope_off;
+    char* kr = qr + rope_stage_bytes(d, qkv_dtype) / 2;
+    r.src[0] = q;
+    r.src[1] = k_cur;
+    r.dst[0] = qr;
+    r.dst[1] = kr;
+    r.n = d.chunk_tokens;
+    r.H = d.num_heads;
+    r.log2_base = rope->log2_base;
+    r.pos0 = rope->pos0;
+    int err = launch_rope_stage((bca_dtype)qkv_dtype, d.head_dim, r, (void*)stream);
+    if (err != 0) return fail(BCA_ERR_HIP, "rotary staging launch failed (hip error %d)", err);
+    q = qr;
+    k_cur = kr;
+  }
   AttnArgs a;
   std::memset(&a, 0, sizeof a);
   a.q = q;
@@ -492,6 +565,36 @@ bca_status bca_attend(const bca_cache* c, int32_t layer, const bca_window_spec* 
   if (err != 0) return fail(BCA_ERR_HIP, "attention launch failed (hip error %d)", err);
   g_err.clear();
   return BCA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+bca_status bca_attend(const bca_cache* c, int32_t layer, const bca_window_spec* s,
+                      const void* q, const void* k_cur, const void* v_cur, int32_t qkv_dtype,
+                      void* o, float* lse, void* workspace, size_t workspace_bytes,
+                      bca_stream_t stream) {
+  return attend_impl(c, layer, s, q, k_cur, v_cur, qkv_dtype, o, lse, workspace,
+                     workspace_bytes, stream, nullptr);
+}
+
+size_t bca_attend_rope_workspace_bytes(const bca_cache* c, const bca_window_spec* s) {
+  if (!c || !s) return 0;
+  const int32_t qkv = c->d.kv_dtype == BCA_F32 ? BCA_F32 : BCA_BF16;
+  return align256(bca_attend_workspace_bytes(c, s)) + rope_stage_bytes(c->d, qkv);
+}
+
+bca_status bca_attend_rope(const bca_cache* c, int32_t layer, const bca_window_spec* s,
+                           const void* q, const void* k_cur, const void* v_cur,
+                           int32_t qkv_dtype, double rope_base, int64_t pos0, void* o,
+                           float* lse, void* workspace, size_t workspace_bytes,
+                           bca_stream_t stream) {
+  bca_status st = check_rope(rope_base, pos0);
+  if (st != BCA_OK) return st;
+  const RopeArg r{std::log2(rope_base), pos0};
+  return attend_impl(c, layer, s, q, k_cur, v_cur, qkv_dtype, o, lse, workspace,
+                     workspace_bytes, stream, &r);
 }
 
 bca_status bca_cache_slot_chunk(const bca_cache* c, int32_t layer, int32_t slot,

@@ -107,12 +107,25 @@ struct AppendArgs {
   int32_t n, H;
   float k_scale[kMaxHeadsFp8];  // fp8 cache only
   float v_scale[kMaxHeadsFp8];
+  int32_t rope;            // 1: rotate K (rotary embedding) before it is stored
+  double rope_log2_base;   // log2 of the rotary base
+  int64_t rope_pos0;       // position of the chunk's token 0
+};
+
+// Rotary embedding of a chunk's Q and K into staging copies (same layout).
+struct RopeStageArgs {
+  const void* src[2];  // q, k_cur: [n][H][d]
+  void* dst[2];
+  int32_t n, H;
+  double log2_base;
+  int64_t pos0;
 };
 
 // Launchers (bca_kernels.hip). They return the HIP error code (0 = success).
 int launch_attention(const Plan& plan, const AttnArgs& args, int head_dim, void* stream);
 int launch_append(bca_dtype in, bca_dtype kv, int head_dim, const AppendArgs& args,
                   void* stream);
+int launch_rope_stage(bca_dtype dt, int head_dim, const RopeStageArgs& args, void* stream);
 // Compute units of the current device, or 0 when it cannot be queried.
 int device_compute_units();
 

@@ -8,6 +8,8 @@
 //   append_copy_kernel fused K/V write of one chunk into its ring slot
 //   append_fp8_kernel  the same with e4m3 quantisation (also the e4m3 copy of
 //                      the current chunk that the fp8 kernel reads)
+//   rope_stage_kernel  rotary embedding of the current chunk's Q and K into
+//                      staging copies (the appends rotate cached K themselves)
 //
 // What is computed follows "WanToFight" (xllm-io review), section 3 model
 // components table (block-causal attention: bidirectional in the chunk, causal
@@ -1356,9 +1358,62 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Rotary position embedding of 8 consecutive elements (dims 8g .. 8g+7, four
+// interleaved pairs) of a token at position pos: pair (2i, 2i+1) turns by the
+// angle pos * base^(-2i/d), (x0, x1) -> (x0 cos - x1 sin, x0 sin + x1 cos).
+// "Matrix-Game 4.0" (paper summary), experimental results: a RoPE fusion
+// kernel; "WorldPlay2" (summary), inference optimisations: QKRoPE. The angle
+// and its cosine and sine are taken in double precision (positions reach 10^5
+// and beyond, where an fp32 angle would be off by about 10^-2), the rotation
+// in fp32.
+template <int D>
+__device__ __forceinline__ void rope8(float (&x)[8], int g, int64_t pos, double log2_base) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = 4 * g + j;
+    const double theta = (double)pos * exp2(-(2.0 * i / D) * log2_base);
+    double sd, cd;
+    sincos(theta, &sd, &cd);
+    const float c = (float)cd, s = (float)sd;
+    const float x0 = x[2 * j], x1 = x[2 * j + 1];
+    x[2 * j] = fmaf(x0, c, -(x1 * s));
+    x[2 * j + 1] = fmaf(x0, s, x1 * c);
+  }
+}
+
+// 8 elements of a bf16 (es 2) or fp32 (es 4) row as floats, and back (bf16
+// rounded to nearest even).
+__device__ __forceinline__ void load8(const char* p, int es, float (&x)[8]) {
+  if (es == 2) {
+    const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (float)v[i];
+  } else {
+    const f32x4_t a = reinterpret_cast<const f32x4_t*>(p)[0];
+    const f32x4_t b = reinterpret_cast<const f32x4_t*>(p)[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = a[i];
+      x[4 + i] = b[i];
+    }
+  }
+}
+__device__ __forceinline__ void store8(char* p, int es, const float (&x)[8]) {
+  if (es == 2) {
+    bf16x8_t v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (__bf16)x[i];
+    *reinterpret_cast<bf16x8_t*>(p) = v;
+  } else {
+    reinterpret_cast<f32x4_t*>(p)[0] = f32x4_t{x[0], x[1], x[2], x[3]};
+    reinterpret_cast<f32x4_t*>(p)[1] = f32x4_t{x[4], x[5], x[6], x[7]};
+  }
+}
+
 // Fused K/V append: [n][H][d] -> the block's [H][n][d] rows (stride (S+R)*n*d
 // between heads), converting to the cache dtype. blockIdx.y selects K or V.
-// Each thread moves 8 elements.
+// Each thread moves 8 elements. With a.rope, K is rotated on the way (token r
+// at position rope_pos0 + r).
 template <int D>
 __global__ __launch_bounds__(256) void append_copy_kernel(const AppendArgs a, int es) {
   constexpr int G = D / 8;
@@ -1373,6 +1428,13 @@ __global__ __launch_bounds__(256) void append_copy_kernel(const AppendArgs a, in
   const char* src = static_cast<const char*>(isv ? a.v : a.k) + (rh * D + g * 8) * es;
   char* dst = static_cast<char*>(isv ? a.vdst : a.kdst) +
               ((int64_t)h * a.head_stride_elems + (int64_t)r * D + g * 8) * es;
+  if (!isv && a.rope) {
+    float x[8];
+    load8(src, es, x);
+    rope8<D>(x, g, a.rope_pos0 + r, a.rope_log2_base);
+    store8(dst, es, x);
+    return;
+  }
   if (es == 2) {
     *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
   } else {
@@ -1384,7 +1446,8 @@ __global__ __launch_bounds__(256) void append_copy_kernel(const AppendArgs a, in
 }
 
 // bf16 -> OCP e4m3 with the head's scale: code = round_to_nearest_even(x / s),
-// saturated to +-448 (NaN stays NaN).
+// saturated to +-448 (NaN stays NaN). With a.rope, K is rotated first (in
+// fp32, before the division).
 template <int D>
 __global__ __launch_bounds__(256) void append_fp8_kernel(const AppendArgs a) {
   constexpr int G = D / 8;
@@ -1397,12 +1460,14 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(const AppendArgs a) {
   const int r = (int)(rh / a.H);
   const bool isv = blockIdx.y == 1;
   const float s = isv ? a.v_scale[h] : a.k_scale[h];
-  const bf16x8_t x = *reinterpret_cast<const bf16x8_t*>(
-      static_cast<const __bf16*>(isv ? a.v : a.k) + rh * D + g * 8);
   float y[8];
+  load8(reinterpret_cast<const char*>(static_cast<const __bf16*>(isv ? a.v : a.k) + rh * D +
+                                      g * 8),
+        2, y);
+  if (!isv && a.rope) rope8<D>(y, g, a.rope_pos0 + r, a.rope_log2_base);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    float t = (float)x[i] / s;
+    float t = y[i] / s;
     y[i] = (fabsf(t) > 448.0f) ? copysignf(448.0f, t) : t;
   }
   int lo = 0, hi = 0;
@@ -1415,6 +1480,24 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(const AppendArgs a) {
   *reinterpret_cast<uint2*>(dst) = make_uint2((unsigned)lo, (unsigned)hi);
 }
 
+// Rotary embedding of the current chunk's Q (blockIdx.y 0) and K (1) into
+// staging copies of the same [n][H][d] layout and dtype; token r at position
+// pos0 + r. The attention kernels then read the copies as q and k_cur.
+template <int D>
+__global__ __launch_bounds__(256) void rope_stage_kernel(const RopeStageArgs a, int es) {
+  constexpr int G = D / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)a.n * a.H * G;
+  if (idx >= total) return;
+  const int g = (int)(idx % G);
+  const int r = (int)(idx / G / a.H);
+  const int64_t off = idx * 8 * es;  // element (idx / G) * D + 8 g
+  float x[8];
+  load8(static_cast<const char*>(a.src[blockIdx.y]) + off, es, x);
+  rope8<D>(x, g, a.pos0 + r, a.log2_base);
+  store8(static_cast<char*>(a.dst[blockIdx.y]) + off, es, x);
+}
+
 template <int D>
 int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
   switch (p.kern) {
@@ -1425,7 +1508,7 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
       if constexpr (D == 128) {
         // quantise the current chunk into the staging copy first, exactly as
         // appending it to the cache would
-        AppendArgs q;
+        AppendArgs q{};  // rope off: the chunk arrives already rotated when asked for
         q.k = a.kcur_in;
         q.v = a.vcur_in;
         q.kdst = const_cast<void*>(a.kcur);
@@ -1454,7 +1537,7 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return (int)e;
   if (p.merge) {
-    MergeArgs m;
+    MergeArgs m{};
     m.part_o = a.part_o;
     m.part_lse = a.part_lse;
     m.o = a.o;
@@ -1486,6 +1569,21 @@ int launch_attention(const Plan& p, const AttnArgs& a, int head_dim, void* strea
   if (head_dim == 64) return launch_attention_d<64>(p, a, s);
   if (head_dim == 128) return launch_attention_d<128>(p, a, s);
   return -1;
+}
+
+int launch_rope_stage(bca_dtype dt, int head_dim, const RopeStageArgs& a, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t total = (int64_t)a.n * a.H * (head_dim / 8);
+  const dim3 grid((unsigned)((total + 255) / 256), 2);
+  const int es = dt == BCA_F32 ? 4 : 2;
+  if (head_dim == 64)
+    hipLaunchKernelGGL(rope_stage_kernel<64>, grid, dim3(256), 0, s, a, es);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL(rope_stage_kernel<128>, grid, dim3(256), 0, s, a, es);
+  else
+    return -1;
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? 0 : (int)e;
 }
 
 int launch_append(bca_dtype in, bca_dtype kv, int head_dim, const AppendArgs& a, void* stream) {

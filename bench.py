@@ -17,6 +17,10 @@ Workloads (synthetic inputs, random values of the stated shapes):
      by log-sum-exp, 30 layers x 1 step.
   3  workload 1 streamed over 64 chunks (steps = 64): sustained time per chunk.
   4  workload 2 with an fp8-e4m3 K/V cache (per-head scales).
+  5  workload 1 with rotary position embedding fused into the path: appends
+     rotate K on the way into the ring (bca_append_chunk_rope) and attends
+     rotate Q and the chunk's own K first (bca_attend_rope); base 10000,
+     token r of chunk t at position t*n + r.
 
 Prints one JSON line. `value` is algorithmic attention TFLOP/s over the whole
 step (4*H*n*N_k*d per chunk-layer, appends included in the time), from a timed
@@ -51,6 +55,8 @@ CONFIGS = {
             steps_per_chunk=4, kv="bf16"),
     4: dict(workload="matrixgame4_fp8cache_chunk", H=24, d=128, n=405, S=20, W=20, R=1, G=4,
             L=30, steps_per_chunk=1, kv="fp8"),
+    5: dict(workload="wantofight_bf16_rope_chunk", H=12, d=128, n=1536, S=2, W=2, R=0, G=0,
+            L=30, steps_per_chunk=4, kv="bf16", rope=10000.0),
 }
 
 
@@ -195,6 +201,8 @@ def main():
     H, d, n, S, W, R, G, L = (cfg[k] for k in ("H", "d", "n", "S", "W", "R", "G", "L"))
     spc = cfg["steps_per_chunk"]
     fp8 = cfg["kv"] == "fp8"
+    rope_base = cfg.get("rope")
+    rope = (lambda t: (rope_base, t * n)) if rope_base else (lambda t: None)
     torch.cuda.set_device(0)
     g = torch.Generator(device="cuda")
     g.manual_seed(20261202)
@@ -213,13 +221,15 @@ def main():
     # fill the ring (chunks 0..S-1) and the reference
     for l in range(L):
         if R:
-            cache.append_chunk(l, 0, gen((n, H, d), g, fp8), gen((n, H, d), g, fp8), is_ref=True)
+            cache.append_chunk(l, 0, gen((n, H, d), g, fp8), gen((n, H, d), g, fp8), is_ref=True,
+                               rope=rope(0))
         for c in range(S):
-            cache.append_chunk(l, c, gen((n, H, d), g, fp8), gen((n, H, d), g, fp8))
+            cache.append_chunk(l, c, gen((n, H, d), g, fp8), gen((n, H, d), g, fp8),
+                               rope=rope(c))
     torch.cuda.synchronize()
     t_chunk = S
     spec0 = cache.spec(t_chunk, W, use_ref=bool(R), num_segments=G)
-    ws = cache.workspace(spec0)
+    ws = cache.workspace(spec0, rope=rope_base is not None)
     plan = cache.plan(0, spec0)
     nk = plan["visible_keys"]
     flop_cl = 4.0 * H * n * nk * d
@@ -230,9 +240,10 @@ def main():
         spec = cache.spec(t, W, use_ref=bool(R), num_segments=G)
         for _ in range(spc):
             for l in range(L):
-                cache.attend(l, Q[l], Kc[l], Vc[l], spec, out=O, lse=LSE, workspace=ws)
+                cache.attend(l, Q[l], Kc[l], Vc[l], spec, out=O, lse=LSE, workspace=ws,
+                             rope=rope(t))
         for l in range(L):
-            cache.append_chunk(l, t, Kc[l], Vc[l])
+            cache.append_chunk(l, t, Kc[l], Vc[l], rope=rope(t))
 
     for _ in range(args.warmup):
         run_chunk(t_chunk)
@@ -267,7 +278,8 @@ def main():
     a0.record()
     for _ in range(a_steps * spc):
         for l in range(L):
-            cache.attend(l, Q[l], Kc[l], Vc[l], spec, out=O, lse=LSE, workspace=ws)
+            cache.attend(l, Q[l], Kc[l], Vc[l], spec, out=O, lse=LSE, workspace=ws,
+                         rope=rope(t_chunk))
     a1.record()
     torch.cuda.synchronize()
     attend_us = a0.elapsed_time(a1) / (a_steps * spc * L) * 1e3
@@ -287,7 +299,8 @@ def main():
         "config": {"workload": cfg["workload"], "heads": H, "head_dim": d, "chunk_tokens": n,
                    "visible_keys": nk, "ring_slots": S, "history": W, "reference": bool(R),
                    "segments": G if G else "auto", "layers": L,
-                   "denoise_steps_per_chunk": spc, "batch": 1},
+                   "denoise_steps_per_chunk": spc, "batch": 1,
+                   "rope_base": rope_base},
         "us_per_chunk_layer": round(ms_step * 1e3 / n_attend, 3),
         "attend_us": round(attend_us, 3),
         "pct_mfma_peak": round(100.0 * achieved / peak, 2),
@@ -295,7 +308,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(cfg["workload"]),
-                     "kernel": "bca_attend: "
+                     "kernel": ("bca_attend_rope: rope_stage_kernel + " if rope_base
+                                else "bca_attend: ")
                                + ("attn_fp8_kernel + append_fp8_kernel (chunk copy)" if fp8
                                   else "attn_bf16_kernel")
                                + (" + merge_kernel" if plan["merge"] else "")},

@@ -171,6 +171,43 @@ bca_status bca_attend(const bca_cache* cache, int32_t layer, const bca_window_sp
                       void* o, float* lse, void* workspace, size_t workspace_bytes,
                       bca_stream_t stream);
 
+/* Rotary position embedding (RoPE) fused into the path. The pages name the step
+ * only ("Matrix-Game 4.0" summary, experimental results: a RoPE fusion kernel;
+ * "WorldPlay2" summary, inference optimisations: QKRoPE); the form used is the
+ * common one-dimensional rotary embedding with interleaved pairs: the token at
+ * position p turns each pair of dimensions (2i, 2i+1), i = 0 .. d/2-1, by the
+ * angle p * rope_base^(-2i/d):
+ *     (x0, x1) -> (x0 cos - x1 sin, x0 sin + x1 cos),
+ * the same for every head. Angles, cosines and sines are computed in double
+ * precision, the rotation in fp32, and the result rounded to the destination
+ * dtype (FP8_E4M3 caches: rotated, then quantised). rope_base must be finite
+ * and > 0 (10000 is usual); positions must be >= 0. Token r of a chunk sits at
+ * position pos0 + r; with pos0 = chunk id * n for every chunk, queries and keys
+ * share one position axis and q.k depends only on the distance between tokens.
+ *
+ * bca_append_chunk_rope: bca_append_chunk with K rotated on its way into the
+ * cache (V is stored as given). Same arguments, ordering and errors, plus
+ * rope_base and pos0.
+ *
+ * bca_attend_rope: bca_attend where Q and k_cur are first rotated (token r at
+ * position pos0 + r) into staging copies inside the workspace, which the
+ * attention then reads; the cached chunks are expected to have been appended
+ * with bca_append_chunk_rope. The workspace must hold
+ * bca_attend_rope_workspace_bytes() (the bca_attend figure rounded up to 256,
+ * plus two [n][H][d] copies in qkv_dtype, each rounded up to 256). Errors as
+ * for bca_attend, plus BCA_ERR_INVALID_ARG for rope_base or pos0. */
+bca_status bca_append_chunk_rope(bca_cache* cache, int32_t layer, int64_t chunk_id,
+                                 int32_t is_ref, const void* k, const void* v, int32_t in_dtype,
+                                 double rope_base, int64_t pos0, bca_stream_t stream);
+
+size_t bca_attend_rope_workspace_bytes(const bca_cache* cache, const bca_window_spec* spec);
+
+bca_status bca_attend_rope(const bca_cache* cache, int32_t layer, const bca_window_spec* spec,
+                           const void* q, const void* k_cur, const void* v_cur,
+                           int32_t qkv_dtype, double rope_base, int64_t pos0, void* o,
+                           float* lse, void* workspace, size_t workspace_bytes,
+                           bca_stream_t stream);
+
 /* Host-side slot table query: chunk id held by ring slot `slot` (0 <= slot < S)
  * of `layer`, -1 if empty. slot == S (with has_ref) reports the reference block
  * (its recorded id, or -1). */

@@ -313,3 +313,30 @@ def test_fp8_cache_plan_needs_the_chunk_copy():
         bca.bca_attend(h, 0, spec, FAKE, FAKE, FAKE, bca.BF16, FAKE, 0, 0, 0, 0)
     assert e.value.status == -3
     bca.bca_cache_destroy(h)
+
+
+def test_rope_entry_points_validate_before_launch():
+    h, _ = make(S=2, R=0, dt=bca.BF16, d=128, H=2, n=16)
+    P = FAKE
+    for base, pos0 in ((float("nan"), 0), (float("inf"), 0), (0.0, 0), (-5.0, 0), (1e4, -1)):
+        with pytest.raises(BcaError) as e:
+            bca.bca_append_chunk_rope(h, 0, 3, 0, P, P, bca.BF16, base, pos0, 0)
+        assert e.value.status == -1, (base, pos0)
+    # the append checks of bca_append_chunk still apply
+    with pytest.raises(BcaError) as e:
+        bca.bca_append_chunk_rope(h, 0, 3, 0, P, P, bca.F32, 1e4, 0, 0)
+    assert e.value.status == -4
+    assert bca.bca_cache_slot_chunk(h, 0, 1) == -1  # nothing recorded
+    spec = bca.bca_window_spec(2, 2, 0, 1, 0.1)
+    need = bca.bca_attend_rope_workspace_bytes(h, spec)
+    # two [n][H][d] bf16 copies on top of what bca_attend needs (none here)
+    assert need == bca.bca_attend_workspace_bytes(h, spec) + 2 * 16 * 2 * 128 * 2
+    for base, pos0 in ((float("nan"), 0), (0.0, 0), (1e4, -1)):
+        with pytest.raises(BcaError) as e:
+            bca.bca_attend_rope(h, 0, spec, P, P, P, bca.BF16, base, pos0, P, 0, P, need, 0)
+        assert e.value.status == -1, (base, pos0)
+    for ws, wsb in ((0, 0), (P, need - 1), (P + 16, need)):
+        with pytest.raises(BcaError) as e:
+            bca.bca_attend_rope(h, 0, spec, P, P, P, bca.BF16, 1e4, 0, P, 0, ws, wsb, 0)
+        assert e.value.status == -3, (ws, wsb)
+    bca.bca_cache_destroy(h)
