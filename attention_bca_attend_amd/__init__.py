@@ -6,7 +6,7 @@ one to one and take raw device pointers (ints) and stream handles.
 ``Cache`` is a small convenience wrapper that uses torch for device memory
 and the current stream.
 
-The library must have been built (``python -m attention_bca_attend_amd.build``
+The library must have been built (``python attention_bca_attend_amd/build.py``
 or ``__graft_entry__.build()``); importing this package without it raises.
 """
 from __future__ import annotations
@@ -72,7 +72,7 @@ def load_library(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with "
-                          f"'python -m attention_bca_attend_amd.build'")
+                          f"'python attention_bca_attend_amd/build.py'")
     # torch ships its own build of the HIP runtime under the same soname
     # (libamdhip64.so.7) as the system one libbca.so is linked against. Loading
     # torch first makes libbca bind to the runtime already in the process;

@@ -1,6 +1,6 @@
 """Builds libbca.so (the C-ABI library of include/bca.h) for gfx950 with hipcc.
 
-    python -m attention_bca_attend_amd.build
+    python attention_bca_attend_amd/build.py
 
 Objects go to _build/ at the repository root; the library is written next to
 this file so that it travels with the source tree.
