@@ -9,7 +9,8 @@
 //   append_fp8_kernel  the same with e4m3 quantisation (also the e4m3 copy of
 //                      the current chunk that the fp8 kernel reads)
 //   rope_stage_kernel  rotary embedding of the current chunk's Q and K into
-//                      staging copies (the appends rotate cached K themselves)
+//                      staging copies
+//   append_rope_k_kernel  the rotated K of an append (copy or e4m3)
 //
 // What is computed follows "WanToFight" (xllm-io review), section 3 model
 // components table (block-causal attention: bidirectional in the chunk, causal
@@ -1363,18 +1364,65 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
 // angle pos * base^(-2i/d), (x0, x1) -> (x0 cos - x1 sin, x0 sin + x1 cos).
 // "Matrix-Game 4.0" (paper summary), experimental results: a RoPE fusion
 // kernel; "WorldPlay2" (summary), inference optimisations: QKRoPE. The angle
-// and its cosine and sine are taken in double precision (positions reach 10^5
-// and beyond, where an fp32 angle would be off by about 10^-2), the rotation
-// in fp32.
+// is formed and reduced in double precision (positions reach 10^5 and beyond,
+// where an fp32 angle would be off by about 10^-2); the rotation is in fp32.
+
+// Heads one thread of the rotary kernels turns with one set of angles.
+constexpr int kRopeHeads = 4;
+
 template <int D>
-__device__ __forceinline__ void rope8(float (&x)[8], int g, int64_t pos, double log2_base) {
+struct RopeAngles {
+  float c[4], s[4];
+};
+
+// Inverse frequencies rope_base^(-2i/d), i = 0 .. d/2-1, in double, one per
+// thread of the first d/2, into an LDS table shared by the work group.
+template <int D>
+__device__ __forceinline__ void rope_inv_freq(double* tab, double log2_base) {
+  if (threadIdx.x < D / 2) tab[threadIdx.x] = exp2(-(2.0 * threadIdx.x / D) * log2_base);
+  __syncthreads();
+}
+
+// Cosines and sines of the 4 pairs of dimension group g (dims 8g .. 8g+7) at
+// position pos. They depend on neither the head nor Q/K, so the kernels take
+// them once per (token, group) and turn several heads with them.
+//
+// Angles reach pos (10^5 and beyond) and are formed and reduced in double:
+// theta = k pi/2 + x with |x| <= pi/4, x taken with three fused multiply-adds
+// against pi/2 written as a sum of three doubles (Cody and Waite's additive
+// reduction; with k below 2^20 the reduction error stays near 1e-16). The
+// cosine and sine of x are then taken in fp32 (a few ulp of fp32, below the
+// fp32 rotation's own rounding), and the quadrant k mod 4 swaps and negates
+// them.
+template <int D>
+__device__ __forceinline__ RopeAngles<D> rope_angles(int g, int64_t pos, const double* inv_freq) {
+  constexpr double kPio2Hi = 1.5707963267948966e+00;   // pi/2 rounded to double
+  constexpr double kPio2Mid = 6.123233995736766e-17;   // pi/2 - kPio2Hi, rounded
+  constexpr double kPio2Lo = -1.4973849048591698e-33;  // the remainder, rounded
+  constexpr double k2OverPi = 6.3661977236758138e-01;
+  RopeAngles<D> r;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int i = 4 * g + j;
-    const double theta = (double)pos * exp2(-(2.0 * i / D) * log2_base);
-    double sd, cd;
-    sincos(theta, &sd, &cd);
-    const float c = (float)cd, s = (float)sd;
+    const double theta = (double)pos * inv_freq[4 * g + j];
+    const double k = rint(theta * k2OverPi);
+    double x = fma(-k, kPio2Hi, theta);
+    x = fma(-k, kPio2Mid, x);
+    x = fma(-k, kPio2Lo, x);
+    float sx, cx;
+    sincosf((float)x, &sx, &cx);
+    const int q = (int)((int64_t)k & 3);
+    const float sq = (q & 1) ? cx : sx, cq = (q & 1) ? sx : cx;
+    r.s[j] = (q & 2) ? -sq : sq;
+    r.c[j] = ((q + 1) & 2) ? -cq : cq;
+  }
+  return r;
+}
+
+template <int D>
+__device__ __forceinline__ void rope8(float (&x)[8], const RopeAngles<D>& r) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float c = r.c[j], s = r.s[j];
     const float x0 = x[2 * j], x1 = x[2 * j + 1];
     x[2 * j] = fmaf(x0, c, -(x1 * s));
     x[2 * j + 1] = fmaf(x0, s, x1 * c);
@@ -1411,11 +1459,11 @@ __device__ __forceinline__ void store8(char* p, int es, const float (&x)[8]) {
 }
 
 // Fused K/V append: [n][H][d] -> the block's [H][n][d] rows (stride (S+R)*n*d
-// between heads), converting to the cache dtype. blockIdx.y selects K or V.
-// Each thread moves 8 elements. With a.rope, K is rotated on the way (token r
-// at position rope_pos0 + r).
+// between heads), converting to the cache dtype. blockIdx.y + kv0 selects K (0)
+// or V (1). Each thread moves 8 elements. A rotated K goes through
+// append_rope_k_kernel instead.
 template <int D>
-__global__ __launch_bounds__(256) void append_copy_kernel(const AppendArgs a, int es) {
+__global__ __launch_bounds__(256) void append_copy_kernel(const AppendArgs a, int es, int kv0) {
   constexpr int G = D / 8;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = (int64_t)a.n * a.H * G;
@@ -1424,17 +1472,10 @@ __global__ __launch_bounds__(256) void append_copy_kernel(const AppendArgs a, in
   const int64_t rh = idx / G;
   const int h = (int)(rh % a.H);
   const int r = (int)(rh / a.H);
-  const bool isv = blockIdx.y == 1;
+  const bool isv = blockIdx.y + kv0 == 1;
   const char* src = static_cast<const char*>(isv ? a.v : a.k) + (rh * D + g * 8) * es;
   char* dst = static_cast<char*>(isv ? a.vdst : a.kdst) +
               ((int64_t)h * a.head_stride_elems + (int64_t)r * D + g * 8) * es;
-  if (!isv && a.rope) {
-    float x[8];
-    load8(src, es, x);
-    rope8<D>(x, g, a.rope_pos0 + r, a.rope_log2_base);
-    store8(dst, es, x);
-    return;
-  }
   if (es == 2) {
     *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
   } else {
@@ -1446,10 +1487,25 @@ __global__ __launch_bounds__(256) void append_copy_kernel(const AppendArgs a, in
 }
 
 // bf16 -> OCP e4m3 with the head's scale: code = round_to_nearest_even(x / s),
-// saturated to +-448 (NaN stays NaN). With a.rope, K is rotated first (in
-// fp32, before the division).
+// saturated to +-448 (NaN stays NaN).
+__device__ __forceinline__ uint2 e4m3x8(const float (&x)[8], float s) {
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float t = x[i] / s;
+    y[i] = (fabsf(t) > 448.0f) ? copysignf(448.0f, t) : t;
+  }
+  int lo = 0, hi = 0;
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], lo, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], hi, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
+  return make_uint2((unsigned)lo, (unsigned)hi);
+}
+
+// The e4m3 append; blockIdx.y + kv0 selects K (0) or V (1).
 template <int D>
-__global__ __launch_bounds__(256) void append_fp8_kernel(const AppendArgs a) {
+__global__ __launch_bounds__(256) void append_fp8_kernel(const AppendArgs a, int kv0) {
   constexpr int G = D / 8;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = (int64_t)a.n * a.H * G;
@@ -1458,44 +1514,73 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(const AppendArgs a) {
   const int64_t rh = idx / G;
   const int h = (int)(rh % a.H);
   const int r = (int)(rh / a.H);
-  const bool isv = blockIdx.y == 1;
+  const bool isv = blockIdx.y + kv0 == 1;
   const float s = isv ? a.v_scale[h] : a.k_scale[h];
   float y[8];
   load8(reinterpret_cast<const char*>(static_cast<const __bf16*>(isv ? a.v : a.k) + rh * D +
                                       g * 8),
         2, y);
-  if (!isv && a.rope) rope8<D>(y, g, a.rope_pos0 + r, a.rope_log2_base);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float t = y[i] / s;
-    y[i] = (fabsf(t) > 448.0f) ? copysignf(448.0f, t) : t;
-  }
-  int lo = 0, hi = 0;
-  lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], lo, false);
-  lo = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], lo, true);
-  hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], hi, false);
-  hi = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], hi, true);
   unsigned char* dst = static_cast<unsigned char*>(isv ? a.vdst : a.kdst) +
                        ((int64_t)h * a.head_stride_elems + (int64_t)r * D + g * 8);
-  *reinterpret_cast<uint2*>(dst) = make_uint2((unsigned)lo, (unsigned)hi);
+  *reinterpret_cast<uint2*>(dst) = e4m3x8(y, s);
 }
 
 // Rotary embedding of the current chunk's Q (blockIdx.y 0) and K (1) into
 // staging copies of the same [n][H][d] layout and dtype; token r at position
-// pos0 + r. The attention kernels then read the copies as q and k_cur.
+// pos0 + r. A thread owns one (token, 8-dim group), takes its cosines and sines
+// once and turns that group in every head. The attention kernels then read the
+// copies as q and k_cur.
 template <int D>
-__global__ __launch_bounds__(256) void rope_stage_kernel(const RopeStageArgs a, int es) {
+__global__ __launch_bounds__(128) void rope_stage_kernel(const RopeStageArgs a, int es) {
   constexpr int G = D / 8;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)a.n * a.H * G;
-  if (idx >= total) return;
+  __shared__ double inv_freq[D / 2];
+  rope_inv_freq<D>(inv_freq, a.log2_base);
+  const int64_t idx = (int64_t)blockIdx.x * 128 + threadIdx.x;
+  if (idx >= (int64_t)a.n * G) return;
   const int g = (int)(idx % G);
-  const int r = (int)(idx / G / a.H);
-  const int64_t off = idx * 8 * es;  // element (idx / G) * D + 8 g
-  float x[8];
-  load8(static_cast<const char*>(a.src[blockIdx.y]) + off, es, x);
-  rope8<D>(x, g, a.pos0 + r, a.log2_base);
-  store8(static_cast<char*>(a.dst[blockIdx.y]) + off, es, x);
+  const int r = (int)(idx / G);
+  const RopeAngles<D> ang = rope_angles<D>(g, a.pos0 + r, inv_freq);
+  const char* src = static_cast<const char*>(a.src[blockIdx.y]);
+  char* dst = static_cast<char*>(a.dst[blockIdx.y]);
+  const int h0 = blockIdx.z * kRopeHeads, h1 = min(a.H, h0 + kRopeHeads);
+#pragma unroll
+  for (int h = h0; h < h1; ++h) {
+    const int64_t off = (((int64_t)r * a.H + h) * D + 8 * g) * es;
+    float x[8];
+    load8(src + off, es, x);
+    rope8<D>(x, ang);
+    store8(dst + off, es, x);
+  }
+}
+
+// The rotated K of an append: like rope_stage_kernel (one thread per token,
+// 8-dim group and kRopeHeads heads), writing the block's [H][n][d] rows in the cache
+// dtype: bf16 or fp32 (es 2 or 4) when FP8 is false, e4m3 with the head's
+// scale (rotated first, in fp32, then quantised) when it is true.
+template <int D, bool FP8>
+__global__ __launch_bounds__(128) void append_rope_k_kernel(const AppendArgs a, int es) {
+  constexpr int G = D / 8;
+  __shared__ double inv_freq[D / 2];
+  rope_inv_freq<D>(inv_freq, a.rope_log2_base);
+  const int64_t idx = (int64_t)blockIdx.x * 128 + threadIdx.x;
+  if (idx >= (int64_t)a.n * G) return;
+  const int g = (int)(idx % G);
+  const int r = (int)(idx / G);
+  const RopeAngles<D> ang = rope_angles<D>(g, a.rope_pos0 + r, inv_freq);
+  const int ies = FP8 ? 2 : es;
+  const char* src = static_cast<const char*>(a.k);
+  const int h0 = blockIdx.z * kRopeHeads, h1 = min(a.H, h0 + kRopeHeads);
+#pragma unroll
+  for (int h = h0; h < h1; ++h) {
+    float x[8];
+    load8(src + (((int64_t)r * a.H + h) * D + 8 * g) * ies, ies, x);
+    rope8<D>(x, ang);
+    const int64_t e = (int64_t)h * a.head_stride_elems + (int64_t)r * D + 8 * g;
+    if constexpr (FP8)
+      *reinterpret_cast<uint2*>(static_cast<unsigned char*>(a.kdst) + e) = e4m3x8(x, a.k_scale[h]);
+    else
+      store8(static_cast<char*>(a.kdst) + e * es, es, x);
+  }
 }
 
 template <int D>
@@ -1522,7 +1607,7 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
         }
         const int64_t total = (int64_t)a.n * a.H * (D / 8);
         hipLaunchKernelGGL(append_fp8_kernel<D>, dim3((unsigned)((total + 255) / 256), 2),
-                           dim3(256), 0, s, q);
+                           dim3(256), 0, s, q, 0);
         hipLaunchKernelGGL(attn_fp8_kernel<D>, dim3(p.wgs), dim3(512), 0, s, a);
       } else {
         return -1;
@@ -1573,32 +1658,44 @@ int launch_attention(const Plan& p, const AttnArgs& a, int head_dim, void* strea
 
 int launch_rope_stage(bca_dtype dt, int head_dim, const RopeStageArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t total = (int64_t)a.n * a.H * (head_dim / 8);
-  const dim3 grid((unsigned)((total + 255) / 256), 2);
+  const int64_t total = (int64_t)a.n * (head_dim / 8);
+  const dim3 grid((unsigned)((total + 127) / 128), 2, (unsigned)((a.H + kRopeHeads - 1) / kRopeHeads));
   const int es = dt == BCA_F32 ? 4 : 2;
   if (head_dim == 64)
-    hipLaunchKernelGGL(rope_stage_kernel<64>, grid, dim3(256), 0, s, a, es);
+    hipLaunchKernelGGL(rope_stage_kernel<64>, grid, dim3(128), 0, s, a, es);
   else if (head_dim == 128)
-    hipLaunchKernelGGL(rope_stage_kernel<128>, grid, dim3(256), 0, s, a, es);
+    hipLaunchKernelGGL(rope_stage_kernel<128>, grid, dim3(128), 0, s, a, es);
   else
     return -1;
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? 0 : (int)e;
 }
 
+// Without rotation one launch moves K (blockIdx.y 0) and V (1). With it, V
+// keeps that kernel (kv0 = 1, one grid row) and K goes through
+// append_rope_k_kernel.
 int launch_append(bca_dtype in, bca_dtype kv, int head_dim, const AppendArgs& a, void* stream) {
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t total = (int64_t)a.n * a.H * (head_dim / 8);
-  const dim3 grid((unsigned)((total + 255) / 256), 2);
+  const int kv0 = a.rope ? 1 : 0;
+  const dim3 grid((unsigned)((total + 255) / 256), 2 - kv0);
+  const dim3 rgrid((unsigned)(((int64_t)a.n * (head_dim / 8) + 127) / 128), 1,
+                   (unsigned)((a.H + kRopeHeads - 1) / kRopeHeads));
   if (kv == BCA_FP8_E4M3) {
     if (head_dim != 128 || in != BCA_BF16) return -1;
-    hipLaunchKernelGGL(append_fp8_kernel<128>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(append_fp8_kernel<128>, grid, dim3(256), 0, s, a, kv0);
+    if (a.rope) hipLaunchKernelGGL((append_rope_k_kernel<128, true>), rgrid, dim3(128), 0, s, a, 1);
   } else {
     const int es = kv == BCA_F32 ? 4 : 2;
-    if (head_dim == 64)
-      hipLaunchKernelGGL(append_copy_kernel<64>, grid, dim3(256), 0, s, a, es);
-    else
-      hipLaunchKernelGGL(append_copy_kernel<128>, grid, dim3(256), 0, s, a, es);
+    if (head_dim == 64) {
+      hipLaunchKernelGGL(append_copy_kernel<64>, grid, dim3(256), 0, s, a, es, kv0);
+      if (a.rope)
+        hipLaunchKernelGGL((append_rope_k_kernel<64, false>), rgrid, dim3(128), 0, s, a, es);
+    } else {
+      hipLaunchKernelGGL(append_copy_kernel<128>, grid, dim3(256), 0, s, a, es, kv0);
+      if (a.rope)
+        hipLaunchKernelGGL((append_rope_k_kernel<128, false>), rgrid, dim3(128), 0, s, a, es);
+    }
   }
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? 0 : (int)e;

@@ -178,8 +178,9 @@ bca_status bca_attend(const bca_cache* cache, int32_t layer, const bca_window_sp
  * position p turns each pair of dimensions (2i, 2i+1), i = 0 .. d/2-1, by the
  * angle p * rope_base^(-2i/d):
  *     (x0, x1) -> (x0 cos - x1 sin, x0 sin + x1 cos),
- * the same for every head. Angles, cosines and sines are computed in double
- * precision, the rotation in fp32, and the result rounded to the destination
+ * the same for every head. Angles are formed and reduced modulo pi/2 in double
+ * precision, their cosines and sines taken in fp32 from the reduced angle, the
+ * rotation done in fp32, and the result rounded to the destination
  * dtype (FP8_E4M3 caches: rotated, then quantised). rope_base must be finite
  * and > 0 (10000 is usual); positions must be >= 0. Token r of a chunk sits at
  * position pos0 + r; with pos0 = chunk id * n for every chunk, queries and keys
