@@ -21,7 +21,8 @@ __all__ = [
     "bca_cache_set_kv_scales", "bca_append_chunk", "bca_attend_workspace_bytes", "bca_attend",
     "bca_append_chunk_rope", "bca_attend_rope_workspace_bytes", "bca_attend_rope",
     "bca_cache_slot_chunk", "bca_cache_set_slot_chunk", "bca_attend_plan", "bca_status_string",
-    "bca_last_error", "Cache", "LIB_PATH", "load_library",
+    "bca_last_error", "bca_sequence_spec", "bca_attend_sequence_workspace_bytes",
+    "bca_attend_sequence", "attend_sequence", "Cache", "LIB_PATH", "load_library",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbca.so")
@@ -43,6 +44,13 @@ class bca_window_spec(ctypes.Structure):
     _fields_ = [("q_chunk_id", ctypes.c_int64), ("history", ctypes.c_int32),
                 ("use_ref", ctypes.c_int32), ("num_segments", ctypes.c_int32),
                 ("scale", ctypes.c_float)]
+
+
+class bca_sequence_spec(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("chunk_tokens", ctypes.c_int32), ("num_chunks", ctypes.c_int32),
+                ("prefix_tokens", ctypes.c_int32), ("history", ctypes.c_int32),
+                ("num_segments", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
 class bca_plan_info(ctypes.Structure):
@@ -104,6 +112,11 @@ def load_library(path: str = LIB_PATH):
     lib.bca_attend_rope_workspace_bytes.restype = SZ
     lib.bca_attend_rope.argtypes = [P, I32, spec_p, P, P, P, I32, D64, I64, P, P, P, SZ, P]
     lib.bca_attend_rope.restype = I32
+    seq_p = ctypes.POINTER(bca_sequence_spec)
+    lib.bca_attend_sequence_workspace_bytes.argtypes = [seq_p, I32]
+    lib.bca_attend_sequence_workspace_bytes.restype = SZ
+    lib.bca_attend_sequence.argtypes = [seq_p, P, P, P, I32, P, P, P, SZ, P]
+    lib.bca_attend_sequence.restype = I32
     lib.bca_cache_slot_chunk.argtypes = [P, I32, I32, ctypes.POINTER(I64)]
     lib.bca_cache_slot_chunk.restype = I32
     lib.bca_cache_set_slot_chunk.argtypes = [P, I32, I32, I64]
@@ -208,6 +221,60 @@ def bca_attend_rope(handle: int, layer: int, spec, q: int, k_cur: int, v_cur: in
                                 ctypes.c_void_p(o), ctypes.c_void_p(lse),
                                 ctypes.c_void_p(workspace), workspace_bytes,
                                 ctypes.c_void_p(stream)))
+
+
+def bca_attend_sequence_workspace_bytes(spec: bca_sequence_spec, qkv_dtype: int) -> int:
+    return int(_lib.bca_attend_sequence_workspace_bytes(ctypes.byref(spec), qkv_dtype))
+
+
+def bca_attend_sequence(spec: bca_sequence_spec, q: int, k: int, v: int, qkv_dtype: int, o: int,
+                        lse: int, workspace: int, workspace_bytes: int, stream: int = 0) -> None:
+    _check(_lib.bca_attend_sequence(ctypes.byref(spec), ctypes.c_void_p(q), ctypes.c_void_p(k),
+                                    ctypes.c_void_p(v), qkv_dtype, ctypes.c_void_p(o),
+                                    ctypes.c_void_p(lse), ctypes.c_void_p(workspace),
+                                    workspace_bytes, ctypes.c_void_p(stream)))
+
+
+def attend_sequence(q, k, v, chunk_tokens: int, history: int, prefix_tokens: int = 0,
+                    num_segments: int = 0, scale: float | None = None, workspace=None,
+                    stream=None):
+    """Training-form block-causal attention over a whole sequence of chunks
+    (bca_attend_sequence) on torch device tensors: q [C*n][H][d], k and v
+    [P + C*n][H][d] (memory prefix first), fp32 or bf16, contiguous. Returns
+    (o [C*n][H][d], lse [C][H][n] fp32). ``workspace``, if given, is a uint8
+    device tensor of at least bca_attend_sequence_workspace_bytes() bytes,
+    256-byte aligned."""
+    import torch
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise BcaError(-4, "q, k, v must be float32 or bfloat16")
+    for t in (q, k, v):
+        if not t.is_cuda or t.dtype != q.dtype or not t.is_contiguous() or t.dim() != 3:
+            raise BcaError(-1, "q, k, v must be contiguous [rows][H][d] device tensors of one dtype")
+    rows_q, H, d = q.shape
+    n = int(chunk_tokens)
+    if n <= 0 or rows_q % n != 0:
+        raise BcaError(-1, f"q rows {rows_q} are not a multiple of chunk_tokens {n}")
+    C = rows_q // n
+    if tuple(k.shape) != (prefix_tokens + rows_q, H, d) or k.shape != v.shape:
+        raise BcaError(-1, f"k and v must have shape {(prefix_tokens + rows_q, H, d)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    spec = bca_sequence_spec(H, d, n, C, int(prefix_tokens), int(history), int(num_segments),
+                             float(scale))
+    dt = F32 if q.dtype == torch.float32 else BF16
+    need = bca_attend_sequence_workspace_bytes(spec, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((C, H, n), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    bca_attend_sequence(spec, q.data_ptr(), k.data_ptr(), v.data_ptr(), dt, o.data_ptr(),
+                        lse.data_ptr(), workspace.data_ptr() if workspace is not None else 0,
+                        workspace.numel() if workspace is not None else 0, int(stream))
+    return o, lse
 
 
 def bca_cache_slot_chunk(handle: int, layer: int, slot: int) -> int:

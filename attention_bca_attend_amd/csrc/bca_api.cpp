@@ -151,12 +151,16 @@ int32_t pieces_bound(int64_t units, int64_t T, int64_t P) {
 // a unit boundary, and each unit has the fewest partial outputs to merge);
 // otherwise one range of tile iterations per resident work group
 // ("stream-K").
-int64_t choose_wgs(const bca_cache* c, Kern k, int64_t units, int64_t T, int32_t G) {
+int64_t choose_wgs_on(int cus, Kern k, int64_t units, int64_t T, int32_t G) {
   const int64_t I = units * T;
   if (G >= 1) return units * std::min<int64_t>(G, T);
-  const int64_t target = (int64_t)compute_units(c) * wgs_per_cu(k);
+  const int64_t target = (int64_t)cus * wgs_per_cu(k);
   if (units <= target) return units * std::min<int64_t>(T, target / units);
   return std::max<int64_t>(1, std::min(I, target));
+}
+
+int64_t choose_wgs(const bca_cache* c, Kern k, int64_t units, int64_t T, int32_t G) {
+  return choose_wgs_on(compute_units(c), k, units, T, G);
 }
 
 // fp8 cache: the current chunk's K and V quantised to e4m3, [H][n][d] each,
@@ -541,6 +545,8 @@ bca_status attend_impl(const bca_cache* c, int32_t layer, const bca_window_spec*
     a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + po);
   }
   a.cache_head_elems = (int64_t)(d.ring_slots + d.has_ref) * d.chunk_tokens * d.head_dim;
+  a.cache_span_elems = a.cache_head_elems;
+  a.cache_row_elems = d.head_dim;
   a.n = d.chunk_tokens;
   a.H = d.num_heads;
   a.nk_cache = p.nk_cache;
@@ -563,6 +569,157 @@ bca_status attend_impl(const bca_cache* c, int32_t layer, const bca_window_spec*
   int err = launch_attention(p, a, d.head_dim, (void*)stream);
   if (err == -1) return fail(BCA_ERR_UNSUPPORTED, "no attention kernel for this dtype pair yet");
   if (err != 0) return fail(BCA_ERR_HIP, "attention launch failed (hip error %d)", err);
+  g_err.clear();
+  return BCA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Training form: every chunk of a sequence at once (bca_attend_sequence).
+
+bool seq_spec_ok(const bca_sequence_spec* s, int32_t qkv_dtype, std::string* why) {
+  if (!s) return *why = "spec is NULL", false;
+  if (s->num_heads <= 0 || s->chunk_tokens <= 0 || s->num_chunks <= 0)
+    return *why = "num_heads, chunk_tokens and num_chunks must be > 0", false;
+  if (s->prefix_tokens < 0) return *why = "prefix_tokens must be >= 0", false;
+  if (s->history < 0) return *why = "history must be >= 0", false;
+  if (s->num_segments < 0 || s->num_segments > kMaxSegments)
+    return *why = "num_segments must be in [0, 64]", false;
+  if (!std::isfinite(s->scale)) return *why = "scale must be finite", false;
+  if (s->head_dim != 64 && s->head_dim != 128) return *why = "head_dim must be 64 or 128", false;
+  if (qkv_dtype != BCA_F32 && qkv_dtype != BCA_BF16)
+    return *why = "qkv_dtype must be BCA_F32 or BCA_BF16", false;
+  // every byte offset into one head's K/V span must fit the kernels' 32-bit
+  // buffer offsets
+  const int64_t rows = (int64_t)s->prefix_tokens + (int64_t)s->num_chunks * s->chunk_tokens;
+  const int64_t span = ((rows - 1) * s->num_heads * s->head_dim + s->head_dim) *
+                       (int64_t)elem_size(qkv_dtype);
+  if (rows > INT32_MAX / 2 || span > (int64_t)INT32_MAX - 4096)
+    return *why = "K/V span per head exceeds 2 GiB", false;
+  return true;
+}
+
+// Plan of chunk c. Its visible cache keys are the prefix and the window's
+// earlier chunks, rows of the token-major K/V: one run when the two touch
+// (c <= W), two otherwise.
+void seq_plan(const bca_sequence_spec* s, int32_t qkv_dtype, int cus, int64_t c, Plan& p) {
+  std::memset(&p, 0, sizeof p);
+  const int64_t n = s->chunk_tokens, P = s->prefix_tokens;
+  const int64_t first = std::max<int64_t>(0, c - s->history);  // first chunk of the window
+  const int64_t hist = (c - first) * n;                        // window keys before chunk c
+  p.nruns = 0;
+  if (P > 0) p.runs[p.nruns++] = Run{0, (int32_t)P, 0, 0};
+  if (hist > 0) {
+    const int64_t phys = P + first * n;
+    if (p.nruns > 0 && p.runs[0].phys + p.runs[0].len == phys)
+      p.runs[0].len += (int32_t)hist;
+    else
+      p.runs[p.nruns++] = Run{(int32_t)P, (int32_t)hist, (int32_t)phys, 0};
+  }
+  p.nk_cache = (int32_t)(P + hist);
+  p.kern = qkv_dtype == BCA_F32 ? Kern::F32 : Kern::BF16;
+  const TileShape ts = tile_shape(p.kern);
+  p.bm = ts.bm;
+  p.bn = ts.bn;
+  p.q_tiles = (int32_t)((n + p.bm - 1) / p.bm);
+  p.cache_tiles = (p.nk_cache + p.bn - 1) / p.bn;
+  p.kv_tiles = p.cache_tiles + (int32_t)((n + p.bn - 1) / p.bn);
+  p.nk = p.nk_cache + (int32_t)n;
+  p.units = s->num_heads * p.q_tiles;
+  p.wgs = (int32_t)choose_wgs_on(cus, p.kern, p.units, p.kv_tiles, s->num_segments);
+  p.jmax = pieces_bound(p.units, p.kv_tiles, p.wgs);
+  p.merge = p.jmax > 1 ? 1 : 0;
+  p.ws_bytes = p.merge ? partial_bytes(p.units, p.jmax, p.bm, s->head_dim) : 0;
+}
+
+// Chunks c >= W all have the plan of chunk W, so chunks 0 .. min(C-1, W) are
+// the only distinct ones; the workspace is the largest they need.
+size_t seq_workspace(const bca_sequence_spec* s, int32_t qkv_dtype, int cus) {
+  size_t ws = 0;
+  const int64_t distinct = std::min<int64_t>(s->num_chunks, (int64_t)s->history + 1);
+  for (int64_t c = 0; c < distinct; ++c) {
+    Plan p;
+    seq_plan(s, qkv_dtype, cus, c, p);
+    ws = std::max(ws, p.ws_bytes);
+  }
+  return ws;
+}
+
+int seq_cus() {
+  const int cus = device_compute_units();
+  return cus > 0 ? cus : 256;
+}
+
+bca_status attend_sequence_impl(const bca_sequence_spec* s, const void* q, const void* k,
+                                const void* v, int32_t qkv_dtype, void* o, float* lse,
+                                void* workspace, size_t workspace_bytes, bca_stream_t stream) {
+  std::string why;
+  if (!s) return fail(BCA_ERR_INVALID_ARG, "spec is NULL");
+  if (elem_size(qkv_dtype) == 0) return fail(BCA_ERR_INVALID_ARG, "qkv_dtype is not a bca_dtype");
+  if ((qkv_dtype != BCA_F32 && qkv_dtype != BCA_BF16) ||
+      (s->head_dim != 64 && s->head_dim != 128))
+    return fail(BCA_ERR_UNSUPPORTED,
+                "sequence attention runs F32 or BF16 with head_dim 64 or 128");
+  if (!seq_spec_ok(s, qkv_dtype, &why)) return fail(BCA_ERR_INVALID_ARG, "%s", why.c_str());
+  if (!q || !k || !v || !o) return fail(BCA_ERR_INVALID_ARG, "q, k, v and o must not be NULL");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      (lse && !aligned(lse, 4)))
+    return fail(BCA_ERR_INVALID_ARG, "q, k, v and o must be 16-byte aligned (lse 4)");
+  const int cus = seq_cus();
+  const size_t need = seq_workspace(s, qkv_dtype, cus);
+  if (need > 0) {
+    if (!workspace) return fail(BCA_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    if (!aligned(workspace, 256))
+      return fail(BCA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(BCA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
+                  need);
+  }
+  const int64_t n = s->chunk_tokens, H = s->num_heads, D = s->head_dim, P = s->prefix_tokens;
+  const size_t es = elem_size(qkv_dtype);
+  const int64_t rows = P + (int64_t)s->num_chunks * n;
+  for (int64_t c = 0; c < s->num_chunks; ++c) {
+    Plan p;
+    seq_plan(s, qkv_dtype, cus, c, p);
+    AttnArgs a;
+    std::memset(&a, 0, sizeof a);
+    const size_t chunk_off = (size_t)(c * n * H * D) * es;      // chunk c's rows of q and o
+    const size_t cur_off = (size_t)((P + c * n) * H * D) * es;  // chunk c's rows of k and v
+    a.q = static_cast<const char*>(q) + chunk_off;
+    a.kcur = static_cast<const char*>(k) + cur_off;
+    a.vcur = static_cast<const char*>(v) + cur_off;
+    a.kc = k;
+    a.vc = v;
+    a.o = static_cast<char*>(o) + chunk_off;
+    a.lse = lse ? lse + (size_t)(c * H * n) : nullptr;
+    if (p.merge) {
+      size_t po = (size_t)p.units * p.jmax * p.bm * D * 4;
+      po = (po + 255) & ~(size_t)255;
+      a.part_o = static_cast<float*>(workspace);
+      a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + po);
+    }
+    // the "cache" is the token-major K/V itself: heads d apart, rows H*d apart
+    a.cache_head_elems = D;
+    a.cache_span_elems = (rows - 1) * H * D + D;
+    a.cache_row_elems = (int32_t)(H * D);
+    a.n = (int32_t)n;
+    a.H = (int32_t)H;
+    a.nk_cache = p.nk_cache;
+    a.cache_tiles = p.cache_tiles;
+    a.T = p.kv_tiles;
+    a.QT = p.q_tiles;
+    a.units = p.units;
+    a.P = p.wgs;
+    a.jmax = p.jmax;
+    a.scale = s->scale;
+    a.scale_log2 = (float)((double)s->scale * 1.4426950408889634);
+    a.xcd_remap = (p.wgs % 8 == 0) ? 1 : 0;
+    a.nruns = p.nruns;
+    for (int i = 0; i < p.nruns; ++i) a.runs[i] = p.runs[i];
+    const int err = launch_attention(p, a, (int)D, (void*)stream);
+    if (err != 0)
+      return fail(BCA_ERR_HIP, "attention launch for chunk %lld failed (hip error %d)",
+                  (long long)c, err);
+  }
   g_err.clear();
   return BCA_OK;
 }
@@ -595,6 +752,18 @@ bca_status bca_attend_rope(const bca_cache* c, int32_t layer, const bca_window_s
   const RopeArg r{std::log2(rope_base), pos0};
   return attend_impl(c, layer, s, q, k_cur, v_cur, qkv_dtype, o, lse, workspace,
                      workspace_bytes, stream, &r);
+}
+
+size_t bca_attend_sequence_workspace_bytes(const bca_sequence_spec* s, int32_t qkv_dtype) {
+  std::string why;
+  if (!seq_spec_ok(s, qkv_dtype, &why)) return 0;
+  return seq_workspace(s, qkv_dtype, seq_cus());
+}
+
+bca_status bca_attend_sequence(const bca_sequence_spec* s, const void* q, const void* k,
+                               const void* v, int32_t qkv_dtype, void* o, float* lse,
+                               void* workspace, size_t workspace_bytes, bca_stream_t stream) {
+  return attend_sequence_impl(s, q, k, v, qkv_dtype, o, lse, workspace, workspace_bytes, stream);
 }
 
 bca_status bca_cache_slot_chunk(const bca_cache* c, int32_t layer, int32_t slot,

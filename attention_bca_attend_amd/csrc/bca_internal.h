@@ -79,7 +79,10 @@ struct AttnArgs {
   float* lse;         // [H][n] or null
   float* part_o;      // [units][jmax][bm][d] fp32
   float* part_lse;    // [units][jmax][bm]
-  int64_t cache_head_elems;  // (S+R)*n*d
+  int64_t cache_head_elems;  // elements between heads' first cache rows: (S+R)*n*d for the
+                             // ring, d for a token-major sequence [rows][H][d]
+  int64_t cache_span_elems;  // elements one head's cache rows span (buffer resource size)
+  int32_t cache_row_elems;   // elements between consecutive cache rows: d (ring), H*d (sequence)
   int32_t n, H, nk_cache, cache_tiles, T, QT, units, P, jmax;
   float scale;        // softmax scale
   float scale_log2;   // scale * log2(e)

@@ -96,7 +96,7 @@ __device__ __forceinline__ HeadSrc head_src(const void* cache_base, const void* 
   HeadSrc r;
   r.cache = uniform_ptr(static_cast<const char*>(cache_base) +
                         (int64_t)h * a.cache_head_elems * es_cache);
-  r.cache_bytes = (int)(a.cache_head_elems * es_cache);
+  r.cache_bytes = (int)(a.cache_span_elems * es_cache);
   r.cur = uniform_ptr(static_cast<const char*>(cur_base) + (int64_t)h * D * es_cur);
   r.cur_bytes = (int)(((int64_t)(a.n - 1) * a.H * D + D) * es_cur);
   return r;
@@ -120,7 +120,8 @@ __device__ __forceinline__ void load_cache_rows(const AttnArgs& a, const HeadSrc
   if (j0 + BN <= R0.vstart + R0.len) {
 #pragma unroll
     for (int i = 0; i < NR; ++i)
-      out[i] = buf16(src.cache, src.cache_bytes, (R0.phys + j[i] - R0.vstart) * D * es + colb);
+      out[i] = buf16(src.cache, src.cache_bytes,
+                     (R0.phys + j[i] - R0.vstart) * a.cache_row_elems * es + colb);
     return;
   }
 #pragma unroll
@@ -132,7 +133,8 @@ __device__ __forceinline__ void load_cache_rows(const AttnArgs& a, const HeadSrc
     for (int i = 0; i < NR; ++i) {
       const bool in = j[i] >= R.vstart && j[i] < R.vstart + R.len;
       const uint4 v = buf16(src.cache, src.cache_bytes,
-                            in ? (R.phys + j[i] - R.vstart) * D * es + colb : kOob);
+                            in ? (R.phys + j[i] - R.vstart) * a.cache_row_elems * es + colb
+                               : kOob);
       out[i].x |= v.x;
       out[i].y |= v.y;
       out[i].z |= v.z;
@@ -277,12 +279,13 @@ __device__ __forceinline__ FetchRun fetch_run_at(const AttnArgs& a, int ri) {
 template <int D>
 struct FetchLane {
   int r[Bf16Cfg<D>::IPW];
+  int roff[Bf16Cfg<D>::IPW];  // r * cache row pitch in bytes
   int kcol[Bf16Cfg<D>::IPW];
   int vcol[Bf16Cfg<D>::IPW];
 };
 
 template <int D>
-__device__ __forceinline__ FetchLane<D> fetch_lane(int wave, int lane) {
+__device__ __forceinline__ FetchLane<D> fetch_lane(int wave, int lane, int rowb) {
   using C = Bf16Cfg<D>;
   FetchLane<D> f;
   const int lrow = lane / C::CPR, lchunk = lane % C::CPR;
@@ -290,6 +293,7 @@ __device__ __forceinline__ FetchLane<D> fetch_lane(int wave, int lane) {
   for (int q = 0; q < C::IPW; ++q) {
     const int r = (wave * C::IPW + q) * C::RPI + lrow;
     f.r[q] = r;
+    f.roff[q] = r * rowb;
     f.kcol[q] = (lchunk ^ k_swizzle<D>(r)) << 4;
     f.vcol[q] = (lchunk ^ v_swizzle<D>(r)) << 4;
   }
@@ -312,10 +316,10 @@ __device__ __forceinline__ void bf16_fetch_tile(const AttnArgs& a, const HeadSrc
     while (j0 >= fr.vend && fr.ri + 1 < a.nruns) fr = fetch_run_at(a, fr.ri + 1);
     if (j0 + C::BN <= fr.vend) {
       // the whole tile lies in one run
-      const int base = fr.phys + j0 - fr.vstart;
+      const int base = (fr.phys + j0 - fr.vstart) * a.cache_row_elems * 2;
 #pragma unroll
       for (int q = 0; q < C::IPW; ++q) {
-        const int off = (base + fl.r[q]) * C::ROWB;
+        const int off = base + fl.roff[q];
         lds_load16(ks.cache, ks.cache_bytes, off + fl.kcol[q], kdst + q * 1024);
         lds_load16(vs.cache, vs.cache_bytes, off + fl.vcol[q], vdst + q * 1024);
       }
@@ -330,8 +334,8 @@ __device__ __forceinline__ void bf16_fetch_tile(const AttnArgs& a, const HeadSrc
           if (R.vstart >= j0 + C::BN) break;
           if (j >= R.vstart && j < R.vstart + R.len) phys = R.phys + j - R.vstart;
         }
-        const int koff = phys >= 0 ? phys * C::ROWB + fl.kcol[q] : kOob;
-        const int voff = phys >= 0 ? phys * C::ROWB + fl.vcol[q] : kOob;
+        const int koff = phys >= 0 ? phys * a.cache_row_elems * 2 + fl.kcol[q] : kOob;
+        const int voff = phys >= 0 ? phys * a.cache_row_elems * 2 + fl.vcol[q] : kOob;
         lds_load16(ks.cache, ks.cache_bytes, koff, kdst + q * 1024);
         lds_load16(vs.cache, vs.cache_bytes, voff, vdst + q * 1024);
       }
@@ -514,7 +518,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
       voff[db] = C::TILE_BYTES + (4 * hi + k) * C::ROWB + ((4 * (db ^ kx) + c0) << 4) +
                  (ai & 1) * 8;
   }
-  const FetchLane<D> fl = fetch_lane<D>(wave, lane);
+  const FetchLane<D> fl = fetch_lane<D>(wave, lane, a.cache_row_elems * 2);
 
   while (it < it_end) {
     const int u = (int)(it / a.T);
@@ -765,7 +769,7 @@ __device__ __forceinline__ F8Src f8_src(const AttnArgs& a, int h) {
   f.vc = uniform_ptr(static_cast<const char*>(a.vc) + (int64_t)h * a.cache_head_elems);
   f.kcur = uniform_ptr(static_cast<const char*>(a.kcur) + (int64_t)h * a.n * D);
   f.vcur = uniform_ptr(static_cast<const char*>(a.vcur) + (int64_t)h * a.n * D);
-  f.cache_bytes = (int)a.cache_head_elems;
+  f.cache_bytes = (int)a.cache_span_elems;
   f.cur_bytes = a.n * D;
   return f;
 }

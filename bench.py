@@ -1,6 +1,6 @@
 """Benchmark of block-causal ring-KV chunk attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1|2|3|4]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1|2|3|4|5|6]
 
 One step is one chunk of the chunk-wise autoregressive loop: for every denoise
 step and every layer one bca_attend (the chunk's queries over the current
@@ -21,6 +21,9 @@ Workloads (synthetic inputs, random values of the stated shapes):
      rotate K on the way into the ring (bca_append_chunk_rope) and attends
      rotate Q and the chunk's own K first (bca_attend_rope); base 10000,
      token r of chunk t at position t*n + r.
+  6  training form of workload 1: a clip of 8 chunks (12 heads, d 128, 1536
+     tokens each, window of the current + previous 2 chunks) attended at once
+     with bca_attend_sequence, 30 layers per step, each with its own Q/K/V.
 
 Prints one JSON line. `value` is algorithmic attention TFLOP/s over the whole
 step (4*H*n*N_k*d per chunk-layer, appends included in the time), from a timed
@@ -57,6 +60,8 @@ CONFIGS = {
             L=30, steps_per_chunk=1, kv="fp8"),
     5: dict(workload="wantofight_bf16_rope_chunk", H=12, d=128, n=1536, S=2, W=2, R=0, G=0,
             L=30, steps_per_chunk=4, kv="bf16", rope=10000.0),
+    6: dict(workload="wantofight_bf16_sequence8", H=12, d=128, n=1536, C=8, W=2, P=0, G=0, L=30,
+            kv="bf16", sequence=True),
 }
 
 
@@ -130,6 +135,119 @@ def cpu_baseline(cache, cfg, q0, k0, v0, t):
                       f"{reps} time(s) (fp64 dense-mask oracle, {dt:.1f} s in all)"}
 
 
+def sequence_flops(H, d, n, C, W, P):
+    """Algorithmic FLOP of one whole-sequence call: chunk c's n queries each
+    meet P + (min(c, W) + 1) n keys, 4 d FLOP per (query, key) pair."""
+    return sum(4.0 * H * n * (P + (min(c, W) + 1) * n) * d for c in range(C))
+
+
+def cpu_baseline_sequence(cfg, q, k, v):
+    """The oracle's whole-sequence form on layer 0, restricted to the first few
+    heads (heads are independent), scaled until the sample takes about 10 s."""
+    import oracle
+
+    H, d, n, C, W, P = (cfg[x] for x in ("H", "d", "n", "C", "W", "P"))
+    qn, kn, vn = (x.float().cpu().numpy() for x in (q, k, v))
+
+    def run(hs):
+        t0 = time.perf_counter()
+        oracle.attend_sequence(qn[:, :hs], kn[:, :hs], vn[:, :hs], n, W, P, 1 / math.sqrt(d))
+        return time.perf_counter() - t0
+
+    hs = 1
+    dt = run(hs)
+    if dt < 3.0 and H > 1:
+        hs = min(H, max(2, int(math.ceil(10.0 / max(dt, 1e-3)))))
+        dt = run(hs)
+    flops = sequence_flops(hs, d, n, C, W, P)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"layer 0 whole sequence, {hs} of {H} heads x {C} chunks of {n} tokens "
+                      f"(fp64 dense-mask oracle, {dt:.1f} s)"}
+
+
+def main_sequence(args, cfg):
+    """Workload 6: one step = one whole-sequence call per layer."""
+    import torch
+
+    import attention_bca_attend_amd as bca
+
+    H, d, n, C, W, P, G, L = (cfg[k] for k in ("H", "d", "n", "C", "W", "P", "G", "L"))
+    steps = args.steps if args.steps is not None else 5
+    torch.cuda.set_device(0)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20261202)
+    log(f"config {args.config}: {cfg}")
+    Q = [gen((C * n, H, d), g) for _ in range(L)]
+    K = [gen((P + C * n, H, d), g) for _ in range(L)]
+    V = [gen((P + C * n, H, d), g) for _ in range(L)]
+    O = torch.empty((C * n, H, d), dtype=torch.bfloat16, device="cuda")
+    spec = bca.bca_sequence_spec(H, d, n, C, P, W, G, 1.0 / math.sqrt(d))
+    need = bca.bca_attend_sequence_workspace_bytes(spec, bca.BF16)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    LSE = torch.empty((C, H, n), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    flop_call = sequence_flops(H, d, n, C, W, P)
+
+    def call(l):
+        bca.bca_attend_sequence(spec, Q[l].data_ptr(), K[l].data_ptr(), V[l].data_ptr(),
+                                bca.BF16, O.data_ptr(), LSE.data_ptr(), ws.data_ptr(), need,
+                                stream)
+
+    def run_step():
+        for l in range(L):
+            call(l)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    # one event pair around the K steps and one per step, none inside a step;
+    # the step is nothing but the whole-sequence calls, so the same region
+    # gives the per-call time
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    per_step = []
+    start.record()
+    for _ in range(steps):
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record()
+        run_step()
+        c1.record()
+        per_step.append((c0, c1))
+    end.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / steps
+    step_ms = [a.elapsed_time(b) for a, b in per_step]
+    call_us = ms_step * 1e3 / L
+    tflops = L * flop_call / (ms_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["bf16"]
+    log(f"{steps} steps: {ms_step:.3f} ms/step, {call_us:.1f} us per sequence call, "
+        f"{tflops:.1f} TFLOP/s")
+    result = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg["workload"], "heads": H, "head_dim": d, "chunk_tokens": n,
+                   "chunks": C, "history": W, "prefix_tokens": P,
+                   "segments": G if G else "auto", "layers": L, "batch": 1},
+        "us_per_chunk_layer": round(call_us / C, 3),
+        "sequence_call_us": round(call_us, 3),
+        "pct_mfma_peak": round(100.0 * tflops / peak, 2),
+        "step_ms_min_max": [round(min(step_ms), 4), round(max(step_ms), 4)],
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                     "traffic": measured_traffic(cfg["workload"]),
+                     "kernel": f"bca_attend_sequence: {C} x (attn_bf16_kernel + merge_kernel "
+                               f"where split)"},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline_sequence(cfg, Q[0], K[0], V[0])
+    print(json.dumps(result), flush=True)
+
+
 KERNEL_SOURCE = os.path.join(ROOT, "attention_bca_attend_amd", "csrc", "bca_kernels.hip")
 COPY_BYTES = 512 << 20
 
@@ -197,6 +315,9 @@ def main():
     cfg = dict(CONFIGS[args.config])
     if args.layers:
         cfg["L"] = args.layers
+    if cfg.get("sequence"):
+        main_sequence(args, cfg)
+        return
     steps = args.steps if args.steps is not None else (64 if args.config == 3 else 5)
     H, d, n, S, W, R, G, L = (cfg[k] for k in ("H", "d", "n", "S", "W", "R", "G", "L"))
     spc = cfg["steps_per_chunk"]

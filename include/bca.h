@@ -209,6 +209,55 @@ bca_status bca_attend_rope(const bca_cache* cache, int32_t layer, const bca_wind
                            float* lse, void* workspace, size_t workspace_bytes,
                            bca_stream_t stream);
 
+/* Block-causal attention over a whole sequence of chunks at once (the
+ * training form). "WanToFight" review, training Stage 2 (causal adaptation):
+ * the model is trained with the same block-causal mask it later streams with,
+ * every chunk of a clip attending bidirectionally to itself and to the W
+ * chunks before it. Memory prefix: a run of context tokens placed before chunk
+ * 0 that every chunk sees (the reference frame of "Matrix-Game 4.0",
+ * prerequisite "causal autoregression and KV cache"; a pinned context of sink
+ * and memory tokens ahead of the generated chunks in the other pages' memory
+ * designs). The prefix has keys and values only, no queries.
+ *
+ * With C = num_chunks, n = chunk_tokens and P = prefix_tokens, query token
+ * r of chunk c (row c*n + r of q) attends to key rows
+ *     0 .. P-1                                     (the prefix)
+ *     P + c'*n .. P + c'*n + n-1  for max(0, c-W) <= c' <= c,
+ * i.e. exactly what bca_attend gives chunk c with the W chunks before it in
+ * the ring and the prefix as its reference block (when P = n).
+ *
+ * Layouts (dense, row-major, qkv_dtype):
+ *     q, o : [C*n][H][d]
+ *     k, v : [P + C*n][H][d]   prefix rows first, then the chunks in order
+ *     lse  : fp32 [C][H][n] (natural log), or NULL
+ * qkv_dtype: BCA_F32 or BCA_BF16; head_dim 64 or 128. The chunks are computed
+ * one after the other on `stream` (each as one attention launch plus, when its
+ * window is split, one merge launch), sharing the workspace.
+ * Errors: BCA_ERR_INVALID_ARG for a NULL or bad spec (non-positive sizes,
+ * history < 0, prefix_tokens < 0, num_segments outside [0, 64], non-finite
+ * scale), NULL or misaligned buffers (16 bytes; lse 4), or K/V larger than
+ * 2 GiB per head's span; BCA_ERR_UNSUPPORTED for another dtype or head_dim;
+ * BCA_ERR_WORKSPACE when the workspace is missing, not 256-byte aligned or
+ * smaller than bca_attend_sequence_workspace_bytes(); BCA_ERR_HIP for a launch
+ * failure (chunks before it may already have been enqueued). */
+typedef struct {
+  int32_t num_heads;     /* H */
+  int32_t head_dim;      /* d */
+  int32_t chunk_tokens;  /* n */
+  int32_t num_chunks;    /* C */
+  int32_t prefix_tokens; /* P >= 0 */
+  int32_t history;       /* W >= 0 (W >= C: every earlier chunk) */
+  int32_t num_segments;  /* as in bca_window_spec: 0 automatic, G >= 1 segments */
+  float scale;           /* softmax scale, usually 1/sqrt(d) */
+} bca_sequence_spec;
+
+/* Workspace bytes bca_attend_sequence needs (0 if none, also 0 on a bad spec). */
+size_t bca_attend_sequence_workspace_bytes(const bca_sequence_spec* spec, int32_t qkv_dtype);
+
+bca_status bca_attend_sequence(const bca_sequence_spec* spec, const void* q, const void* k,
+                               const void* v, int32_t qkv_dtype, void* o, float* lse,
+                               void* workspace, size_t workspace_bytes, bca_stream_t stream);
+
 /* Host-side slot table query: chunk id held by ring slot `slot` (0 <= slot < S)
  * of `layer`, -1 if empty. slot == S (with has_ref) reports the reference block
  * (its recorded id, or -1). */

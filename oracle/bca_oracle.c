@@ -231,6 +231,45 @@ int bca_oracle_attend(int H, int d, int n, int n_hist, const int64_t* hist_ids,
 }
 
 /*
+ * Block-causal attention over a whole sequence at once, the training form
+ * [WTF training Stage 2, causal adaptation: training uses the block-causal
+ * mask itself], with a memory prefix of P context tokens ahead of chunk 0
+ * that every chunk sees [MG4 prerequisite on the reference frame].
+ *   q [C*n][H][d]; k, v [P + C*n][H][d] (prefix rows first); o [C*n][H][d];
+ *   lse [H][C*n].
+ * Query row i belongs to chunk i / n; key row j is a prefix token when j < P,
+ * otherwise a token of chunk (j - P) / n. The dense mask, written out as a
+ * (C*n) x (P + C*n) byte matrix, admits key j for row i iff j is a prefix
+ * token, or its chunk c' satisfies chunk(i) - W <= c' <= chunk(i) (the chunk
+ * itself, bidirectionally, and the W chunks before it). Then
+ * bca_oracle_attend_masked.
+ */
+int bca_oracle_attend_sequence(int C, int n, int H, int d, int P, int W, const double* q,
+                               const double* k, const double* v, double scale, double* o,
+                               double* lse) {
+  if (C < 1 || n < 1 || H < 1 || d < 1 || P < 0 || W < 0) return -1;
+  int nq = C * n, nk = P + C * n;
+  uint8_t* M = (uint8_t*)malloc((size_t)nq * nk);
+  if (!M) return -2;
+  for (int i = 0; i < nq; ++i) {
+    int ci = i / n;
+    for (int j = 0; j < nk; ++j) {
+      int admit;
+      if (j < P) {
+        admit = 1;
+      } else {
+        int cj = (j - P) / n;
+        admit = (cj >= ci - W) && (cj <= ci);
+      }
+      M[(size_t)i * nk + j] = (uint8_t)admit;
+    }
+  }
+  int rc = bca_oracle_attend_masked(nq, nk, H, d, q, k, v, M, scale, 0, o, lse);
+  free(M);
+  return rc;
+}
+
+/*
  * Log-sum-exp merge of G partial results over disjoint key sets [MG4
  * prerequisite "causal autoregression and KV cache": partial outputs of the
  * window's intervals are merged by log-sum-exp]. Each partial is a normalised

@@ -71,6 +71,9 @@ class OracleLib:
         lib.bca_oracle_set_threads.restype = None
         lib.bca_oracle_rope.argtypes = [ctypes.c_int] * 3 + [P, ctypes.c_int64, ctypes.c_double, P]
         lib.bca_oracle_rope.restype = ctypes.c_int
+        lib.bca_oracle_attend_sequence.argtypes = [ctypes.c_int] * 6 + [P, P, P, ctypes.c_double,
+                                                                         P, P]
+        lib.bca_oracle_attend_sequence.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -154,6 +157,24 @@ class OracleLib:
         flat = [self.lib.bca_oracle_e4m3_encode(float(v)) for v in a.reshape(-1)]
         return np.array(flat, dtype=np.uint8).reshape(a.shape)
 
+    def attend_sequence(self, q, k, v, n: int, W: int, prefix: int, scale: float):
+        """Training-form block-causal attention over a whole sequence: q
+        [C*n][H][d], k and v [prefix + C*n][H][d]. Returns (o [C*n][H][d],
+        lse [C][H][n]) in float64."""
+        q, k, v = _f64(q), _f64(k), _f64(v)
+        nq, H, d = q.shape
+        assert nq % n == 0
+        C = nq // n
+        assert k.shape == (prefix + nq, H, d) and v.shape == k.shape
+        o = np.empty((nq, H, d), dtype=np.float64)
+        lse = np.empty((H, nq), dtype=np.float64)
+        rc = self.lib.bca_oracle_attend_sequence(C, n, H, d, int(prefix), int(W), _ptr(q),
+                                                 _ptr(k), _ptr(v), float(scale), _ptr(o),
+                                                 _ptr(lse))
+        if rc != 0:
+            raise RuntimeError(f"bca_oracle_attend_sequence failed ({rc})")
+        return o, np.ascontiguousarray(lse.reshape(H, C, n).transpose(1, 0, 2))
+
     def rope(self, x, pos0: int, base: float) -> np.ndarray:
         """Rotary position embedding of x [n][H][d]; token r at position pos0 + r."""
         a = _f64(x)
@@ -214,6 +235,10 @@ def e4m3_encode(*a, **k):
 
 def rope(*a, **k):
     return default().rope(*a, **k)
+
+
+def attend_sequence(*a, **k):
+    return default().attend_sequence(*a, **k)
 
 
 def quant_e4m3(*a, **k):

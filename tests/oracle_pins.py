@@ -19,7 +19,11 @@ What pins what:
 * large logits (max subtraction);
 * OCP E4M3 codec against torch.float8_e4m3fn and the spec's rounding rules;
 * rotary embedding: identity at position 0, lengths, composition, dependence
-  on the position difference only, and an independent implementation.
+  on the position difference only, and an independent implementation;
+* the whole-sequence (training) form: reductions to library attention (no
+  mask, the library's own causal mask, a prefix without mask), agreement with
+  the chunk-by-chunk oracle, the Q = 0 closed form and invariance to
+  everything outside each chunk's window.
 """
 from __future__ import annotations
 
@@ -360,7 +364,106 @@ def pin_rope(lib):
     assert np.abs(got - ref).max() <= 2e-5, "differs from the interleaved-pair rotary form"
 
 
+def _seq(C, n, H, d, P, seed):
+    rows = P + C * n
+    q = synth.tensor((C * n, H, d), synth.TAG_Q, seed, 0, 0, dtype="fp32").astype(np.float64)
+    k = synth.tensor((rows, H, d), synth.TAG_K, seed, 0, 0, dtype="fp32").astype(np.float64)
+    v = synth.tensor((rows, H, d), synth.TAG_V, seed, 0, 0, dtype="fp32").astype(np.float64)
+    return q, k, v
+
+
+def pin_sequence_reduces_to_library_attention(lib):
+    """Training form against torch SDPA (float64, CPU) where the block-causal
+    mask reduces to something the library does itself."""
+    import torch
+    import torch.nn.functional as F
+    H, d = 2, 16
+    scale = d ** -0.5
+    # W = 0, no prefix: every chunk attends to itself only, with no mask
+    C, n = 4, 6
+    q, k, v = _seq(C, n, H, d, 0, 31)
+    o, l = lib.attend_sequence(q, k, v, n, 0, 0, scale)
+    for c in range(C):
+        sl = slice(c * n, (c + 1) * n)
+        o_s, l_s = _sdpa(q[sl], k[sl], v[sl], np.ones((n, n), bool), scale)
+        np.testing.assert_allclose(o[sl], o_s, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l[c], l_s, rtol=0, atol=1e-12)
+    # n = 1 and a window covering everything: plain causal attention, with the
+    # library's own causal mask (is_causal)
+    T = 9
+    q, k, v = _seq(T, 1, H, d, 0, 32)
+    for W in (T - 1, T + 3):
+        o, l = lib.attend_sequence(q, k, v, 1, W, 0, scale)
+        tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x)).permute(1, 0, 2).contiguous()
+                      for x in (q, k, v))
+        o_s = F.scaled_dot_product_attention(tq, tk, tv, is_causal=True, scale=scale)
+        np.testing.assert_allclose(o, o_s.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+    # W = 0 with a prefix of P tokens: chunk c attends to [prefix; chunk c], no mask
+    C, n, P = 3, 5, 7
+    q, k, v = _seq(C, n, H, d, P, 33)
+    o, l = lib.attend_sequence(q, k, v, n, 0, P, scale)
+    for c in range(C):
+        rows = np.r_[0:P, P + c * n:P + (c + 1) * n]
+        sl = slice(c * n, (c + 1) * n)
+        o_s, l_s = _sdpa(q[sl], k[rows], v[rows], np.ones((n, len(rows)), bool), scale)
+        np.testing.assert_allclose(o[sl], o_s, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(l[c], l_s, rtol=0, atol=1e-12)
+
+
+def pin_sequence_matches_chunk_by_chunk(lib):
+    """The training form equals the streaming oracle run chunk by chunk (every
+    earlier chunk committed, the prefix as the reference chunk when P = n)."""
+    H, d, n, C = 2, 8, 5, 6
+    scale = 0.4
+    for P, W in ((0, 2), (n, 2), (n, 0), (0, 7)):
+        q, k, v = _seq(C, n, H, d, P, 34 + P + W)
+        o, l = lib.attend_sequence(q, k, v, n, W, P, scale)
+        ref = (k[:P], v[:P]) if P else None
+        hist = {}
+        for c in range(C):
+            cur = slice(P + c * n, P + (c + 1) * n)
+            sl = slice(c * n, (c + 1) * n)
+            o_c, l_c = lib.attend(q[sl], k[cur], v[cur], dict(hist), t=c, W=W, scale=scale,
+                                  ref=ref, use_ref=bool(P))
+            np.testing.assert_allclose(o[sl], o_c, rtol=0, atol=1e-12)
+            np.testing.assert_allclose(l[c], l_c, rtol=0, atol=1e-12)
+            hist[c] = (k[cur], v[cur])
+
+
+def pin_sequence_q_zero_and_invariance(lib):
+    """Q = 0: every visible key has weight 1/N, so LSE = ln N with
+    N = P + (min(c, W) + 1) n, and O = the mean of the visible V rows. And the
+    output of chunk c is bit-identical when every key row outside its window
+    (older chunks, later chunks) is replaced by NaN or infinities."""
+    H, d, n, C, P, W = 2, 8, 4, 6, 3, 2
+    q, k, v = _seq(C, n, H, d, P, 40)
+    z = np.zeros_like(q)
+    o, l = lib.attend_sequence(z, k, v, n, W, P, 1.0)
+    for c in range(C):
+        first = max(0, c - W)
+        rows = np.r_[0:P, P + first * n:P + (c + 1) * n]
+        N = P + (c - first + 1) * n
+        assert len(rows) == N
+        np.testing.assert_allclose(l[c], np.full((H, n), math.log(N)), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(o[c * n:(c + 1) * n],
+                                   np.broadcast_to(v[rows].mean(axis=0), (n, H, d)),
+                                   rtol=0, atol=1e-13)
+    o1, l1 = lib.attend_sequence(q, k, v, n, W, P, 0.5)
+    for c in range(C):
+        first = max(0, c - W)
+        k2, v2 = k.copy(), v.copy()
+        outside = np.ones(P + C * n, bool)
+        outside[:P] = False
+        outside[P + first * n:P + (c + 1) * n] = False
+        k2[outside] = np.nan
+        v2[outside] = np.inf
+        o2, l2 = lib.attend_sequence(q, k2, v2, n, W, P, 0.5)
+        sl = slice(c * n, (c + 1) * n)
+        assert np.array_equal(o2[sl], o1[sl]) and np.array_equal(l2[c], l1[c]), c
+
+
 ALL_PINS = [pin_hand_cases, pin_q_zero_closed_form, pin_one_hot_probe, pin_window_invariance,
             pin_split_merge, pin_merge_closed_forms, pin_constant_and_affine_v,
             pin_reduces_to_library_attention, pin_token_level_sliding_window, pin_large_logits,
-            pin_e4m3_codec, pin_rope]
+            pin_e4m3_codec, pin_rope, pin_sequence_reduces_to_library_attention,
+            pin_sequence_matches_chunk_by_chunk, pin_sequence_q_zero_and_invariance]

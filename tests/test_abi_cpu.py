@@ -340,3 +340,40 @@ def test_rope_entry_points_validate_before_launch():
             bca.bca_attend_rope(h, 0, spec, P, P, P, bca.BF16, 1e4, 0, P, 0, ws, wsb, 0)
         assert e.value.status == -3, (ws, wsb)
     bca.bca_cache_destroy(h)
+
+
+def test_sequence_entry_point_validates_before_launch():
+    P = FAKE
+    S = bca.bca_sequence_spec
+    good = dict(num_heads=2, head_dim=128, chunk_tokens=300, num_chunks=4, prefix_tokens=0,
+                history=1, num_segments=7, scale=0.1)
+    spec = S(**good)
+    need = bca.bca_attend_sequence_workspace_bytes(spec, bca.BF16)
+    # chunks c >= 1 see 600 keys in 7 segments: the largest plan's partials
+    # (2 heads x 2 query tiles x 7 pieces x 256 rows x (128 + 1) fp32)
+    assert need >= 2 * 2 * 7 * 256 * 129 * 4
+    assert bca.bca_attend_sequence_workspace_bytes(spec, bca.FP8_E4M3) == 0
+    for field, value in (("num_heads", 0), ("chunk_tokens", 0), ("num_chunks", 0),
+                         ("prefix_tokens", -1), ("history", -1), ("num_segments", 65),
+                         ("scale", float("nan"))):
+        bad = S(**{**good, field: value})
+        assert bca.bca_attend_sequence_workspace_bytes(bad, bca.BF16) == 0, field
+        with pytest.raises(BcaError) as e:
+            bca.bca_attend_sequence(bad, P, P, P, bca.BF16, P, 0, P, need, 0)
+        assert e.value.status == -1, field
+    for dt, hd in ((bca.FP8_E4M3, 128), (bca.BF16, 96)):
+        with pytest.raises(BcaError) as e:
+            bca.bca_attend_sequence(S(**{**good, "head_dim": hd}), P, P, P, dt, P, 0, P, need, 0)
+        assert e.value.status == -4, (dt, hd)
+    with pytest.raises(BcaError) as e:
+        bca.bca_attend_sequence(spec, 0, P, P, bca.BF16, P, 0, P, need, 0)
+    assert e.value.status == -1
+    for ws, wsb in ((0, 0), (P, need - 1), (P + 16, need)):
+        with pytest.raises(BcaError) as e:
+            bca.bca_attend_sequence(spec, P, P, P, bca.BF16, P, 0, ws, wsb, 0)
+        assert e.value.status == -3, (ws, wsb)
+    # K/V spans beyond the kernels' 32-bit offsets are refused
+    huge = S(**{**good, "chunk_tokens": 1 << 20, "num_chunks": 8})
+    with pytest.raises(BcaError) as e:
+        bca.bca_attend_sequence(huge, P, P, P, bca.BF16, P, 0, P, 1 << 40, 0)
+    assert e.value.status == -1

@@ -1,0 +1,142 @@
+"""Training-form block-causal attention over a whole sequence of chunks
+(bca_attend_sequence) against the CPU oracle (oracle.attend_sequence, fp64,
+explicit dense mask) on the same seeded, rounded inputs.
+
+Bars as for bca_attend: max |dO| and |dLSE| <= 1e-5 for fp32, 1e-2 for bf16
+with fp32 accumulation. Invisible key rows poisoned with NaN must leave the
+chunks that cannot see them bit-identical.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from bca_harness import TOL, assert_close, log, to_dev, to_np
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import attention_bca_attend_amd  # noqa: F401  (fails loudly when libbca.so is missing)
+    yield
+
+
+def seq_inputs(C, n, H, d, P, dtype, seed):
+    rows = P + C * n
+    q = synth.tensor((C * n, H, d), synth.TAG_Q, seed, 0, 0, dtype=dtype)
+    k = synth.tensor((rows, H, d), synth.TAG_K, seed, 0, 0, dtype=dtype)
+    v = synth.tensor((rows, H, d), synth.TAG_V, seed, 0, 0, dtype=dtype)
+    return q, k, v
+
+
+def run(q, k, v, n, W, P, G, dtype):
+    import attention_bca_attend_amd as bca
+    o, lse = bca.attend_sequence(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), n, W,
+                                 prefix_tokens=P, num_segments=G)
+    torch.cuda.synchronize()
+    return to_np(o), to_np(lse)
+
+
+CASES = [
+    # dtype, H, d, n, C, P, W, G
+    ("fp32", 2, 64, 16, 6, 0, 2, 0),
+    ("fp32", 2, 64, 16, 5, 16, 1, 2),
+    ("fp32", 3, 128, 37, 4, 5, 1, 3),
+    ("bf16", 2, 128, 100, 5, 0, 2, 0),
+    ("bf16", 3, 64, 17, 6, 9, 2, 3),
+    ("bf16", 2, 128, 405, 3, 405, 20, 4),
+    ("bf16", 2, 128, 64, 4, 0, 0, 1),
+    ("bf16", 2, 128, 300, 4, 0, 1, 7),
+    ("bf16", 1, 128, 1, 40, 0, 3, 0),
+]
+
+
+@pytest.mark.parametrize("dtype,H,d,n,C,P,W,G", CASES)
+def test_sequence_matches_oracle(dtype, H, d, n, C, P, W, G):
+    log(f"sequence {dtype} H {H} d {d} n {n} C {C} P {P} W {W} G {G}")
+    q, k, v = seq_inputs(C, n, H, d, P, dtype, 50 + n + C)
+    o, lse = run(q, k, v, n, W, P, G, dtype)
+    eo, el = oracle.attend_sequence(q, k, v, n, W, P, 1.0 / math.sqrt(d))
+    assert_close(o, lse, eo, el, TOL[dtype], f"sequence {dtype} n {n} C {C} P {P} W {W} G {G}")
+
+
+def test_sequence_invisible_rows_do_not_leak():
+    # NaN in chunk 0's keys and values: chunks c > W never see chunk 0, so their
+    # outputs must equal those of an unpoisoned run bit for bit
+    H, d, n, C, P, W = 2, 128, 100, 6, 0, 2
+    q, k, v = seq_inputs(C, n, H, d, P, "bf16", 61)
+    o1, l1 = run(q, k, v, n, W, P, 0, "bf16")
+    k2, v2 = k.copy(), v.copy()
+    k2[:n] = np.nan
+    v2[:n] = np.inf
+    o2, l2 = run(q, k2, v2, n, W, P, 0, "bf16")
+    for c in range(W + 1, C):
+        sl = slice(c * n, (c + 1) * n)
+        assert np.array_equal(o1[sl], o2[sl]) and np.array_equal(l1[c], l2[c]), c
+    # the poison did reach the chunks that see chunk 0 (what they then hold is
+    # not specified: the keys are not numbers)
+    assert not np.array_equal(o1[n:2 * n], o2[n:2 * n]), "chunk 1 sees chunk 0"
+    log("sequence: NaN in chunk 0 stays out of chunks 3..5")
+
+
+def test_sequence_equals_streaming_calls():
+    # the same clip streamed through a ring cache (bca_attend per chunk, the
+    # prefix as the reference chunk) gives the same result within bf16 bars
+    import attention_bca_attend_amd as bca
+    H, d, n, C, W = 2, 128, 96, 5, 2
+    q, k, v = seq_inputs(C, n, H, d, n, "bf16", 62)
+    o_seq, l_seq = run(q, k, v, n, W, n, 0, "bf16")
+    cache = bca.Cache(1, H, d, n, W, has_ref=True, kv_dtype="bf16")
+    cache.append_chunk(0, 0, to_dev(k[:n], "bf16"), to_dev(v[:n], "bf16"), is_ref=True)
+    for c in range(C):
+        cur = slice(n + c * n, n + (c + 1) * n)
+        sl = slice(c * n, (c + 1) * n)
+        spec = cache.spec(c, W, use_ref=True)
+        o, lse = cache.attend(0, to_dev(q[sl], "bf16"), to_dev(k[cur], "bf16"),
+                              to_dev(v[cur], "bf16"), spec)
+        assert_close(to_np(o), to_np(lse), o_seq[sl], l_seq[c], TOL["bf16"],
+                     f"streamed chunk {c} vs sequence")
+        cache.append_chunk(0, c, to_dev(k[cur], "bf16"), to_dev(v[cur], "bf16"))
+
+
+def test_sequence_full_size_wan_shape():
+    # 4 chunks of the Wan-shaped step (12 heads x 1536 tokens, window 2), the
+    # launch configuration the benchmark times; the oracle on heads 0 and 11
+    H, d, n, C, W = 12, 128, 1536, 4, 2
+    q, k, v = seq_inputs(C, n, H, d, 0, "bf16", 63)
+    o, lse = run(q, k, v, n, W, 0, 0, "bf16")
+    for h in (0, 11):
+        hs = slice(h, h + 1)
+        eo, el = oracle.attend_sequence(q[:, hs], k[:, hs], v[:, hs], n, W, 0, 1.0 / math.sqrt(d))
+        assert_close(o[:, hs], lse[:, hs], eo, el, TOL["bf16"], f"Wan-shaped sequence head {h}")
+
+
+def test_sequence_refused_calls():
+    import attention_bca_attend_amd as bca
+    q = torch.zeros((32, 2, 64), dtype=torch.bfloat16, device="cuda")
+    kv = torch.zeros((32, 2, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(bca.BcaError) as e:
+        bca.attend_sequence(q, kv, kv, 16, -1)
+    assert e.value.status == -1
+    with pytest.raises(bca.BcaError) as e:
+        bca.attend_sequence(q, kv, kv, 10, 1)  # 32 rows are not chunks of 10
+    assert e.value.status == -1
+    spec = bca.bca_sequence_spec(2, 64, 16, 2, 0, 1, 4, 0.125)
+    need = bca.bca_attend_sequence_workspace_bytes(spec, bca.BF16)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    with pytest.raises(bca.BcaError) as e:
+        bca.bca_attend_sequence(spec, q.data_ptr(), kv.data_ptr(), kv.data_ptr(), bca.BF16,
+                                o.data_ptr(), 0, ws.data_ptr(), need - 256)
+    assert e.value.status == -3
+    with pytest.raises(bca.BcaError) as e:
+        bca.bca_attend_sequence(spec, q.data_ptr(), kv.data_ptr(), kv.data_ptr(), bca.FP8_E4M3,
+                                o.data_ptr(), 0, ws.data_ptr(), need)
+    assert e.value.status == -4

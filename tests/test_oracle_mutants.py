@@ -42,6 +42,12 @@ MUTANTS = [
      "const double pos = (double)(pos0 + r + 1);"),
     ("rope_pairs_split_halves", "const double x0 = xi[2 * i], x1 = xi[2 * i + 1];",
      "const double x0 = xi[i], x1 = xi[i + d / 2];"),
+    ("sequence_window_off_by_one", "admit = (cj >= ci - W) && (cj <= ci);",
+     "admit = (cj >= ci - W - 1) && (cj <= ci);"),
+    ("sequence_next_chunk_visible", "admit = (cj >= ci - W) && (cj <= ci);",
+     "admit = (cj >= ci - W) && (cj <= ci + 1);"),
+    ("sequence_prefix_dropped", "        admit = 1;\n      } else {", "        admit = 0;\n      } else {"),
+    ("sequence_chunk_of_key_ignores_prefix", "int cj = (j - P) / n;", "int cj = j / n;"),
 ]
 
 
