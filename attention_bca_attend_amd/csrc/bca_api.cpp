@@ -183,6 +183,7 @@ size_t partial_bytes(int64_t units, int64_t jmax, int bm, int d) {
 // bca_attend_workspace_bytes. Validates everything except device pointers.
 bca_status make_plan(const bca_cache* c, int32_t layer, const bca_window_spec* s,
                      int32_t qkv_dtype, Plan& p) {
+  std::memset(&p, 0, sizeof p);
   if (!c) return fail(BCA_ERR_INVALID_ARG, "cache is NULL");
   if (!s) return fail(BCA_ERR_INVALID_ARG, "spec is NULL");
   if (!layer_ok(c, layer))
@@ -244,7 +245,7 @@ bca_status make_plan(const bca_cache* c, int32_t layer, const bca_window_spec* s
     r.vstart = i * n;
     r.len = n;
     r.phys = b * n;
-    r.pad_ = 0;
+    r.moves = 0;
     p.runs[p.nruns++] = r;
   }
   p.nk_cache = (p.nvis - 1) * n;
@@ -559,6 +560,7 @@ bca_status attend_impl(const bca_cache* c, int32_t layer, const bca_window_spec*
   a.scale = s->scale;
   a.scale_log2 = (float)((double)s->scale * 1.4426950408889634);
   a.xcd_remap = (p.wgs % 8 == 0) ? 1 : 0;
+  a.upc = p.units;  // one chunk
   a.nruns = p.nruns;
   for (int i = 0; i < p.nruns; ++i) a.runs[i] = p.runs[i];
   if (d.kv_dtype == BCA_FP8_E4M3)
@@ -598,10 +600,13 @@ bool seq_spec_ok(const bca_sequence_spec* s, int32_t qkv_dtype, std::string* why
   return true;
 }
 
-// Plan of chunk c. Its visible cache keys are the prefix and the window's
-// earlier chunks, rows of the token-major K/V: one run when the two touch
-// (c <= W), two otherwise.
-void seq_plan(const bca_sequence_spec* s, int32_t qkv_dtype, int cus, int64_t c, Plan& p) {
+// Plan of chunks c .. c + count - 1, one launch. Their visible cache keys are
+// the prefix and the window's earlier chunks, rows of the token-major K/V:
+// one run when the two touch (c <= W), two otherwise. Chunks share a launch
+// only when they see the same number of keys and the prefix (which stays) is
+// a run of its own: then only the window's run moves, n rows per chunk.
+void seq_plan(const bca_sequence_spec* s, int32_t qkv_dtype, int cus, int64_t c, int64_t count,
+              Plan& p) {
   std::memset(&p, 0, sizeof p);
   const int64_t n = s->chunk_tokens, P = s->prefix_tokens;
   const int64_t first = std::max<int64_t>(0, c - s->history);  // first chunk of the window
@@ -613,10 +618,11 @@ void seq_plan(const bca_sequence_spec* s, int32_t qkv_dtype, int cus, int64_t c,
     if (p.nruns > 0 && p.runs[0].phys + p.runs[0].len == phys)
       p.runs[0].len += (int32_t)hist;
     else
-      p.runs[p.nruns++] = Run{(int32_t)P, (int32_t)hist, (int32_t)phys, 0};
+      p.runs[p.nruns++] = Run{(int32_t)P, (int32_t)hist, (int32_t)phys, 1};
   }
   p.nk_cache = (int32_t)(P + hist);
   p.kern = qkv_dtype == BCA_F32 ? Kern::F32 : Kern::BF16;
+  p.seq = 1;
   const TileShape ts = tile_shape(p.kern);
   p.bm = ts.bm;
   p.bn = ts.bn;
@@ -624,21 +630,35 @@ void seq_plan(const bca_sequence_spec* s, int32_t qkv_dtype, int cus, int64_t c,
   p.cache_tiles = (p.nk_cache + p.bn - 1) / p.bn;
   p.kv_tiles = p.cache_tiles + (int32_t)((n + p.bn - 1) / p.bn);
   p.nk = p.nk_cache + (int32_t)n;
-  p.units = s->num_heads * p.q_tiles;
+  p.units = (int32_t)(count * s->num_heads * p.q_tiles);
   p.wgs = (int32_t)choose_wgs_on(cus, p.kern, p.units, p.kv_tiles, s->num_segments);
   p.jmax = pieces_bound(p.units, p.kv_tiles, p.wgs);
   p.merge = p.jmax > 1 ? 1 : 0;
   p.ws_bytes = p.merge ? partial_bytes(p.units, p.jmax, p.bm, s->head_dim) : 0;
 }
 
-// Chunks c >= W all have the plan of chunk W, so chunks 0 .. min(C-1, W) are
-// the only distinct ones; the workspace is the largest they need.
+// The launches of a sequence: (first chunk, chunk count). Chunks before the
+// steady window go one by one; from chunk W (W + 1 with a prefix, where chunk
+// W's window still touches the prefix) on every chunk sees the same number of
+// keys, and the bf16 kernel takes them all in one launch. The fp32 kernel
+// runs chunk by chunk.
+std::vector<std::pair<int64_t, int64_t>> seq_launches(const bca_sequence_spec* s,
+                                                      int32_t qkv_dtype) {
+  std::vector<std::pair<int64_t, int64_t>> out;
+  const int64_t C = s->num_chunks;
+  const int64_t steady = (int64_t)s->history + (s->prefix_tokens > 0 ? 1 : 0);
+  const int64_t single = qkv_dtype == BCA_BF16 ? std::min(C, steady) : C;
+  for (int64_t c = 0; c < single; ++c) out.push_back({c, 1});
+  if (single < C) out.push_back({single, C - single});
+  return out;
+}
+
+// The workspace is the largest any launch of the sequence needs.
 size_t seq_workspace(const bca_sequence_spec* s, int32_t qkv_dtype, int cus) {
   size_t ws = 0;
-  const int64_t distinct = std::min<int64_t>(s->num_chunks, (int64_t)s->history + 1);
-  for (int64_t c = 0; c < distinct; ++c) {
+  for (const auto& l : seq_launches(s, qkv_dtype)) {
     Plan p;
-    seq_plan(s, qkv_dtype, cus, c, p);
+    seq_plan(s, qkv_dtype, cus, l.first, l.second, p);
     ws = std::max(ws, p.ws_bytes);
   }
   return ws;
@@ -677,9 +697,10 @@ bca_status attend_sequence_impl(const bca_sequence_spec* s, const void* q, const
   const int64_t n = s->chunk_tokens, H = s->num_heads, D = s->head_dim, P = s->prefix_tokens;
   const size_t es = elem_size(qkv_dtype);
   const int64_t rows = P + (int64_t)s->num_chunks * n;
-  for (int64_t c = 0; c < s->num_chunks; ++c) {
+  for (const auto& l : seq_launches(s, qkv_dtype)) {
+    const int64_t c = l.first;
     Plan p;
-    seq_plan(s, qkv_dtype, cus, c, p);
+    seq_plan(s, qkv_dtype, cus, c, l.second, p);
     AttnArgs a;
     std::memset(&a, 0, sizeof a);
     const size_t chunk_off = (size_t)(c * n * H * D) * es;      // chunk c's rows of q and o
@@ -713,6 +734,11 @@ bca_status attend_sequence_impl(const bca_sequence_spec* s, const void* q, const
     a.scale = s->scale;
     a.scale_log2 = (float)((double)s->scale * 1.4426950408889634);
     a.xcd_remap = (p.wgs % 8 == 0) ? 1 : 0;
+    // chunks c .. c + count - 1: unit u belongs to chunk c + u / upc
+    a.upc = (int32_t)(H * p.q_tiles);
+    a.chunk_rows = (int32_t)n;
+    a.chunk_elems = n * H * D;
+    a.chunk_lse = H * n;
     a.nruns = p.nruns;
     for (int i = 0; i < p.nruns; ++i) a.runs[i] = p.runs[i];
     const int err = launch_attention(p, a, (int)D, (void*)stream);

@@ -26,7 +26,9 @@ struct Run {
   int32_t vstart;  // first key of the run in key order
   int32_t len;     // number of keys
   int32_t phys;    // first row in the head's cache matrix
-  int32_t pad_;
+  int32_t moves;   // 1: in a launch over several chunks of a sequence, the run
+                   // moves down by chunk_rows rows per chunk (the window);
+                   // 0: it stays (a memory prefix)
 };
 
 // Kernel families; each has fixed tile sizes.
@@ -49,6 +51,7 @@ inline TileShape tile_shape(Kern k) {
 // What one bca_attend call does, as resolved on the host.
 struct Plan {
   Kern kern;
+  int32_t seq;                      // 1: a bca_attend_sequence launch (token-major cache rows)
   int32_t nvis;                     // visible blocks, current included
   int32_t vis_block[kMaxBlocks];    // physical block (S = reference, -1 = current)
   int64_t vis_id[kMaxBlocks];
@@ -87,6 +90,14 @@ struct AttnArgs {
   float scale;        // softmax scale
   float scale_log2;   // scale * log2(e)
   int32_t xcd_remap;  // 1: spread work-group ids so each XCD gets a contiguous range
+  // One launch may cover several consecutive chunks of a sequence that share
+  // a plan: unit u is unit u % upc of chunk u / upc, whose q, k_cur, v_cur and
+  // o start chunk_elems elements further per chunk, lse chunk_lse floats, and
+  // whose moving runs start chunk_rows rows further. upc = units otherwise.
+  int32_t upc;
+  int32_t chunk_rows;
+  int64_t chunk_elems;
+  int64_t chunk_lse;
   int32_t nruns;
   Run runs[kMaxBlocks];
   float k_scale[kMaxHeadsFp8];  // fp8 cache: dequantisation scale per head
@@ -99,6 +110,9 @@ struct MergeArgs {
   void* o;
   float* lse;
   int32_t n, H, T, QT, units, P, jmax, bm;
+  int32_t upc;          // units per chunk (see AttnArgs)
+  int64_t chunk_elems;  // o elements per chunk
+  int64_t chunk_lse;    // lse floats per chunk
 };
 
 struct AppendArgs {

@@ -263,14 +263,16 @@ __device__ __forceinline__ void lds_load16(const char* base, int bytes, int off,
 // the next run.
 struct FetchRun {
   int ri, vstart, vend, phys;
+  int shift;  // rows a moving run is displaced by (the unit's chunk in a batched launch)
 };
 
-__device__ __forceinline__ FetchRun fetch_run_at(const AttnArgs& a, int ri) {
+__device__ __forceinline__ FetchRun fetch_run_at(const AttnArgs& a, int ri, int shift = 0) {
   FetchRun f;
   f.ri = ri;
+  f.shift = shift;
   f.vstart = a.runs[ri].vstart;
   f.vend = f.vstart + a.runs[ri].len;
-  f.phys = a.runs[ri].phys;
+  f.phys = a.runs[ri].phys + (a.runs[ri].moves ? shift : 0);
   return f;
 }
 
@@ -302,8 +304,10 @@ __device__ __forceinline__ FetchLane<D> fetch_lane(int wave, int lane, int rowb)
 
 // Requests K and V of key tile `tile` into one LDS stage; completion is
 // awaited with vmcnt before the work-group barrier that precedes its use.
-// Wave w's load q fills the 1 KB of the stage at (w IPW + q) KB.
-template <int D>
+// Wave w's load q fills the 1 KB of the stage at (w IPW + q) KB. SEQ: cache
+// rows are a token-major sequence (row pitch a.cache_row_elems); otherwise
+// the ring's head-major rows of d elements.
+template <int D, bool SEQ>
 __device__ __forceinline__ void bf16_fetch_tile(const AttnArgs& a, const HeadSrc& ks,
                                                 const HeadSrc& vs, int tile, FetchRun& fr,
                                                 const FetchLane<D>& fl, unsigned char* stage,
@@ -313,10 +317,11 @@ __device__ __forceinline__ void bf16_fetch_tile(const AttnArgs& a, const HeadSrc
   unsigned char* vdst = kdst + C::TILE_BYTES;
   if (tile < a.cache_tiles) {
     const int j0 = tile * C::BN;
-    while (j0 >= fr.vend && fr.ri + 1 < a.nruns) fr = fetch_run_at(a, fr.ri + 1);
+    while (j0 >= fr.vend && fr.ri + 1 < a.nruns) fr = fetch_run_at(a, fr.ri + 1, fr.shift);
+    const int rowb = SEQ ? a.cache_row_elems * 2 : C::ROWB;
     if (j0 + C::BN <= fr.vend) {
       // the whole tile lies in one run
-      const int base = (fr.phys + j0 - fr.vstart) * a.cache_row_elems * 2;
+      const int base = (fr.phys + j0 - fr.vstart) * rowb;
 #pragma unroll
       for (int q = 0; q < C::IPW; ++q) {
         const int off = base + fl.roff[q];
@@ -332,10 +337,11 @@ __device__ __forceinline__ void bf16_fetch_tile(const AttnArgs& a, const HeadSrc
         for (int rr = fr.ri; rr < a.nruns; ++rr) {
           const Run R = a.runs[rr];
           if (R.vstart >= j0 + C::BN) break;
-          if (j >= R.vstart && j < R.vstart + R.len) phys = R.phys + j - R.vstart;
+          if (j >= R.vstart && j < R.vstart + R.len)
+            phys = R.phys + (SEQ && R.moves ? fr.shift : 0) + j - R.vstart;
         }
-        const int koff = phys >= 0 ? phys * a.cache_row_elems * 2 + fl.kcol[q] : kOob;
-        const int voff = phys >= 0 ? phys * a.cache_row_elems * 2 + fl.vcol[q] : kOob;
+        const int koff = phys >= 0 ? phys * rowb + fl.kcol[q] : kOob;
+        const int voff = phys >= 0 ? phys * rowb + fl.vcol[q] : kOob;
         lds_load16(ks.cache, ks.cache_bytes, koff, kdst + q * 1024);
         lds_load16(vs.cache, vs.cache_bytes, voff, vdst + q * 1024);
       }
@@ -486,7 +492,10 @@ __device__ __forceinline__ void pp_softmax(PPState<D>& st, int lim, int hi, floa
   st.pf[3] = __builtin_convertvector(p1.hi, bf16x8_t);
 }
 
-template <int D>
+// SEQ: a launch of bca_attend_sequence (token-major cache rows, units of
+// several chunks); otherwise a ring-cache call, where that generality would
+// only cost scalar registers.
+template <int D, bool SEQ>
 __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
   using C = Bf16Cfg<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::NSTAGE * C::STAGE];
@@ -518,28 +527,32 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
       voff[db] = C::TILE_BYTES + (4 * hi + k) * C::ROWB + ((4 * (db ^ kx) + c0) << 4) +
                  (ai & 1) * 8;
   }
-  const FetchLane<D> fl = fetch_lane<D>(wave, lane, a.cache_row_elems * 2);
+  const FetchLane<D> fl = fetch_lane<D>(wave, lane, SEQ ? a.cache_row_elems * 2 : C::ROWB);
 
   while (it < it_end) {
     const int u = (int)(it / a.T);
     const int t0 = (int)(it - (int64_t)u * a.T);
     const int t1 = (int)((it_end - it) < (int64_t)(a.T - t0) ? t0 + (it_end - it) : a.T);
     const int nt = t1 - t0;
-    const int h = __builtin_amdgcn_readfirstlane(u / a.QT);
-    const int qt = u - h * a.QT;
+    const int ci = SEQ ? __builtin_amdgcn_readfirstlane(u / a.upc) : 0;  // chunk of the launch
+    const int ul = u - ci * a.upc;
+    const int h = __builtin_amdgcn_readfirstlane(ul / a.QT);
+    const int qt = ul - h * a.QT;
     const int q0 = qt * C::BM + (wave & 7) * 32;  // = 128 grp + 32 (wave % 4)
     const bool wave_rows = q0 < a.n;
-    const HeadSrc ksrc = head_src(a.kc, a.kcur, a, h, D, 2, 2);
-    const HeadSrc vsrc = head_src(a.vc, a.vcur, a, h, D, 2, 2);
+    const int64_t cel = SEQ ? (int64_t)ci * a.chunk_elems : 0;  // the chunk's first q/k/v/o element
+    const HeadSrc ksrc = head_src(a.kc, static_cast<const __bf16*>(a.kcur) + cel, a, h, D, 2, 2);
+    const HeadSrc vsrc = head_src(a.vc, static_cast<const __bf16*>(a.vcur) + cel, a, h, D, 2, 2);
     const float c = a.scale_log2;  // base-2 softmax scale
 
-    FetchRun fr = fetch_run_at(a, 0);
-    bf16_fetch_tile<D>(a, ksrc, vsrc, t0, fr, fl, smem, wave);
-    if (nt > 1) bf16_fetch_tile<D>(a, ksrc, vsrc, t0 + 1, fr, fl, smem + C::STAGE, wave);
+    FetchRun fr = fetch_run_at(a, 0, SEQ ? ci * a.chunk_rows : 0);
+    bf16_fetch_tile<D, SEQ>(a, ksrc, vsrc, t0, fr, fl, smem, wave);
+    if (nt > 1) bf16_fetch_tile<D, SEQ>(a, ksrc, vsrc, t0 + 1, fr, fl, smem + C::STAGE, wave);
 
     // Q^T fragments (B operand): lane holds query q0+l32, dims 16kk+8hi .. +7;
     // rows past the chunk read as zeros (out-of-range buffer offsets).
-    const HeadSrc qsrc = head_src(a.q, a.q, a, h, D, 2, 2);
+    const __bf16* qc = static_cast<const __bf16*>(a.q) + cel;
+    const HeadSrc qsrc = head_src(qc, qc, a, h, D, 2, 2);
     bf16x8_t qf[D / 16];
     {
       const int row = q0 + l32;
@@ -571,7 +584,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
     auto begin_phase = [&](int k) {
       const int r = k >> 1;
       if ((k & 1) == 0 && r + 2 < nt)
-        bf16_fetch_tile<D>(a, ksrc, vsrc, t0 + r + 2, fr, fl, smem + ((r + 2) & 3) * C::STAGE,
+        bf16_fetch_tile<D, SEQ>(a, ksrc, vsrc, t0 + r + 2, fr, fl, smem + ((r + 2) & 3) * C::STAGE,
                            wave);
     };
     auto end_phase = [&](int k) {
@@ -665,7 +678,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
       const bool whole = (t0 == 0) && (t1 == a.T);
       if (row < a.n) {
         if (whole) {
-          __bf16* op = static_cast<__bf16*>(a.o) + ((int64_t)row * a.H + h) * D;
+          __bf16* op = static_cast<__bf16*>(a.o) + cel + ((int64_t)row * a.H + h) * D;
 #pragma unroll
           for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -676,7 +689,8 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
               *reinterpret_cast<bf16x4_t*>(op + 32 * db + 8 * g + 4 * hi) =
                   __builtin_convertvector(v4, bf16x4_t);
             }
-          if (hi == 0 && a.lse) a.lse[(int64_t)h * a.n + row] = lse_val;
+          if (hi == 0 && a.lse)
+            a.lse[(SEQ ? ci * a.chunk_lse : 0) + (int64_t)h * a.n + row] = lse_val;
         } else {
           const int64_t jslot = (int64_t)w - first_wg_of((int64_t)u * a.T, I, a.P);
           const int64_t prow = ((int64_t)u * a.jmax + jslot) * C::BM + (wave & 7) * 32 + l32;
@@ -1333,7 +1347,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   const int rloc = rb * RPB + threadIdx.x / TPR;
   const int c4 = (threadIdx.x % TPR) * 4;
   if (rloc >= a.bm) return;
-  const int h = u / a.QT, qt = u - h * a.QT;
+  const int ci = u / a.upc, ul = u - ci * a.upc;  // chunk of a batched launch
+  const int h = ul / a.QT, qt = ul - h * a.QT;
   const int row = qt * a.bm + rloc;
   if (row >= a.n) return;
   float M = -INFINITY;
@@ -1353,13 +1368,14 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   }
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
   acc *= inv;
-  OutT* op = static_cast<OutT*>(a.o) + ((int64_t)row * a.H + h) * D + c4;
+  OutT* op = static_cast<OutT*>(a.o) + ci * a.chunk_elems + ((int64_t)row * a.H + h) * D + c4;
   if constexpr (sizeof(OutT) == 2) {
     *reinterpret_cast<bf16x4_t*>(op) = __builtin_convertvector(acc, bf16x4_t);
   } else {
     *reinterpret_cast<f32x4_t*>(op) = acc;
   }
-  if (c4 == 0 && a.lse) a.lse[(int64_t)h * a.n + row] = (M == -INFINITY) ? M : M + logf(wsum);
+  if (c4 == 0 && a.lse)
+    a.lse[ci * a.chunk_lse + (int64_t)h * a.n + row] = (M == -INFINITY) ? M : M + logf(wsum);
 }
 
 // ---------------------------------------------------------------------------
@@ -1591,7 +1607,10 @@ template <int D>
 int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
   switch (p.kern) {
     case Kern::BF16:
-      hipLaunchKernelGGL(attn_bf16_kernel<D>, dim3(p.wgs), dim3(512), 0, s, a);
+      if (p.seq)
+        hipLaunchKernelGGL((attn_bf16_kernel<D, true>), dim3(p.wgs), dim3(512), 0, s, a);
+      else
+        hipLaunchKernelGGL((attn_bf16_kernel<D, false>), dim3(p.wgs), dim3(512), 0, s, a);
       break;
     case Kern::FP8:
       if constexpr (D == 128) {
@@ -1639,6 +1658,9 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
     m.P = a.P;
     m.jmax = a.jmax;
     m.bm = p.bm;
+    m.upc = a.upc;
+    m.chunk_elems = a.chunk_elems;
+    m.chunk_lse = a.chunk_lse;
     constexpr int RPB = 256 / (D / 4);
     const int blocks = a.units * ((p.bm + RPB - 1) / RPB);
     if (p.kern == Kern::F32)

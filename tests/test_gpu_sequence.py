@@ -54,6 +54,11 @@ CASES = [
     ("bf16", 2, 128, 64, 4, 0, 0, 1),
     ("bf16", 2, 128, 300, 4, 0, 1, 7),
     ("bf16", 1, 128, 1, 40, 0, 3, 0),
+    # steady chunks share one launch: a prefix that stays while the window moves
+    ("bf16", 2, 128, 256, 6, 100, 0, 0),
+    # 39 steady chunks x 8 heads = 312 units, more than the chip holds: ranges
+    # of key tiles cross unit (and chunk) boundaries
+    ("bf16", 8, 64, 256, 40, 0, 1, 0),
 ]
 
 
