@@ -22,7 +22,8 @@ __all__ = [
     "bca_append_chunk_rope", "bca_attend_rope_workspace_bytes", "bca_attend_rope",
     "bca_cache_slot_chunk", "bca_cache_set_slot_chunk", "bca_attend_plan", "bca_status_string",
     "bca_last_error", "bca_sequence_spec", "bca_attend_sequence_workspace_bytes",
-    "bca_attend_sequence", "attend_sequence", "Cache", "LIB_PATH", "load_library",
+    "bca_attend_sequence", "attend_sequence", "bca_append_chunk_dev",
+    "bca_chunk_counter_advance", "bca_attend_replayable", "Cache", "LIB_PATH", "load_library",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbca.so")
@@ -117,6 +118,12 @@ def load_library(path: str = LIB_PATH):
     lib.bca_attend_sequence_workspace_bytes.restype = SZ
     lib.bca_attend_sequence.argtypes = [seq_p, P, P, P, I32, P, P, P, SZ, P]
     lib.bca_attend_sequence.restype = I32
+    lib.bca_append_chunk_dev.argtypes = [P, I32, P, P, P, I32, P]
+    lib.bca_append_chunk_dev.restype = I32
+    lib.bca_chunk_counter_advance.argtypes = [P, P]
+    lib.bca_chunk_counter_advance.restype = I32
+    lib.bca_attend_replayable.argtypes = [P, I32, spec_p, ctypes.POINTER(I32)]
+    lib.bca_attend_replayable.restype = I32
     lib.bca_cache_slot_chunk.argtypes = [P, I32, I32, ctypes.POINTER(I64)]
     lib.bca_cache_slot_chunk.restype = I32
     lib.bca_cache_set_slot_chunk.argtypes = [P, I32, I32, I64]
@@ -277,6 +284,24 @@ def attend_sequence(q, k, v, chunk_tokens: int, history: int, prefix_tokens: int
     return o, lse
 
 
+def bca_append_chunk_dev(handle: int, layer: int, d_chunk_id: int, k: int, v: int,
+                         in_dtype: int, stream: int = 0) -> None:
+    _check(_lib.bca_append_chunk_dev(ctypes.c_void_p(handle), layer, ctypes.c_void_p(d_chunk_id),
+                                     ctypes.c_void_p(k), ctypes.c_void_p(v), in_dtype,
+                                     ctypes.c_void_p(stream)))
+
+
+def bca_chunk_counter_advance(d_chunk_id: int, stream: int = 0) -> None:
+    _check(_lib.bca_chunk_counter_advance(ctypes.c_void_p(d_chunk_id), ctypes.c_void_p(stream)))
+
+
+def bca_attend_replayable(handle: int, layer: int, spec) -> bool:
+    out = ctypes.c_int32()
+    _check(_lib.bca_attend_replayable(ctypes.c_void_p(handle), layer, ctypes.byref(_spec(spec)),
+                                      ctypes.byref(out)))
+    return bool(out.value)
+
+
 def bca_cache_slot_chunk(handle: int, layer: int, slot: int) -> int:
     out = ctypes.c_int64()
     _check(_lib.bca_cache_slot_chunk(ctypes.c_void_p(handle), layer, slot, ctypes.byref(out)))
@@ -407,6 +432,24 @@ class Cache:
 
     def plan(self, layer: int, spec) -> dict:
         return bca_attend_plan(self.handle, layer, spec)
+
+    def replayable(self, layer: int, spec) -> bool:
+        return bca_attend_replayable(self.handle, layer, spec)
+
+    def append_chunk_dev(self, layer: int, d_chunk_id, k, v, stream=None):
+        """bca_append_chunk_dev: the chunk id is read from the int64 device tensor
+        d_chunk_id when the kernels run (for replayed graphs)."""
+        import torch
+        self._check_qkv(k, v)
+        if d_chunk_id.dtype != torch.int64 or not d_chunk_id.is_cuda:
+            raise BcaError(-1, "d_chunk_id must be an int64 device tensor")
+        bca_append_chunk_dev(self.handle, layer, d_chunk_id.data_ptr(), k.data_ptr(),
+                             v.data_ptr(), _DT[self.qkv_dtype], self._stream(stream))
+
+    @staticmethod
+    def advance_counter(d_chunk_id, stream=None):
+        """bca_chunk_counter_advance on an int64 device tensor."""
+        bca_chunk_counter_advance(d_chunk_id.data_ptr(), Cache._stream(stream))
 
     def attend(self, layer: int, q, k_cur, v_cur, spec, out=None, lse=None, workspace=None,
                stream=None, rope=None):

@@ -429,6 +429,83 @@ bca_status append_impl(bca_cache* c, int32_t layer, int64_t chunk_id, int32_t is
 
 extern "C" {
 
+bca_status bca_append_chunk_dev(bca_cache* c, int32_t layer, const int64_t* d_chunk_id,
+                                const void* k, const void* v, int32_t in_dtype,
+                                bca_stream_t stream) {
+  if (!c) return fail(BCA_ERR_INVALID_ARG, "cache is NULL");
+  if (!layer_ok(c, layer))
+    return fail(BCA_ERR_INVALID_ARG, "layer %d out of range [0, %d)", layer, c->d.num_layers);
+  if (!d_chunk_id || !aligned(d_chunk_id, 8))
+    return fail(BCA_ERR_INVALID_ARG, "d_chunk_id must be a non-NULL, 8-byte aligned pointer");
+  if (!k || !v) return fail(BCA_ERR_INVALID_ARG, "k or v is NULL");
+  if (!aligned(k, 16) || !aligned(v, 16))
+    return fail(BCA_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+  if (elem_size(in_dtype) == 0) return fail(BCA_ERR_INVALID_ARG, "in_dtype is not a bca_dtype");
+  const int32_t kv = c->d.kv_dtype;
+  bool ok = (in_dtype == BCA_F32 && kv == BCA_F32) || (in_dtype == BCA_BF16 && kv == BCA_BF16) ||
+            (in_dtype == BCA_BF16 && kv == BCA_FP8_E4M3);
+  if (!ok)
+    return fail(BCA_ERR_UNSUPPORTED, "cannot append dtype %d into a cache of dtype %d",
+                in_dtype, kv);
+  const bca_cache_desc& d = c->d;
+  const size_t block_elems = (size_t)d.chunk_tokens * d.head_dim;
+  char* layer_k = c->mem + 2 * (size_t)layer * half_layer_bytes(d);
+  AppendArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.k = k;
+  a.v = v;
+  a.kdst = layer_k;  // block 0; the kernels add (id mod S) blocks
+  a.vdst = layer_k + half_layer_bytes(d);
+  a.head_stride_elems = (int64_t)(d.ring_slots + d.has_ref) * (int64_t)block_elems;
+  a.n = d.chunk_tokens;
+  a.H = d.num_heads;
+  a.dev_chunk = d_chunk_id;
+  a.slots = d.ring_slots;
+  a.block_elems = (int64_t)block_elems;
+  if (kv == BCA_FP8_E4M3)
+    for (int h = 0; h < d.num_heads; ++h) {
+      a.k_scale[h] = c->k_scale[(size_t)layer * d.num_heads + h];
+      a.v_scale[h] = c->v_scale[(size_t)layer * d.num_heads + h];
+    }
+  int err = launch_append((bca_dtype)in_dtype, (bca_dtype)kv, d.head_dim, a, (void*)stream);
+  if (err != 0) return fail(BCA_ERR_HIP, "append kernel launch failed (hip error %d)", err);
+  g_err.clear();
+  return BCA_OK;
+}
+
+bca_status bca_chunk_counter_advance(int64_t* d_chunk_id, bca_stream_t stream) {
+  if (!d_chunk_id || !aligned(d_chunk_id, 8))
+    return fail(BCA_ERR_INVALID_ARG, "d_chunk_id must be a non-NULL, 8-byte aligned pointer");
+  int err = launch_counter_advance(d_chunk_id, (void*)stream);
+  if (err != 0) return fail(BCA_ERR_HIP, "counter kernel launch failed (hip error %d)", err);
+  g_err.clear();
+  return BCA_OK;
+}
+
+bca_status bca_attend_replayable(const bca_cache* c, int32_t layer, const bca_window_spec* s,
+                                 int32_t* replayable) {
+  if (!replayable) return fail(BCA_ERR_INVALID_ARG, "replayable is NULL");
+  *replayable = 0;
+  Plan p;
+  bca_status st = make_plan(c, layer, s, c ? (c->d.kv_dtype == BCA_F32 ? BCA_F32 : BCA_BF16)
+                                            : BCA_BF16, p);
+  if (st != BCA_OK) return st;
+  // Every ring slot holds one of the chunks t-S .. t-1 (so all S are visible
+  // and consecutive appends keep them so), the window covers the whole ring,
+  // and a requested reference is present: then the plan of chunk t is the
+  // plan of every later chunk of a consecutive stream.
+  const int S = c->d.ring_slots;
+  const int64_t t = s->q_chunk_id;
+  bool ok = s->history >= S && (!s->use_ref || c->ref_valid[layer]);
+  for (int sl = 0; ok && sl < S; ++sl) {
+    const int64_t id = c->slot[(size_t)layer * S + sl];
+    ok = id >= t - S && id <= t - 1;
+  }
+  *replayable = ok ? 1 : 0;
+  g_err.clear();
+  return BCA_OK;
+}
+
 bca_status bca_append_chunk(bca_cache* c, int32_t layer, int64_t chunk_id, int32_t is_ref,
                             const void* k, const void* v, int32_t in_dtype,
                             bca_stream_t stream) {

@@ -124,6 +124,13 @@ struct AppendArgs {
   int32_t n, H;
   float k_scale[kMaxHeadsFp8];  // fp8 cache only
   float v_scale[kMaxHeadsFp8];
+  // Device-side chunk id (graph replay): when set, kdst/vdst are the layer's
+  // block 0 and the kernels read the id when they run and write block
+  // (id mod slots), block_elems elements per block; a negative id writes
+  // nothing.
+  const int64_t* dev_chunk;
+  int32_t slots;
+  int64_t block_elems;
   int32_t rope;            // 1: rotate K (rotary embedding) before it is stored
   double rope_log2_base;   // log2 of the rotary base
   int64_t rope_pos0;       // position of the chunk's token 0
@@ -143,6 +150,7 @@ int launch_attention(const Plan& plan, const AttnArgs& args, int head_dim, void*
 int launch_append(bca_dtype in, bca_dtype kv, int head_dim, const AppendArgs& args,
                   void* stream);
 int launch_rope_stage(bca_dtype dt, int head_dim, const RopeStageArgs& args, void* stream);
+int launch_counter_advance(int64_t* counter, void* stream);
 // Compute units of the current device, or 0 when it cannot be queried.
 int device_compute_units();
 

@@ -11,6 +11,7 @@
 //   rope_stage_kernel  rotary embedding of the current chunk's Q and K into
 //                      staging copies
 //   append_rope_k_kernel  the rotated K of an append (copy or e4m3)
+//   counter_advance_kernel  the device-side chunk counter of a replayed step
 //
 // What is computed follows "WanToFight" (xllm-io review), section 3 model
 // components table (block-causal attention: bidirectional in the chunk, causal
@@ -1478,6 +1479,16 @@ __device__ __forceinline__ void store8(char* p, int es, const float (&x)[8]) {
   }
 }
 
+// Element offset of the destination block of an append: 0 when the host
+// resolved the block, (id mod slots) * block_elems for a device-side chunk
+// id, -1 (write nothing) for a negative one.
+__device__ __forceinline__ int64_t append_block_offset(const AppendArgs& a) {
+  if (!a.dev_chunk) return 0;
+  const int64_t id = *a.dev_chunk;
+  if (id < 0) return -1;
+  return (id % a.slots) * a.block_elems;
+}
+
 // Fused K/V append: [n][H][d] -> the block's [H][n][d] rows (stride (S+R)*n*d
 // between heads), converting to the cache dtype. blockIdx.y + kv0 selects K (0)
 // or V (1). Each thread moves 8 elements. A rotated K goes through
@@ -1493,9 +1504,11 @@ __global__ __launch_bounds__(256) void append_copy_kernel(const AppendArgs a, in
   const int h = (int)(rh % a.H);
   const int r = (int)(rh / a.H);
   const bool isv = blockIdx.y + kv0 == 1;
+  const int64_t blk = append_block_offset(a);
+  if (blk < 0) return;
   const char* src = static_cast<const char*>(isv ? a.v : a.k) + (rh * D + g * 8) * es;
   char* dst = static_cast<char*>(isv ? a.vdst : a.kdst) +
-              ((int64_t)h * a.head_stride_elems + (int64_t)r * D + g * 8) * es;
+              (blk + (int64_t)h * a.head_stride_elems + (int64_t)r * D + g * 8) * es;
   if (es == 2) {
     *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
   } else {
@@ -1535,13 +1548,15 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(const AppendArgs a, int
   const int h = (int)(rh % a.H);
   const int r = (int)(rh / a.H);
   const bool isv = blockIdx.y + kv0 == 1;
+  const int64_t blk = append_block_offset(a);
+  if (blk < 0) return;
   const float s = isv ? a.v_scale[h] : a.k_scale[h];
   float y[8];
   load8(reinterpret_cast<const char*>(static_cast<const __bf16*>(isv ? a.v : a.k) + rh * D +
                                       g * 8),
         2, y);
   unsigned char* dst = static_cast<unsigned char*>(isv ? a.vdst : a.kdst) +
-                       ((int64_t)h * a.head_stride_elems + (int64_t)r * D + g * 8);
+                       (blk + (int64_t)h * a.head_stride_elems + (int64_t)r * D + g * 8);
   *reinterpret_cast<uint2*>(dst) = e4m3x8(y, s);
 }
 
@@ -1723,6 +1738,18 @@ int launch_append(bca_dtype in, bca_dtype kv, int head_dim, const AppendArgs& a,
         hipLaunchKernelGGL((append_rope_k_kernel<128, false>), rgrid, dim3(128), 0, s, a, es);
     }
   }
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? 0 : (int)e;
+}
+
+// The device-side chunk counter of a replayed chunk step: one thread adds 1.
+__global__ void counter_advance_kernel(int64_t* counter) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) *counter += 1;
+}
+
+int launch_counter_advance(int64_t* counter, void* stream) {
+  hipLaunchKernelGGL(counter_advance_kernel, dim3(1), dim3(64), 0,
+                     static_cast<hipStream_t>(stream), counter);
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? 0 : (int)e;
 }

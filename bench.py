@@ -1,6 +1,6 @@
 """Benchmark of block-causal ring-KV chunk attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1|2|3|4|5|6]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1|...|7]
 
 One step is one chunk of the chunk-wise autoregressive loop: for every denoise
 step and every layer one bca_attend (the chunk's queries over the current
@@ -24,6 +24,8 @@ Workloads (synthetic inputs, random values of the stated shapes):
   6  training form of workload 1: a clip of 8 chunks (12 heads, d 128, 1536
      tokens each, window of the current + previous 2 chunks) attended at once
      with bca_attend_sequence, 30 layers per step, each with its own Q/K/V.
+  7  workload 3 with the chunk step captured once in a HIP graph and replayed
+     for every chunk (device-side chunk id read by the appends).
 
 Prints one JSON line. `value` is algorithmic attention TFLOP/s over the whole
 step (4*H*n*N_k*d per chunk-layer, appends included in the time), from a timed
@@ -60,6 +62,8 @@ CONFIGS = {
             L=30, steps_per_chunk=1, kv="fp8"),
     5: dict(workload="wantofight_bf16_rope_chunk", H=12, d=128, n=1536, S=2, W=2, R=0, G=0,
             L=30, steps_per_chunk=4, kv="bf16", rope=10000.0),
+    7: dict(workload="wantofight_bf16_stream64_graph", H=12, d=128, n=1536, S=2, W=2, R=0, G=0,
+            L=30, steps_per_chunk=4, kv="bf16", graph=True),
     6: dict(workload="wantofight_bf16_sequence8", H=12, d=128, n=1536, C=8, W=2, P=0, G=0, L=30,
             kv="bf16", sequence=True),
 }
@@ -164,6 +168,115 @@ def cpu_baseline_sequence(cfg, q, k, v):
             "kind": "oracle",
             "sample": f"layer 0 whole sequence, {hs} of {H} heads x {C} chunks of {n} tokens "
                       f"(fp64 dense-mask oracle, {dt:.1f} s)"}
+
+
+def main_graph(args, cfg):
+    """Workload 7: the chunk step (every attend, one device-id append per layer,
+    the counter advance) captured once and replayed per chunk."""
+    import torch
+
+    import attention_bca_attend_amd as bca
+
+    H, d, n, S, W, G, L = (cfg[k] for k in ("H", "d", "n", "S", "W", "G", "L"))
+    spc = cfg["steps_per_chunk"]
+    steps = args.steps if args.steps is not None else 64
+    torch.cuda.set_device(0)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20261202)
+    log(f"config {args.config}: {cfg}")
+    cache = bca.Cache(L, H, d, n, S, kv_dtype="bf16")
+    Q = [gen((n, H, d), g) for _ in range(L)]
+    Kc = [gen((n, H, d), g) for _ in range(L)]
+    Vc = [gen((n, H, d), g) for _ in range(L)]
+    O = torch.empty((n, H, d), dtype=torch.bfloat16, device="cuda")
+    LSE = torch.empty((H, n), dtype=torch.float32, device="cuda")
+    for l in range(L):
+        for c in range(S):
+            cache.append_chunk(l, c, gen((n, H, d), g), gen((n, H, d), g))
+    t_chunk = S
+    spec = cache.spec(t_chunk, W, num_segments=G)
+    ws = cache.workspace(spec)
+    plan = cache.plan(0, spec)
+    nk = plan["visible_keys"]
+    flop_cl = 4.0 * H * n * nk * d
+    for l in range(L):
+        if not cache.replayable(l, spec):
+            raise SystemExit("chunk step is not replayable for this workload")
+    d_chunk = torch.full((1,), t_chunk, dtype=torch.int64, device="cuda")
+    # one eager step first (loads the code objects, and it is chunk S)
+    for _ in range(spc):
+        for l in range(L):
+            cache.attend(l, Q[l], Kc[l], Vc[l], spec, out=O, lse=LSE, workspace=ws)
+    for l in range(L):
+        cache.append_chunk_dev(l, d_chunk, Kc[l], Vc[l])
+    bca.Cache.advance_counter(d_chunk)
+    torch.cuda.synchronize()
+    for l in range(L):
+        cache.set_slot_chunk(l, t_chunk % S, t_chunk)
+    t_chunk += 1
+    spec = cache.spec(t_chunk, W, num_segments=G)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(spc):
+            for l in range(L):
+                cache.attend(l, Q[l], Kc[l], Vc[l], spec, out=O, lse=LSE, workspace=ws)
+        for l in range(L):
+            cache.append_chunk_dev(l, d_chunk, Kc[l], Vc[l])
+        bca.Cache.advance_counter(d_chunk)
+    torch.cuda.synchronize()
+
+    def replay():
+        nonlocal t_chunk
+        graph.replay()
+        for l in range(L):
+            cache.set_slot_chunk(l, t_chunk % S, t_chunk)
+        t_chunk += 1
+
+    for _ in range(args.warmup):
+        replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    per_chunk = []
+    start.record()
+    for _ in range(steps):
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c0.record()
+        replay()
+        c1.record()
+        per_chunk.append((c0, c1))
+    end.record()
+    torch.cuda.synchronize()
+    assert int(d_chunk.item()) == t_chunk, "device chunk counter out of step"
+    ms_step = start.elapsed_time(end) / steps
+    chunk_ms = [a.elapsed_time(b) for a, b in per_chunk]
+    n_attend = spc * L
+    tflops = n_attend * flop_cl / (ms_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS["bf16"]
+    log(f"{steps} replayed chunks: {ms_step:.3f} ms per chunk, {tflops:.1f} TFLOP/s")
+    result = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg["workload"], "heads": H, "head_dim": d, "chunk_tokens": n,
+                   "visible_keys": nk, "ring_slots": S, "history": W, "reference": False,
+                   "segments": G if G else "auto", "layers": L,
+                   "denoise_steps_per_chunk": spc, "batch": 1, "graph": True},
+        "us_per_chunk_layer": round(ms_step * 1e3 / n_attend, 3),
+        "pct_mfma_peak": round(100.0 * tflops / peak, 2),
+        "chunk_ms_min_max": [round(min(chunk_ms), 4), round(max(chunk_ms), 4)],
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                     "traffic": measured_traffic(cfg["workload"]),
+                     "kernel": "replayed chunk step (attends with appends, whole-step time)"},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline(cache, dict(cfg, R=0), Q[0], Kc[0], Vc[0],
+                                              t_chunk)
+    print(json.dumps(result), flush=True)
 
 
 def main_sequence(args, cfg):
@@ -317,6 +430,9 @@ def main():
         cfg["L"] = args.layers
     if cfg.get("sequence"):
         main_sequence(args, cfg)
+        return
+    if cfg.get("graph"):
+        main_graph(args, cfg)
         return
     steps = args.steps if args.steps is not None else (64 if args.config == 3 else 5)
     H, d, n, S, W, R, G, L = (cfg[k] for k in ("H", "d", "n", "S", "W", "R", "G", "L"))

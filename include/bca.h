@@ -258,6 +258,45 @@ bca_status bca_attend_sequence(const bca_sequence_spec* spec, const void* q, con
                                const void* v, int32_t qkv_dtype, void* o, float* lse,
                                void* workspace, size_t workspace_bytes, bca_stream_t stream);
 
+/* Replaying the chunk loop from a captured HIP graph. "Matrix-Game 4.0"
+ * summary, prerequisite "FP8 quantisation and CUDA Graph" and experimental
+ * results: the per-chunk launches are recorded once and replayed. A graph
+ * freezes every launch argument, so what changes from chunk to chunk must
+ * live in device memory: here the chunk id, in one int64 the caller owns.
+ *
+ * bca_append_chunk_dev: bca_append_chunk (not the reference block) whose
+ * chunk id is read from *d_chunk_id when the kernels run, writing ring slot
+ * (id mod S); a negative id writes nothing. The host cannot see that id, so
+ * this call neither checks the order of ids nor updates the host slot table:
+ * after the work has run, the caller records it with
+ * bca_cache_set_slot_chunk(layer, id mod S, id), as it does after a replay.
+ * No rotary form. Errors as for bca_append_chunk, plus BCA_ERR_INVALID_ARG for
+ * a NULL or misaligned (8 bytes) d_chunk_id.
+ *
+ * bca_chunk_counter_advance: *d_chunk_id += 1 in stream order (one thread).
+ *
+ * bca_attend_replayable: sets *replayable to 1 when a bca_attend of this spec
+ * captured now stays right for every later chunk of a stream that appends
+ * consecutive ids: the window covers the whole ring (history >= S), every
+ * ring slot holds one of the chunks t-S .. t-1, and a requested reference is
+ * present. The plan (visible blocks, tiles, work groups) is then the same
+ * for every such chunk, and the captured launch reads whatever the slots hold
+ * when it runs. Otherwise 0 (a smaller window sees different slots from
+ * chunk to chunk). Errors as for bca_attend's checks of cache, layer and spec.
+ *
+ * bca_attend and bca_append_chunk_dev enqueue kernels only: no allocation,
+ * no memset, no synchronisation, so they can be captured. One captured chunk
+ * step is: the attends of every layer and denoise step, one
+ * bca_append_chunk_dev per layer, one bca_chunk_counter_advance. */
+bca_status bca_append_chunk_dev(bca_cache* cache, int32_t layer, const int64_t* d_chunk_id,
+                                const void* k, const void* v, int32_t in_dtype,
+                                bca_stream_t stream);
+
+bca_status bca_chunk_counter_advance(int64_t* d_chunk_id, bca_stream_t stream);
+
+bca_status bca_attend_replayable(const bca_cache* cache, int32_t layer,
+                                 const bca_window_spec* spec, int32_t* replayable);
+
 /* Host-side slot table query: chunk id held by ring slot `slot` (0 <= slot < S)
  * of `layer`, -1 if empty. slot == S (with has_ref) reports the reference block
  * (its recorded id, or -1). */

@@ -377,3 +377,42 @@ def test_sequence_entry_point_validates_before_launch():
     with pytest.raises(BcaError) as e:
         bca.bca_attend_sequence(huge, P, P, P, bca.BF16, P, 0, P, 1 << 40, 0)
     assert e.value.status == -1
+
+
+def test_replay_entry_points_validate_before_launch():
+    h, _ = make(S=2, R=0, dt=bca.BF16, d=128, H=2, n=16)
+    P = FAKE
+    for ptr in (0, P + 4):
+        with pytest.raises(BcaError) as e:
+            bca.bca_append_chunk_dev(h, 0, ptr, P, P, bca.BF16, 0)
+        assert e.value.status == -1
+        with pytest.raises(BcaError) as e:
+            bca.bca_chunk_counter_advance(ptr, 0)
+        assert e.value.status == -1
+    with pytest.raises(BcaError) as e:
+        bca.bca_append_chunk_dev(h, 2, P, P, P, bca.BF16, 0)  # layer out of range
+    assert e.value.status == -1
+    with pytest.raises(BcaError) as e:
+        bca.bca_append_chunk_dev(h, 0, P, P, P, bca.F32, 0)
+    assert e.value.status == -4
+    bca.bca_cache_destroy(h)
+
+
+def test_attend_replayable_rule():
+    # host-only: slot contents declared through the restore hook
+    h, _ = make(S=2, R=1, dt=bca.BF16, d=128, H=2, n=16)
+    spec = lambda t, W, ref=0: bca.bca_window_spec(t, W, ref, 0, 0.1)  # noqa: E731
+    assert not bca.bca_attend_replayable(h, 0, spec(2, 2))  # empty ring
+    bca.bca_cache_set_slot_chunk(h, 0, 0, 0)
+    assert not bca.bca_attend_replayable(h, 0, spec(2, 2))  # slot 1 still empty
+    bca.bca_cache_set_slot_chunk(h, 0, 1, 1)
+    assert bca.bca_attend_replayable(h, 0, spec(2, 2))      # chunks 0, 1 for t = 2
+    assert not bca.bca_attend_replayable(h, 0, spec(2, 1))  # window smaller than the ring
+    assert not bca.bca_attend_replayable(h, 0, spec(3, 2))  # chunk 0 is outside t = 3's window
+    assert not bca.bca_attend_replayable(h, 0, spec(2, 2, ref=1))  # no reference appended
+    bca.bca_cache_set_slot_chunk(h, 0, 2, 0)                # declare the reference
+    assert bca.bca_attend_replayable(h, 0, spec(2, 2, ref=1))
+    assert not bca.bca_attend_replayable(h, 1, spec(2, 2))  # layer 1 is empty
+    with pytest.raises(BcaError):
+        bca.bca_attend_replayable(h, 0, spec(2, 3))          # history > ring slots
+    bca.bca_cache_destroy(h)

@@ -1,0 +1,140 @@
+"""The chunk loop captured once in a HIP graph and replayed chunk after chunk
+(bca_append_chunk_dev with a device-side chunk id, bca_chunk_counter_advance,
+captured bca_attend calls) against the same loop run eagerly on a second
+cache with the same contents.
+
+Both run the same kernels with the same plans on the same inputs, so every
+replay must give bit-identical outputs, LSE and cache bytes; the eager loop is
+itself held to the oracle by the parity tests. Each replay is separated from
+the next by eager work (new inputs copied in, the eager loop, comparisons)
+and a synchronisation.
+"""
+import numpy as np
+import pytest
+
+import synth
+from bca_harness import log, to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import attention_bca_attend_amd  # noqa: F401  (fails loudly when libbca.so is missing)
+    yield
+
+
+def _chunk(n, H, d, layer, t, fp8):
+    q, k, v = synth.qkv(n, H, d, 70 + layer, t, 0, dtype="bf16",
+                        outlier_frac=0.01 if fp8 else 0.0)
+    return to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+
+
+CASES = [
+    # kv dtype, L, H, d, n, S (= W), reference, segments
+    ("bf16", 2, 2, 128, 100, 2, False, 0),
+    ("bf16", 2, 3, 64, 64, 3, True, 2),
+    ("fp8", 2, 2, 128, 96, 2, True, 0),
+]
+
+
+@pytest.mark.parametrize("kv,L,H,d,n,S,R,G", CASES)
+def test_replayed_chunk_step_equals_eager(kv, L, H, d, n, S, R, G):
+    import attention_bca_attend_amd as bca
+    fp8 = kv == "fp8"
+    log(f"graph replay {kv} L {L} H {H} d {d} n {n} S {S} R {R} G {G}")
+    A = bca.Cache(L, H, d, n, S, has_ref=R, kv_dtype=kv)
+    B = bca.Cache(L, H, d, n, S, has_ref=R, kv_dtype=kv)
+    for c in (A, B):
+        if fp8:
+            for l in range(L):
+                c.set_kv_scales(l, [8.0 / 448.0] * H, [8.0 / 448.0] * H)
+        for l in range(L):
+            if R:
+                _, k, v = _chunk(n, H, d, l, 1000, fp8)
+                c.append_chunk(l, 0, k, v, is_ref=True)
+            for t in range(S):
+                _, k, v = _chunk(n, H, d, l, t, fp8)
+                c.append_chunk(l, t, k, v)
+    # static buffers the graph reads and writes
+    Q = [torch.empty((n, H, d), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    K = [torch.empty_like(Q[0]) for _ in range(L)]
+    V = [torch.empty_like(Q[0]) for _ in range(L)]
+    O = [torch.empty_like(Q[0]) for _ in range(L)]
+    LSE = [torch.empty((H, n), dtype=torch.float32, device="cuda") for _ in range(L)]
+    t0 = S
+    spec0 = A.spec(t0, S, use_ref=R, num_segments=G)
+    ws = A.workspace(spec0)
+    d_chunk = torch.full((1,), t0, dtype=torch.int64, device="cuda")
+    for l in range(L):
+        assert A.replayable(l, spec0)
+    # every kernel the graph holds runs once before the capture (code objects
+    # load on first launch), on B's spare twin so that A and B stay equal
+    scratch = bca.Cache(L, H, d, n, S, has_ref=R, kv_dtype=kv)
+    if fp8:
+        scratch.set_kv_scales(0, [8.0 / 448.0] * H, [8.0 / 448.0] * H)
+    dummy = torch.full((1,), -1, dtype=torch.int64, device="cuda")
+    q, k, v = _chunk(n, H, d, 0, 0, fp8)
+    scratch.attend(0, q, k, v, scratch.spec(0, S, num_segments=G), workspace=None)
+    scratch.append_chunk_dev(0, dummy, k, v)
+    bca.Cache.advance_counter(dummy)
+    torch.cuda.synchronize()
+    assert int(dummy.item()) == 0
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for l in range(L):
+            A.attend(l, Q[l], K[l], V[l], spec0, out=O[l], lse=LSE[l], workspace=ws)
+            A.append_chunk_dev(l, d_chunk, K[l], V[l])
+        bca.Cache.advance_counter(d_chunk)
+    torch.cuda.synchronize()
+
+    for t in range(t0, t0 + 2 * S + 3):  # wraps the ring more than twice
+        for l in range(L):
+            q, k, v = _chunk(n, H, d, l, t, fp8)
+            Q[l].copy_(q)
+            K[l].copy_(k)
+            V[l].copy_(v)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for l in range(L):
+            A.set_slot_chunk(l, t % S, t)
+        assert int(d_chunk.item()) == t + 1
+        spec = B.spec(t, S, use_ref=R, num_segments=G)
+        for l in range(L):
+            o, lse = B.attend(l, Q[l], K[l], V[l], spec)
+            torch.cuda.synchronize()
+            assert torch.equal(o, O[l]) and torch.equal(lse, LSE[l]), (t, l)
+            B.append_chunk(l, t, K[l], V[l])
+        torch.cuda.synchronize()
+        assert torch.equal(A.mem, B.mem), f"cache bytes differ after chunk {t}"
+        for l in range(L):
+            assert A.slot_chunk(l, t % S) == B.slot_chunk(l, t % S) == t
+    log(f"graph replay {kv}: chunks {t0}..{t} bit-identical to the eager loop")
+
+
+def test_device_chunk_id_negative_writes_nothing():
+    import attention_bca_attend_amd as bca
+    H, d, n, S = 2, 128, 40, 2
+    c = bca.Cache(1, H, d, n, S, kv_dtype="bf16")
+    c.mem.fill_(7)
+    before = c.mem.clone()
+    _, k, v = _chunk(n, H, d, 0, 0, False)
+    neg = torch.full((1,), -3, dtype=torch.int64, device="cuda")
+    c.append_chunk_dev(0, neg, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(c.mem, before)
+    # a device id of 5 writes slot 1 exactly as bca_append_chunk(5) does
+    five = torch.full((1,), 5, dtype=torch.int64, device="cuda")
+    c.append_chunk_dev(0, five, k, v)
+    ref = bca.Cache(1, H, d, n, S, kv_dtype="bf16")
+    ref.mem.fill_(7)
+    ref.append_chunk(0, 5, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(c.mem, ref.mem)
+    assert np.array_equal(c.blocks(0)[0][:, 1].float().cpu().numpy(),
+                          k.float().cpu().numpy().transpose(1, 0, 2))
