@@ -238,12 +238,15 @@ def main_graph(args, cfg):
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     per_chunk = []
+    host_s = 0.0
     start.record()
     for _ in range(steps):
         c0 = torch.cuda.Event(enable_timing=True)
         c1 = torch.cuda.Event(enable_timing=True)
         c0.record()
+        h0 = time.perf_counter()
         replay()
+        host_s += time.perf_counter() - h0
         c1.record()
         per_chunk.append((c0, c1))
     end.record()
@@ -267,6 +270,7 @@ def main_graph(args, cfg):
         "us_per_chunk_layer": round(ms_step * 1e3 / n_attend, 3),
         "pct_mfma_peak": round(100.0 * tflops / peak, 2),
         "chunk_ms_min_max": [round(min(chunk_ms), 4), round(max(chunk_ms), 4)],
+        "host_ms_per_step": round(host_s * 1e3 / steps, 4),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                      "traffic": measured_traffic(cfg["workload"]),
@@ -491,12 +495,15 @@ def main():
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     per_chunk = []
+    host_s = 0.0
     start.record()
     for i in range(steps):
         c0 = torch.cuda.Event(enable_timing=True)
         c1 = torch.cuda.Event(enable_timing=True)
         c0.record()
+        h0 = time.perf_counter()
         run_chunk(t_chunk)
+        host_s += time.perf_counter() - h0
         c1.record()
         per_chunk.append((c0, c1))
         t_chunk += 1
@@ -542,6 +549,7 @@ def main():
         "attend_us": round(attend_us, 3),
         "pct_mfma_peak": round(100.0 * achieved / peak, 2),
         "chunk_ms_min_max": [round(min(chunk_ms), 4), round(max(chunk_ms), 4)],
+        "host_ms_per_step": round(host_s * 1e3 / steps, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(cfg["workload"]),
