@@ -1334,16 +1334,24 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(const AttnArgs a) {
 //   M = max_g LSE_g, w_g = exp(LSE_g - M) (0 for LSE_g = -inf),
 //   O = sum_g w_g O_g / sum_g w_g, LSE = M + ln sum_g w_g.
 // One work group covers 256 / (D/4) rows of one unit; each thread four dims.
+// Pieces whose loads the merge issues all at once.
+constexpr int kMergeBatch = 4;
+
 template <int D, typename OutT>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   constexpr int TPR = D / 4, RPB = 256 / TPR;
   const int blocks_per_unit = (a.bm + RPB - 1) / RPB;
   const int u = blockIdx.x / blocks_per_unit;
   const int rb = blockIdx.x - u * blocks_per_unit;
-  const int64_t I = (int64_t)a.units * a.T;
-  const int64_t w0 = first_wg_of((int64_t)u * a.T, I, a.P);
-  const int64_t w1 = first_wg_of((int64_t)(u + 1) * a.T - 1, I, a.P);
-  const int pieces = (int)(w1 - w0 + 1);
+  // pieces of unit u: P / units when every unit is cut alike, else from the ranges
+  int pieces;
+  if (a.P % a.units == 0) {
+    pieces = a.P / a.units;
+  } else {
+    const int64_t I = (int64_t)a.units * a.T;
+    pieces = (int)(first_wg_of((int64_t)(u + 1) * a.T - 1, I, a.P) -
+                   first_wg_of((int64_t)u * a.T, I, a.P) + 1);
+  }
   if (pieces <= 1) return;  // written whole by the attention kernel
   const int rloc = rb * RPB + threadIdx.x / TPR;
   const int c4 = (threadIdx.x % TPR) * 4;
@@ -1352,19 +1360,46 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   const int h = ul / a.QT, qt = ul - h * a.QT;
   const int row = qt * a.bm + rloc;
   if (row >= a.n) return;
+  const int64_t prow0 = (int64_t)u * a.jmax * a.bm + rloc;  // piece j: prow0 + j bm
   float M = -INFINITY;
-  for (int j = 0; j < pieces; ++j)
-    M = fmaxf(M, a.part_lse[((int64_t)u * a.jmax + j) * a.bm + rloc]);
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  if (M != -INFINITY) {
-    for (int j = 0; j < pieces; ++j) {
-      const int64_t prow = ((int64_t)u * a.jmax + j) * a.bm + rloc;
-      const float lj = a.part_lse[prow];
-      const float wj = (lj == -INFINITY) ? 0.f : expf(lj - M);
-      wsum += wj;
-      const f32x4_t oj = *reinterpret_cast<const f32x4_t*>(a.part_o + prow * D + c4);
-      acc += wj * oj;
+  if (pieces <= kMergeBatch) {
+    // every load of the row first, then the combination (one memory latency)
+    float lj[kMergeBatch];
+    f32x4_t oj[kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      if (j < pieces) {
+        const int64_t prow = prow0 + (int64_t)j * a.bm;
+        lj[j] = a.part_lse[prow];
+        oj[j] = *reinterpret_cast<const f32x4_t*>(a.part_o + prow * D + c4);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j)
+      if (j < pieces) M = fmaxf(M, lj[j]);
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) {
+        if (j < pieces) {
+          const float wj = (lj[j] == -INFINITY) ? 0.f : expf(lj[j] - M);
+          wsum += wj;
+          acc += wj * oj[j];
+        }
+      }
+    }
+  } else {
+    for (int j = 0; j < pieces; ++j) M = fmaxf(M, a.part_lse[prow0 + (int64_t)j * a.bm]);
+    if (M != -INFINITY) {
+      for (int j = 0; j < pieces; ++j) {
+        const int64_t prow = prow0 + (int64_t)j * a.bm;
+        const float lj = a.part_lse[prow];
+        const float wj = (lj == -INFINITY) ? 0.f : expf(lj - M);
+        wsum += wj;
+        const f32x4_t oj = *reinterpret_cast<const f32x4_t*>(a.part_o + prow * D + c4);
+        acc += wj * oj;
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
