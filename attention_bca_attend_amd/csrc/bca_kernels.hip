@@ -695,7 +695,8 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
         } else {
           const int64_t jslot = (int64_t)w - first_wg_of((int64_t)u * a.T, I, a.P);
           const int64_t prow = ((int64_t)u * a.jmax + jslot) * C::BM + (wave & 7) * 32 + l32;
-          float* pp = a.part_o + prow * D;
+          // bf16 partial outputs (normalised, so |O| stays within the values' range)
+          __bf16* pp = reinterpret_cast<__bf16*>(a.part_o) + prow * D;
 #pragma unroll
           for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -703,7 +704,8 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
               f32x4_t v4 = {st.o[db][4 * g], st.o[db][4 * g + 1], st.o[db][4 * g + 2],
                             st.o[db][4 * g + 3]};
               v4 *= inv;
-              *reinterpret_cast<f32x4_t*>(pp + 32 * db + 8 * g + 4 * hi) = v4;
+              *reinterpret_cast<bf16x4_t*>(pp + 32 * db + 8 * g + 4 * hi) =
+                  __builtin_convertvector(v4, bf16x4_t);
             }
           if (hi == 0) a.part_lse[prow] = lse_val;
         }
@@ -1337,7 +1339,15 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(const AttnArgs a) {
 // Pieces whose loads the merge issues all at once.
 constexpr int kMergeBatch = 4;
 
-template <int D, typename OutT>
+// Four partial-output values: fp32 (fp32 path, e4m3 cache) or bf16 (bf16 path).
+__device__ __forceinline__ f32x4_t load_part4(const float* p) {
+  return *reinterpret_cast<const f32x4_t*>(p);
+}
+__device__ __forceinline__ f32x4_t load_part4(const __bf16* p) {
+  return __builtin_convertvector(*reinterpret_cast<const bf16x4_t*>(p), f32x4_t);
+}
+
+template <int D, typename OutT, typename PartT>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   constexpr int TPR = D / 4, RPB = 256 / TPR;
   const int blocks_per_unit = (a.bm + RPB - 1) / RPB;
@@ -1373,7 +1383,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
       if (j < pieces) {
         const int64_t prow = prow0 + (int64_t)j * a.bm;
         lj[j] = a.part_lse[prow];
-        oj[j] = *reinterpret_cast<const f32x4_t*>(a.part_o + prow * D + c4);
+        oj[j] = load_part4(reinterpret_cast<const PartT*>(a.part_o) + prow * D + c4);
       }
     }
 #pragma unroll
@@ -1397,7 +1407,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
         const float lj = a.part_lse[prow];
         const float wj = (lj == -INFINITY) ? 0.f : expf(lj - M);
         wsum += wj;
-        const f32x4_t oj = *reinterpret_cast<const f32x4_t*>(a.part_o + prow * D + c4);
+        const f32x4_t oj = load_part4(reinterpret_cast<const PartT*>(a.part_o) + prow * D + c4);
         acc += wj * oj;
       }
     }
@@ -1714,9 +1724,11 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
     constexpr int RPB = 256 / (D / 4);
     const int blocks = a.units * ((p.bm + RPB - 1) / RPB);
     if (p.kern == Kern::F32)
-      hipLaunchKernelGGL((merge_kernel<D, float>), dim3(blocks), dim3(256), 0, s, m);
+      hipLaunchKernelGGL((merge_kernel<D, float, float>), dim3(blocks), dim3(256), 0, s, m);
+    else if (p.kern == Kern::FP8)
+      hipLaunchKernelGGL((merge_kernel<D, __bf16, float>), dim3(blocks), dim3(256), 0, s, m);
     else
-      hipLaunchKernelGGL((merge_kernel<D, __bf16>), dim3(blocks), dim3(256), 0, s, m);
+      hipLaunchKernelGGL((merge_kernel<D, __bf16, __bf16>), dim3(blocks), dim3(256), 0, s, m);
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
   }
