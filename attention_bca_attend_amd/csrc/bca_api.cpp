@@ -114,11 +114,6 @@ bool pair_supported(int32_t qkv, int32_t kv) {
 }
 
 int wgs_per_cu(Kern k) {
-  static int override_ = [] {
-    const char* e = getenv("BCA_WGS_PER_CU");
-    return e ? atoi(e) : 0;
-  }();
-  if (override_ > 0) return override_;
   // resident work groups per CU (LDS and register limited)
   switch (k) {
     case Kern::F32: return 4;
