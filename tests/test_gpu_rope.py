@@ -168,3 +168,29 @@ def test_attend_rope_matches_attend_on_rotated_inputs():
     o2, l2 = cache.attend(0, qr, kr, to_dev(v, "bf16"), spec)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_attend_rope_full_size_wan_shape():
+    """The Wan-shaped call the benchmark times with the rotation fused in (12
+    heads x 1536 tokens, ring of 2 full slots, automatic split), chunk 2 at
+    positions 2n .. 3n-1; the oracle on heads 0 and 11 in full."""
+    H, d, n, S, W, t = 12, 128, 1536, 2, 2, 2
+    cache = new_cache(1, H, d, n, S)
+    history = {}
+    for c in range(S):
+        _, k, v = synth.qkv(n, H, d, 13, c, 0, dtype="bf16")
+        cache.append_chunk(0, c, to_dev(k, "bf16"), to_dev(v, "bf16"), rope=(BASE, c * n))
+        history[c] = (oracle.rope(k.astype(np.float64), c * n, BASE), v.astype(np.float64))
+    q, k, v = synth.qkv(n, H, d, 13, t, 0, dtype="bf16")
+    spec = cache.spec(t, W)
+    o, lse = cache.attend(0, to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), spec,
+                          rope=(BASE, t * n))
+    o, lse = to_np(o), to_np(lse)
+    qr = oracle.rope(q.astype(np.float64), t * n, BASE)
+    kr = oracle.rope(k.astype(np.float64), t * n, BASE)
+    for h in (0, 11):
+        hs = slice(h, h + 1)
+        hist = {c: (kv[0][:, hs], kv[1][:, hs]) for c, kv in history.items()}
+        eo, el = oracle.attend(qr[:, hs], kr[:, hs], v[:, hs].astype(np.float64), hist, t=t, W=W,
+                               scale=1.0 / math.sqrt(d))
+        assert_close(o[:, hs], lse[hs], eo, el, TOL["bf16"], f"Wan-shaped rope call head {h}")
