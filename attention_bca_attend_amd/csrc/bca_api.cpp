@@ -16,6 +16,7 @@
 //    the newest chunk over the oldest slot in place; split-window attention
 //    with a log-sum-exp merge) and "technical novelty" (7 intervals, 8-bit KV).
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -87,6 +88,15 @@ bool desc_ok(const bca_cache_desc* d, std::string* why) {
   // keys per head (all blocks plus the current chunk) must fit int32 with room
   const int64_t blocks = (int64_t)d->ring_slots + d->has_ref + 1;
   if (blocks * (int64_t)d->chunk_tokens > (int64_t)1 << 30) return bad("chunk_tokens too large");
+  // the kernels address one head's cache blocks, and one chunk's q/k/v/o
+  // rows, with 32-bit byte offsets
+  const int64_t limit = (int64_t)INT32_MAX - 4096;
+  const int64_t head_bytes = ((int64_t)d->ring_slots + d->has_ref) * d->chunk_tokens *
+                             d->head_dim * (int64_t)elem_size(d->kv_dtype);
+  const int64_t qkv_es = d->kv_dtype == BCA_F32 ? 4 : 2;
+  const int64_t chunk_bytes = (int64_t)d->chunk_tokens * d->num_heads * d->head_dim * qkv_es;
+  if (head_bytes > limit) return bad("one head's cache blocks exceed 2 GiB");
+  if (chunk_bytes > limit) return bad("one chunk's q/k/v rows exceed 2 GiB");
   return true;
 }
 

@@ -416,3 +416,15 @@ def test_attend_replayable_rule():
     with pytest.raises(BcaError):
         bca.bca_attend_replayable(h, 0, spec(2, 3))          # history > ring slots
     bca.bca_cache_destroy(h)
+
+
+def test_descriptor_limits_of_32_bit_offsets():
+    # one head's cache blocks: (S+R) * n * d * es bytes must stay below 2 GiB
+    over = bca.bca_cache_desc(1, 1, 128, 140000, 62, 0, bca.BF16)  # 62 * 140000 * 256 B ≈ 2.22 GB
+    assert bca.bca_cache_bytes(over) == 0
+    ok = bca.bca_cache_desc(1, 1, 128, 1 << 16, 62, 0, bca.BF16)  # ≈ 1.04 GB
+    assert bca.bca_cache_bytes(ok) > 0
+    # one chunk's q/k/v rows: n * H * d * 2 bytes (bf16) must stay below 2 GiB
+    big = bca.bca_cache_desc(1, 64, 128, 1 << 17, 1, 0, bca.BF16)  # 2^17 * 64 * 256 B = 2 GiB
+    assert bca.bca_cache_bytes(big) == 0
+    assert bca.bca_cache_bytes(bca.bca_cache_desc(1, 32, 128, 1 << 17, 1, 0, bca.BF16)) > 0
