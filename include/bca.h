@@ -97,7 +97,10 @@ typedef struct {
 } bca_window_spec;
 
 /* Bytes of device memory a cache with this descriptor needs (K/V blocks of all
- * layers). Returns 0 for an invalid descriptor. */
+ * layers). Returns 0 for an invalid descriptor, including one whose blocks of
+ * one head ((S+R)*n*d elements) or whose chunk rows (n*H*d elements of q, k,
+ * v or o) would reach 2 GiB: the kernels address those with 32-bit byte
+ * offsets. */
 size_t bca_cache_bytes(const bca_cache_desc* desc);
 
 /* Creates the host handle over caller memory dev_mem (at least
@@ -149,7 +152,8 @@ size_t bca_attend_workspace_bytes(const bca_cache* cache, const bca_window_spec*
  * itself is therefore not visible.
  * o: device [n][H][d] in qkv_dtype. lse: device fp32 [H][n], may be NULL.
  * workspace: device, at least bca_attend_workspace_bytes(); may be NULL when
- * that is 0. It holds the fp32 partial outputs of a split window and, on an
+ * that is 0. It holds the partial outputs of a split window (normalised O in
+ * bf16 on a BF16 cache, fp32 otherwise, and fp32 LSE) and, on an
  * FP8_E4M3 cache, the e4m3 copy of the current chunk's K and V ([H][n][d] each,
  * quantised with the layer's per-head scales, so the chunk attends to itself
  * through the same codec as the cached chunks); an FP8_E4M3 cache always
@@ -230,9 +234,12 @@ bca_status bca_attend_rope(const bca_cache* cache, int32_t layer, const bca_wind
  *     q, o : [C*n][H][d]
  *     k, v : [P + C*n][H][d]   prefix rows first, then the chunks in order
  *     lse  : fp32 [C][H][n] (natural log), or NULL
- * qkv_dtype: BCA_F32 or BCA_BF16; head_dim 64 or 128. The chunks are computed
- * one after the other on `stream` (each as one attention launch plus, when its
- * window is split, one merge launch), sharing the workspace.
+ * qkv_dtype: BCA_F32 or BCA_BF16; head_dim 64 or 128. The work is enqueued on
+ * `stream` as attention launches that share the workspace, each followed by a
+ * merge launch when its windows are split: with BCA_BF16 one launch per chunk
+ * before the window reaches its full length (chunks 0 .. W-1, and chunk W too
+ * with a prefix) and one launch for all the remaining chunks, which see the
+ * same number of keys; with BCA_F32 one launch per chunk.
  * Errors: BCA_ERR_INVALID_ARG for a NULL or bad spec (non-positive sizes,
  * history < 0, prefix_tokens < 0, num_segments outside [0, 64], non-finite
  * scale), NULL or misaligned buffers (16 bytes; lse 4), or K/V larger than
