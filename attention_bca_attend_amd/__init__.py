@@ -16,7 +16,7 @@ import math
 import os
 
 __all__ = [
-    "F32", "BF16", "FP8_E4M3", "BcaError", "bca_cache_desc", "bca_window_spec",
+    "F32", "BF16", "FP8_E4M3", "FP8_E4M3_BLOCK", "BcaError", "bca_cache_desc", "bca_window_spec",
     "bca_plan_info", "bca_cache_bytes", "bca_cache_create", "bca_cache_destroy",
     "bca_cache_set_kv_scales", "bca_append_chunk", "bca_attend_workspace_bytes", "bca_attend",
     "bca_append_chunk_rope", "bca_attend_rope_workspace_bytes", "bca_attend_rope",
@@ -28,7 +28,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbca.so")
 
-F32, BF16, FP8_E4M3 = 0, 1, 2
+F32, BF16, FP8_E4M3, FP8_E4M3_BLOCK = 0, 1, 2, 3
 BCA_OK = 0
 STATUS = {0: "BCA_OK", -1: "BCA_ERR_INVALID_ARG", -2: "BCA_ERR_OUT_OF_ORDER",
           -3: "BCA_ERR_WORKSPACE", -4: "BCA_ERR_UNSUPPORTED", -5: "BCA_ERR_HIP"}
@@ -327,7 +327,8 @@ def bca_attend_plan(handle: int, layer: int, spec) -> dict:
     }
 
 
-_DT = {"fp32": F32, "f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "fp8_e4m3": FP8_E4M3}
+_DT = {"fp32": F32, "f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "fp8_e4m3": FP8_E4M3,
+       "fp8_block": FP8_E4M3_BLOCK}
 
 
 class Cache:
@@ -364,14 +365,29 @@ class Cache:
         import torch
         d = self.desc
         nb = d.ring_slots + d.has_ref
-        tdt = {F32: torch.float32, BF16: torch.bfloat16, FP8_E4M3: torch.uint8}[d.kv_dtype]
-        es = {F32: 4, BF16: 2, FP8_E4M3: 1}[d.kv_dtype]
+        tdt = {F32: torch.float32, BF16: torch.bfloat16, FP8_E4M3: torch.uint8,
+               FP8_E4M3_BLOCK: torch.uint8}[d.kv_dtype]
+        es = {F32: 4, BF16: 2, FP8_E4M3: 1, FP8_E4M3_BLOCK: 1}[d.kv_dtype]
         half = d.num_heads * nb * d.chunk_tokens * d.head_dim * es
         base = 2 * layer * half
         k = self.mem[base:base + half].view(tdt).view(d.num_heads, nb, d.chunk_tokens, d.head_dim)
         v = self.mem[base + half:base + 2 * half].view(tdt).view(d.num_heads, nb,
                                                                    d.chunk_tokens, d.head_dim)
         return k, v
+
+    def block_scales(self, layer: int):
+        """FP8_E4M3_BLOCK caches: (K, V) scale views of one layer, fp32 [S+R][H]
+        (the table after the blocks: [L][K|V][S+R][H])."""
+        import torch
+        d = self.desc
+        if d.kv_dtype != FP8_E4M3_BLOCK:
+            raise BcaError(-1, "only FP8_E4M3_BLOCK caches keep scales per block")
+        nb = d.ring_slots + d.has_ref
+        base = 2 * d.num_layers * d.num_heads * nb * d.chunk_tokens * d.head_dim
+        per = nb * d.num_heads * 4
+        k = self.mem[base + 2 * layer * per:base + (2 * layer + 1) * per].view(torch.float32)
+        v = self.mem[base + (2 * layer + 1) * per:base + (2 * layer + 2) * per].view(torch.float32)
+        return k.view(nb, d.num_heads), v.view(nb, d.num_heads)
 
     def slot_chunk(self, layer: int, slot: int) -> int:
         return bca_cache_slot_chunk(self.handle, layer, slot)

@@ -63,9 +63,12 @@ size_t elem_size(int32_t dt) {
     case BCA_F32: return 4;
     case BCA_BF16: return 2;
     case BCA_FP8_E4M3: return 1;
+    case BCA_FP8_E4M3_BLOCK: return 1;
   }
   return 0;
 }
+
+bool is_fp8(int32_t kv) { return kv == BCA_FP8_E4M3 || kv == BCA_FP8_E4M3_BLOCK; }
 
 bool desc_ok(const bca_cache_desc* d, std::string* why) {
   auto bad = [&](const char* m) {
@@ -81,7 +84,7 @@ bool desc_ok(const bca_cache_desc* d, std::string* why) {
     return bad("ring_slots must be in [1, 62]");
   if (d->has_ref != 0 && d->has_ref != 1) return bad("has_ref must be 0 or 1");
   if (elem_size(d->kv_dtype) == 0) return bad("kv_dtype is not a bca_dtype");
-  if (d->kv_dtype == BCA_FP8_E4M3) {
+  if (is_fp8(d->kv_dtype)) {
     if (d->num_heads > kMaxHeadsFp8) return bad("FP8_E4M3 caches support at most 64 heads");
     if (d->head_dim != 128) return bad("FP8_E4M3 caches need head_dim 128");
   }
@@ -108,6 +111,17 @@ size_t half_layer_bytes(const bca_cache_desc& d) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// FP8_E4M3_BLOCK: the scale table after the blocks, fp32 [L][K|V][S+R][H].
+size_t block_scale_bytes(const bca_cache_desc& d) {
+  if (d.kv_dtype != BCA_FP8_E4M3_BLOCK) return 0;
+  const size_t n = (size_t)d.num_layers * 2 * (d.ring_slots + d.has_ref) * d.num_heads * 4;
+  return (n + 255) & ~(size_t)255;
+}
+
+// Key tiles of one block: FP8_E4M3_BLOCK pads every visible block to whole
+// tiles, so that each tile has one block's scales.
+int block_tiles(const bca_cache_desc& d) { return (d.chunk_tokens + 63) / 64; }
+
 bool layer_ok(const bca_cache* c, int32_t layer) {
   return layer >= 0 && layer < c->d.num_layers;
 }
@@ -120,7 +134,7 @@ Kern kernel_for(int32_t qkv, int32_t kv) {
 
 bool pair_supported(int32_t qkv, int32_t kv) {
   return (qkv == BCA_F32 && kv == BCA_F32) || (qkv == BCA_BF16 && kv == BCA_BF16) ||
-         (qkv == BCA_BF16 && kv == BCA_FP8_E4M3);
+         (qkv == BCA_BF16 && kv == BCA_FP8_E4M3) || (qkv == BCA_BF16 && kv == BCA_FP8_E4M3_BLOCK);
 }
 
 int wgs_per_cu(Kern k) {
@@ -173,6 +187,18 @@ int64_t choose_wgs(const bca_cache* c, Kern k, int64_t units, int64_t T, int32_t
 size_t fp8_stage_bytes(const bca_cache_desc& d) {
   const size_t one = ((size_t)d.num_heads * d.chunk_tokens * d.head_dim + 255) & ~(size_t)255;
   return 2 * one;
+}
+
+// FP8_E4M3_BLOCK: the current chunk's own scales [K|V][H] after its copy.
+size_t cur_scale_bytes(const bca_cache_desc& d) {
+  return ((size_t)2 * d.num_heads * 4 + 255) & ~(size_t)255;
+}
+
+// FP8_E4M3_BLOCK scale table of one layer's K (kv 0) or V (kv 1): [S+R][H].
+float* block_scales(const bca_cache* c, int32_t layer, int kv) {
+  const bca_cache_desc& d = c->d;
+  float* t = reinterpret_cast<float*>(c->mem + 2 * (size_t)d.num_layers * half_layer_bytes(d));
+  return t + ((size_t)layer * 2 + kv) * (d.ring_slots + d.has_ref) * d.num_heads;
 }
 
 size_t partial_bytes(int64_t units, int64_t jmax, int bm, int d) {
@@ -239,8 +265,21 @@ bca_status make_plan(const bca_cache* c, int32_t layer, const bca_window_spec* s
   p.nk = p.nvis * n;
 
   // runs of the cache part: consecutive physical blocks share one run
+  // (FP8_E4M3_BLOCK: one run per block, each padded to whole key tiles)
   p.nruns = 0;
-  for (int i = 0; i + 1 < p.nvis; ++i) {
+  p.blk = d.kv_dtype == BCA_FP8_E4M3_BLOCK ? 1 : 0;
+  p.tpb = block_tiles(d);
+  if (p.blk) {
+    for (int i = 0; i + 1 < p.nvis; ++i) {
+      Run r;
+      r.vstart = i * p.tpb * 64;
+      r.len = n;
+      r.phys = p.vis_block[i] * n;
+      r.moves = 0;
+      p.runs[p.nruns++] = r;
+    }
+  }
+  for (int i = 0; !p.blk && i + 1 < p.nvis; ++i) {
     const int b = p.vis_block[i];
     if (p.nruns > 0 && p.runs[p.nruns - 1].phys + p.runs[p.nruns - 1].len == b * n) {
       p.runs[p.nruns - 1].len += n;
@@ -253,7 +292,7 @@ bca_status make_plan(const bca_cache* c, int32_t layer, const bca_window_spec* s
     r.moves = 0;
     p.runs[p.nruns++] = r;
   }
-  p.nk_cache = (p.nvis - 1) * n;
+  p.nk_cache = p.blk ? (p.nvis - 1) * p.tpb * 64 : (p.nvis - 1) * n;
 
   // a3: work planning. Every query row of the chunk sees the same keys, so all
   // units (head, query tile) have the same number of key tiles T. The
@@ -276,6 +315,7 @@ bca_status make_plan(const bca_cache* c, int32_t layer, const bca_window_spec* s
   p.ws_bytes = p.merge ? partial_bytes(p.units, p.jmax, p.bm, d.head_dim) : 0;
   p.stage_off = p.ws_bytes;
   if (p.kern == Kern::FP8) p.ws_bytes += fp8_stage_bytes(d);
+  if (p.blk) p.ws_bytes += cur_scale_bytes(d);
   return BCA_OK;
 }
 
@@ -286,7 +326,7 @@ extern "C" {
 size_t bca_cache_bytes(const bca_cache_desc* desc) {
   std::string why;
   if (!desc_ok(desc, &why)) return 0;
-  return 2 * (size_t)desc->num_layers * half_layer_bytes(*desc);
+  return 2 * (size_t)desc->num_layers * half_layer_bytes(*desc) + block_scale_bytes(*desc);
 }
 
 bca_status bca_cache_create(const bca_cache_desc* desc, void* dev_mem, size_t bytes,
@@ -326,6 +366,8 @@ bca_status bca_cache_destroy(bca_cache* cache) {
 bca_status bca_cache_set_kv_scales(bca_cache* c, int32_t layer, const float* k_scale,
                                    const float* v_scale) {
   if (!c) return fail(BCA_ERR_INVALID_ARG, "cache is NULL");
+  if (c->d.kv_dtype == BCA_FP8_E4M3_BLOCK)
+    return fail(BCA_ERR_UNSUPPORTED, "FP8_E4M3_BLOCK caches take their scales from the appends");
   if (c->d.kv_dtype != BCA_FP8_E4M3)
     return fail(BCA_ERR_INVALID_ARG, "scales apply to FP8_E4M3 caches only");
   if (!layer_ok(c, layer)) return fail(BCA_ERR_INVALID_ARG, "layer %d out of range", layer);
@@ -383,7 +425,7 @@ bca_status append_impl(bca_cache* c, int32_t layer, int64_t chunk_id, int32_t is
   if (elem_size(in_dtype) == 0) return fail(BCA_ERR_INVALID_ARG, "in_dtype is not a bca_dtype");
   const int32_t kv = c->d.kv_dtype;
   bool ok = (in_dtype == BCA_F32 && kv == BCA_F32) || (in_dtype == BCA_BF16 && kv == BCA_BF16) ||
-            (in_dtype == BCA_BF16 && kv == BCA_FP8_E4M3);
+            (in_dtype == BCA_BF16 && is_fp8(kv));
   if (!ok)
     return fail(BCA_ERR_UNSUPPORTED, "cannot append dtype %d into a cache of dtype %d",
                 in_dtype, kv);
@@ -412,6 +454,14 @@ bca_status append_impl(bca_cache* c, int32_t layer, int64_t chunk_id, int32_t is
       a.k_scale[h] = c->k_scale[(size_t)layer * d.num_heads + h];
       a.v_scale[h] = c->v_scale[(size_t)layer * d.num_heads + h];
     }
+  if (kv == BCA_FP8_E4M3_BLOCK) {
+    if (rope)
+      return fail(BCA_ERR_UNSUPPORTED, "no rotary append into an FP8_E4M3_BLOCK cache");
+    a.dev_scales = 1;
+    a.host_blk = blk;
+    a.ksc = block_scales(c, layer, 0);
+    a.vsc = block_scales(c, layer, 1);
+  }
   if (rope) {
     a.rope = 1;
     a.rope_log2_base = rope->log2_base;
@@ -448,7 +498,7 @@ bca_status bca_append_chunk_dev(bca_cache* c, int32_t layer, const int64_t* d_ch
   if (elem_size(in_dtype) == 0) return fail(BCA_ERR_INVALID_ARG, "in_dtype is not a bca_dtype");
   const int32_t kv = c->d.kv_dtype;
   bool ok = (in_dtype == BCA_F32 && kv == BCA_F32) || (in_dtype == BCA_BF16 && kv == BCA_BF16) ||
-            (in_dtype == BCA_BF16 && kv == BCA_FP8_E4M3);
+            (in_dtype == BCA_BF16 && is_fp8(kv));
   if (!ok)
     return fail(BCA_ERR_UNSUPPORTED, "cannot append dtype %d into a cache of dtype %d",
                 in_dtype, kv);
@@ -472,6 +522,11 @@ bca_status bca_append_chunk_dev(bca_cache* c, int32_t layer, const int64_t* d_ch
       a.k_scale[h] = c->k_scale[(size_t)layer * d.num_heads + h];
       a.v_scale[h] = c->v_scale[(size_t)layer * d.num_heads + h];
     }
+  if (kv == BCA_FP8_E4M3_BLOCK) {
+    a.dev_scales = 1;
+    a.ksc = block_scales(c, layer, 0);
+    a.vsc = block_scales(c, layer, 1);
+  }
   int err = launch_append((bca_dtype)in_dtype, (bca_dtype)kv, d.head_dim, a, (void*)stream);
   if (err != 0) return fail(BCA_ERR_HIP, "append kernel launch failed (hip error %d)", err);
   g_err.clear();
@@ -541,13 +596,17 @@ size_t bca_attend_workspace_bytes(const bca_cache* c, const bca_window_spec* s) 
   // all ring slots, the reference and the current chunk.
   size_t worst = 0;
   const int max_blocks = S + c->d.has_ref + 1;
+  const bool blk = c->d.kv_dtype == BCA_FP8_E4M3_BLOCK;
   for (int blocks = 1; blocks <= max_blocks; ++blocks) {
-    int64_t T = ((int64_t)(blocks - 1) * n + ts.bn - 1) / ts.bn + (n + ts.bn - 1) / ts.bn;
+    const int64_t cache_keys = blk ? (int64_t)(blocks - 1) * block_tiles(c->d) * 64
+                                   : (int64_t)(blocks - 1) * n;
+    int64_t T = (cache_keys + ts.bn - 1) / ts.bn + (n + ts.bn - 1) / ts.bn;
     int64_t P = choose_wgs(c, k, units, T, s->num_segments);
     int32_t jmax = pieces_bound(units, T, P);
     if (jmax > 1) worst = std::max(worst, partial_bytes(units, jmax, ts.bm, c->d.head_dim));
   }
   if (k == Kern::FP8) worst += fp8_stage_bytes(c->d);
+  if (blk) worst += cur_scale_bytes(c->d);
   return worst;
 }
 
@@ -586,6 +645,8 @@ bca_status attend_impl(const bca_cache* c, int32_t layer, const bca_window_spec*
       return fail(BCA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
                   need);
   }
+  if (rope && d.kv_dtype == BCA_FP8_E4M3_BLOCK)
+    return fail(BCA_ERR_UNSUPPORTED, "no rotary attention over an FP8_E4M3_BLOCK cache");
   if (rope) {
     RopeStageArgs r;
     std::memset(&r, 0, sizeof r);
@@ -650,6 +711,16 @@ bca_status attend_impl(const bca_cache* c, int32_t layer, const bca_window_spec*
       a.k_scale[h] = c->k_scale[(size_t)layer * d.num_heads + h];
       a.v_scale[h] = c->v_scale[(size_t)layer * d.num_heads + h];
     }
+  if (p.blk) {
+    a.blk = 1;
+    a.tpb = p.tpb;
+    a.nvis_cache = p.nvis - 1;
+    a.ksc = block_scales(c, layer, 0);
+    a.vsc = block_scales(c, layer, 1);
+    a.cur_sc = reinterpret_cast<const float*>(static_cast<char*>(workspace) + p.stage_off +
+                                              fp8_stage_bytes(d));
+    for (int i = 0; i + 1 < p.nvis; ++i) a.vis_blk[i] = (int8_t)p.vis_block[i];
+  }
   int err = launch_attention(p, a, d.head_dim, (void*)stream);
   if (err == -1) return fail(BCA_ERR_UNSUPPORTED, "no attention kernel for this dtype pair yet");
   if (err != 0) return fail(BCA_ERR_HIP, "attention launch failed (hip error %d)", err);

@@ -52,6 +52,8 @@ inline TileShape tile_shape(Kern k) {
 struct Plan {
   Kern kern;
   int32_t seq;                      // 1: a bca_attend_sequence launch (token-major cache rows)
+  int32_t blk;                      // 1: FP8_E4M3_BLOCK cache (tiles aligned to blocks)
+  int32_t tpb;                      // key tiles per block when blk
   int32_t nvis;                     // visible blocks, current included
   int32_t vis_block[kMaxBlocks];    // physical block (S = reference, -1 = current)
   int64_t vis_id[kMaxBlocks];
@@ -102,6 +104,15 @@ struct AttnArgs {
   Run runs[kMaxBlocks];
   float k_scale[kMaxHeadsFp8];  // fp8 cache: dequantisation scale per head
   float v_scale[kMaxHeadsFp8];
+  // FP8_E4M3_BLOCK: every visible cache block is its own run, padded to tpb
+  // whole key tiles; ksc/vsc are the layer's scale tables [S+R][H], cur_sc the
+  // current chunk's scales [K|V][H]; vis_blk the physical block of each of the
+  // nvis_cache visible cache blocks.
+  int32_t blk, tpb, nvis_cache;
+  const float* ksc;
+  const float* vsc;
+  const float* cur_sc;
+  int8_t vis_blk[kMaxBlocks];
 };
 
 struct MergeArgs {
@@ -131,6 +142,13 @@ struct AppendArgs {
   const int64_t* dev_chunk;
   int32_t slots;
   int64_t block_elems;
+  // Scales from device memory (FP8_E4M3_BLOCK, and the current chunk's copy):
+  // ksc/vsc point at [blocks][H] tables; the block is host_blk, or
+  // (id mod slots) with dev_chunk. append_amax_kernel writes them first.
+  int32_t dev_scales;
+  int32_t host_blk;
+  float* ksc;
+  float* vsc;
   int32_t rope;            // 1: rotate K (rotary embedding) before it is stored
   double rope_log2_base;   // log2 of the rotary base
   int64_t rope_pos0;       // position of the chunk's token 0

@@ -915,7 +915,11 @@ __device__ __forceinline__ void f8_gemm(F8State<D>& st, const unsigned char* SV,
 // than 4; P is scaled by 2^4, so P <= 2^8 stays within e4m3 and values down
 // to 2^-13 of the row's maximum keep a normal e4m3 representation.
 template <int D>
-__device__ __forceinline__ void f8_softmax(F8State<D>& st, int lim, int hi, float c) {
+// off_add and sum_fac serve caches with one scale per block (per tile): P
+// comes out multiplied by 2^off_add = s_V(tile) / s_ref <= 1, and the row
+// sum gets the tile's weights divided back by that ratio (sum_fac).
+__device__ __forceinline__ void f8_softmax(F8State<D>& st, int lim, int hi, float c,
+                                           float off_add = 0.f, float sum_fac = 1.f) {
   if (lim < 64) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -944,7 +948,7 @@ __device__ __forceinline__ void f8_softmax(F8State<D>& st, int lim, int hi, floa
     st.m_run = m_new;
   }
   // P x 2^4 = 2^(s c - m + 4): at most 2^8
-  const float off = st.m_run == -INFINITY ? 4.f : 4.f - st.m_run;
+  const float off = (st.m_run == -INFINITY ? 4.f : 4.f - st.m_run) + off_add;
   f32x16_t p0, p1;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
@@ -954,7 +958,8 @@ __device__ __forceinline__ void f8_softmax(F8State<D>& st, int lim, int hi, floa
   float t8[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) t8[e] = (p0[e] + p0[e + 8]) + (p1[e] + p1[e + 8]);
-  st.l_run += ((t8[0] + t8[4]) + (t8[1] + t8[5])) + ((t8[2] + t8[6]) + (t8[3] + t8[7]));
+  st.l_run += (((t8[0] + t8[4]) + (t8[1] + t8[5])) + ((t8[2] + t8[6]) + (t8[3] + t8[7]))) *
+              sum_fac;
   // byte j = 16 kb + e of P^T holds key block kb's score e
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
@@ -967,10 +972,16 @@ __device__ __forceinline__ void f8_softmax(F8State<D>& st, int lim, int hi, floa
   }
 }
 
-template <int D>
+// BLK: an FP8_E4M3_BLOCK cache. Every visible block is its own run padded to
+// whole key tiles, so each tile has one block's K and V scales: the K scale
+// multiplies the tile's softmax constant, and the V scale relative to the
+// unit's largest (s_ref) enters P as an exponent offset, with the row sum
+// corrected per tile and s_ref applied at normalisation.
+template <int D, bool BLK>
 __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
   using C = F8Cfg<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::NSTAGE * C::STAGE];
+  __shared__ float sc_k[kMaxBlocks], sc_v[kMaxBlocks];  // BLK: the unit's block scales
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1057,9 +1068,23 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
           qf[1][ks][2 * x + 1] = hi4[1];
         }
       // base-2 scale of the raw products: softmax scale, K scale, Q row scale
-      c = a.scale_log2 * a.k_scale[h] * qs;
+      // (BLK: the K scale comes per tile)
+      c = BLK ? a.scale_log2 * qs : a.scale_log2 * a.k_scale[h] * qs;
     }
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    float sv_ref = 1.f;
+    if constexpr (BLK) {
+      // the visible blocks' scales of this head, then the current chunk's
+      if (tid <= a.nvis_cache) {
+        const bool cur = tid == a.nvis_cache;
+        const int64_t e = cur ? h : (int64_t)a.vis_blk[tid] * a.H + h;
+        sc_k[tid] = cur ? a.cur_sc[e] : a.ksc[e];
+        sc_v[tid] = cur ? a.cur_sc[a.H + e] : a.vsc[e];
+      }
+      __syncthreads();
+      sv_ref = sc_v[0];
+      for (int j = 1; j <= a.nvis_cache; ++j) sv_ref = fmaxf(sv_ref, sc_v[j]);
+    }
 
     F8State<D> st;
 #pragma unroll
@@ -1070,6 +1095,20 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
     st.pf[1] = i32x8_t{};
     st.m_run = -INFINITY;
     st.l_run = 0.f;
+
+    // softmax of tile tt (BLK: with its block's scales)
+    auto softmax_tile = [&](int tt) {
+      if constexpr (BLK) {
+        const bool cache_tile = tt < a.cache_tiles;
+        const int j = cache_tile ? tt / a.tpb : a.nvis_cache;
+        const int lim = cache_tile ? min(C::BN, a.n - C::BN * (tt - j * a.tpb))
+                                   : tile_valid(a, tt, C::BN);
+        const float ratio = sc_v[j] / sv_ref;
+        f8_softmax<D>(st, lim, hi, c * sc_k[j], __log2f(ratio), 1.0f / ratio);
+      } else {
+        f8_softmax<D>(st, tile_valid(a, tt, C::BN), hi, c);
+      }
+    };
 
     // Even phases 2r start by requesting tile r+2; odd phases 2q-1 end by
     // waiting for this wave's requests of tile q (read from phase 2q on).
@@ -1101,7 +1140,7 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
       }
       end_phase(0);
       begin_phase(1);
-      if (wave_rows) f8_softmax<D>(st, tile_valid(a, t0, C::BN), hi, c);
+      if (wave_rows) softmax_tile(t0);
       end_phase(1);
       for (int r = 1; r < nt; ++r) {
         begin_phase(2 * r);
@@ -1112,7 +1151,7 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
         }
         end_phase(2 * r);
         begin_phase(2 * r + 1);
-        if (wave_rows) f8_softmax<D>(st, tile_valid(a, t0 + r, C::BN), hi, c);
+        if (wave_rows) softmax_tile(t0 + r);
         end_phase(2 * r + 1);
       }
       begin_phase(2 * nt);
@@ -1136,7 +1175,7 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
       end_phase(1);
       for (int r = 1; r < nt; ++r) {
         begin_phase(2 * r);
-        if (wave_rows) f8_softmax<D>(st, tile_valid(a, t0 + r - 1, C::BN), hi, c);
+        if (wave_rows) softmax_tile(t0 + r - 1);
         end_phase(2 * r);
         begin_phase(2 * r + 1);
         if (wave_rows) {
@@ -1147,7 +1186,7 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
         end_phase(2 * r + 1);
       }
       begin_phase(2 * nt);
-      if (wave_rows) f8_softmax<D>(st, tile_valid(a, t0 + nt - 1, C::BN), hi, c);
+      if (wave_rows) softmax_tile(t0 + nt - 1);
       end_phase(2 * nt);
       begin_phase(2 * nt + 1);
       if (wave_rows) {
@@ -1161,7 +1200,7 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
     // epilogue: P carried 2^4 (in l and in O alike); O is in V-scale units
     if (wave_rows) {
       const float l_tot = xhalf_sum(st.l_run);
-      const float inv = a.v_scale[h] / l_tot;
+      const float inv = (BLK ? sv_ref : a.v_scale[h]) / l_tot;
       const float lse_val = (st.m_run - 4.0f + log2f(l_tot)) * kLn2;
       const int row = q0 + l32;
       const bool whole = (t0 == 0) && (t1 == a.T);
@@ -1581,6 +1620,45 @@ __device__ __forceinline__ uint2 e4m3x8(const float (&x)[8], float s) {
   return make_uint2((unsigned)lo, (unsigned)hi);
 }
 
+// Block index of an append's scales: host_blk, or (id mod slots) for a
+// device-side chunk id (negative ids write nothing, as for the codes).
+__device__ __forceinline__ int append_scale_block(const AppendArgs& a) {
+  if (!a.dev_chunk) return a.host_blk;
+  const int64_t id = *a.dev_chunk;
+  return id < 0 ? -1 : (int)(id % a.slots);
+}
+
+// Scales of an FP8_E4M3_BLOCK append (and of the current chunk's e4m3 copy):
+// per head, scale = (largest |x| of the chunk's rows of that head) / 448,
+// 1 when that maximum is 0 or not finite. One work group per (head, K|V);
+// blockIdx.y selects K (0) or V (1).
+template <int D>
+__global__ __launch_bounds__(256) void append_amax_kernel(const AppendArgs a) {
+  constexpr int G = D / 8;
+  const int h = blockIdx.x;
+  const bool isv = blockIdx.y == 1;
+  const int bi = append_scale_block(a);
+  if (bi < 0) return;
+  const __bf16* src = static_cast<const __bf16*>(isv ? a.v : a.k);
+  float amax = 0.f;
+  for (int64_t i = threadIdx.x; i < (int64_t)a.n * G; i += 256) {
+    const int r = (int)(i / G), g = (int)(i % G);
+    const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(src + ((int64_t)r * a.H + h) * D + 8 * g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[e]));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  __shared__ float wmax[4];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float sc = (m > 0.f && m <= 3.402823466e38f) ? m / 448.0f : 1.0f;
+    (isv ? a.vsc : a.ksc)[(int64_t)bi * a.H + h] = sc;
+  }
+}
+
 // The e4m3 append; blockIdx.y + kv0 selects K (0) or V (1).
 template <int D>
 __global__ __launch_bounds__(256) void append_fp8_kernel(const AppendArgs a, int kv0) {
@@ -1595,7 +1673,9 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(const AppendArgs a, int
   const bool isv = blockIdx.y + kv0 == 1;
   const int64_t blk = append_block_offset(a);
   if (blk < 0) return;
-  const float s = isv ? a.v_scale[h] : a.k_scale[h];
+  const float s = a.dev_scales
+                      ? (isv ? a.vsc : a.ksc)[(int64_t)append_scale_block(a) * a.H + h]
+                      : (isv ? a.v_scale[h] : a.k_scale[h]);
   float y[8];
   load8(reinterpret_cast<const char*>(static_cast<const __bf16*>(isv ? a.v : a.k) + rh * D +
                                       g * 8),
@@ -1688,10 +1768,21 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
           q.k_scale[i] = a.k_scale[i];
           q.v_scale[i] = a.v_scale[i];
         }
+        if (a.blk) {
+          // the chunk's own per-head scales, as an append would take them
+          q.dev_scales = 1;
+          q.host_blk = 0;
+          q.ksc = const_cast<float*>(a.cur_sc);
+          q.vsc = const_cast<float*>(a.cur_sc) + a.H;
+          hipLaunchKernelGGL(append_amax_kernel<D>, dim3((unsigned)a.H, 2), dim3(256), 0, s, q);
+        }
         const int64_t total = (int64_t)a.n * a.H * (D / 8);
         hipLaunchKernelGGL(append_fp8_kernel<D>, dim3((unsigned)((total + 255) / 256), 2),
                            dim3(256), 0, s, q, 0);
-        hipLaunchKernelGGL(attn_fp8_kernel<D>, dim3(p.wgs), dim3(512), 0, s, a);
+        if (a.blk)
+          hipLaunchKernelGGL((attn_fp8_kernel<D, true>), dim3(p.wgs), dim3(512), 0, s, a);
+        else
+          hipLaunchKernelGGL((attn_fp8_kernel<D, false>), dim3(p.wgs), dim3(512), 0, s, a);
       } else {
         return -1;
       }
@@ -1769,8 +1860,10 @@ int launch_append(bca_dtype in, bca_dtype kv, int head_dim, const AppendArgs& a,
   const dim3 grid((unsigned)((total + 255) / 256), 2 - kv0);
   const dim3 rgrid((unsigned)(((int64_t)a.n * (head_dim / 8) + 127) / 128), 1,
                    (unsigned)((a.H + kRopeHeads - 1) / kRopeHeads));
-  if (kv == BCA_FP8_E4M3) {
+  if (kv == BCA_FP8_E4M3 || kv == BCA_FP8_E4M3_BLOCK) {
     if (head_dim != 128 || in != BCA_BF16) return -1;
+    if (a.dev_scales)
+      hipLaunchKernelGGL(append_amax_kernel<128>, dim3((unsigned)a.H, 2), dim3(256), 0, s, a);
     hipLaunchKernelGGL(append_fp8_kernel<128>, grid, dim3(256), 0, s, a, kv0);
     if (a.rope) hipLaunchKernelGGL((append_rope_k_kernel<128, true>), rgrid, dim3(128), 0, s, a, 1);
   } else {

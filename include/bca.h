@@ -71,7 +71,13 @@ typedef enum {
   BCA_ERR_HIP = -5           /* a HIP runtime call (launch, copy) failed              */
 } bca_status;
 
-typedef enum { BCA_F32 = 0, BCA_BF16 = 1, BCA_FP8_E4M3 = 2 } bca_dtype;
+/* BCA_FP8_E4M3_BLOCK: e4m3 codes with one scale per (layer, block, head),
+ * taken from each appended chunk itself (its largest magnitude per head over
+ * 448), so an append re-quantises only the block it writes ("Matrix-Game 4.0"
+ * summary, technical novelty: 8-bit K/V per interval, only the changed
+ * interval re-quantised). The scales live in the cache memory after the
+ * blocks. */
+typedef enum { BCA_F32 = 0, BCA_BF16 = 1, BCA_FP8_E4M3 = 2, BCA_FP8_E4M3_BLOCK = 3 } bca_dtype;
 
 typedef struct bca_cache bca_cache; /* opaque host handle */
 

@@ -11,7 +11,7 @@ import numpy as np
 import oracle
 import synth
 
-TOL = {"fp32": 1e-5, "bf16": 1e-2, "fp8": 5e-2}
+TOL = {"fp32": 1e-5, "bf16": 1e-2, "fp8": 5e-2, "fp8_block": 5e-2}
 
 
 def log(msg: str) -> None:
@@ -22,7 +22,7 @@ def log(msg: str) -> None:
 def to_dev(x: np.ndarray, dtype: str):
     import torch
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
-    t = t.to(torch.bfloat16) if dtype in ("bf16", "fp8") else t
+    t = t.to(torch.bfloat16) if dtype in ("bf16", "fp8", "fp8_block") else t
     return t.cuda()
 
 
@@ -49,6 +49,16 @@ def fp8_stored(x, scales):
     for h in range(x.shape[1]):
         out[:, h, :] = tab[oracle.quant_e4m3(x[:, h, :], scales[h])] * scales[h]
     return out
+
+
+def block_scales_of(x) -> np.ndarray:
+    """Per-head scales of an e4m3 cache block that takes them from the chunk
+    itself: fp32(max |x| over the head's rows) / 448 in fp32, 1 when that
+    maximum is 0 or not finite. x: [n][H][d] (bf16 values)."""
+    a = np.abs(np.asarray(x, dtype=np.float32)).max(axis=(0, 2))
+    ok = (a > 0) & np.isfinite(a)
+    s = np.where(ok, a / np.float32(448.0), np.float32(1.0))
+    return s.astype(np.float32)
 
 
 class Sequence:
@@ -78,6 +88,8 @@ class Sequence:
                          outlier_frac=self.outlier_frac)
 
     def stored(self, k, v):
+        if self.dtype == "fp8_block":
+            return (fp8_stored(k, block_scales_of(k)), fp8_stored(v, block_scales_of(v)))
         if self.dtype == "fp8" and self.scales is not None:
             return fp8_stored(k, self.scales[0]), fp8_stored(v, self.scales[1])
         return k.astype(np.float64), v.astype(np.float64)

@@ -428,3 +428,32 @@ def test_descriptor_limits_of_32_bit_offsets():
     big = bca.bca_cache_desc(1, 64, 128, 1 << 17, 1, 0, bca.BF16)  # 2^17 * 64 * 256 B = 2 GiB
     assert bca.bca_cache_bytes(big) == 0
     assert bca.bca_cache_bytes(bca.bca_cache_desc(1, 32, 128, 1 << 17, 1, 0, bca.BF16)) > 0
+
+
+def test_block_scaled_fp8_cache_on_the_host():
+    B = bca.FP8_E4M3_BLOCK
+    d = bca.bca_cache_desc(3, 4, 128, 405, 20, 1, B)
+    table = ((3 * 2 * 21 * 4 * 4 + 255) // 256) * 256
+    assert bca.bca_cache_bytes(d) == 3 * 2 * 4 * 21 * 405 * 128 + table
+    assert bca.bca_cache_bytes(bca.bca_cache_desc(1, 4, 64, 16, 2, 0, B)) == 0  # head_dim 128 only
+    h = bca.bca_cache_create(d, FAKE, bca.bca_cache_bytes(d))
+    with pytest.raises(BcaError) as e:
+        bca.bca_cache_set_kv_scales(h, 0, [1.0] * 4, [1.0] * 4)
+    assert e.value.status == -4
+    with pytest.raises(BcaError) as e:
+        bca.bca_append_chunk_rope(h, 0, 0, 0, FAKE, FAKE, bca.BF16, 1e4, 0, 0)
+    assert e.value.status == -4
+    for sl in range(20):
+        bca.bca_cache_set_slot_chunk(h, 0, sl, sl)
+    bca.bca_cache_set_slot_chunk(h, 0, 20, 0)
+    spec = bca.bca_window_spec(20, 20, 1, 4, 0.1)
+    plan = bca.bca_attend_plan(h, 0, spec)
+    # every visible block padded to whole 64-key tiles: 21 cache blocks x 7 + 7
+    assert plan["kv_tiles"] == 22 * 7 and plan["visible_keys"] == 22 * 405, plan
+    need = bca.bca_attend_workspace_bytes(h, spec)
+    assert need == plan["workspace_bytes"] and need >= 2 * 4 * 405 * 128 + 2 * 4 * 4
+    with pytest.raises(BcaError) as e:
+        bca.bca_attend_rope(h, 0, spec, FAKE, FAKE, FAKE, bca.BF16, 1e4, 0, FAKE, 0, FAKE,
+                            bca.bca_attend_rope_workspace_bytes(h, spec), 0)
+    assert e.value.status == -4
+    bca.bca_cache_destroy(h)

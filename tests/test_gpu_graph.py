@@ -38,18 +38,23 @@ CASES = [
     ("bf16", 2, 2, 128, 100, 2, False, 0),
     ("bf16", 2, 3, 64, 64, 3, True, 2),
     ("fp8", 2, 2, 128, 96, 2, True, 0),
+    ("fp8_block", 2, 2, 128, 96, 2, True, 0),
 ]
 
 
 @pytest.mark.parametrize("kv,L,H,d,n,S,R,G", CASES)
 def test_replayed_chunk_step_equals_eager(kv, L, H, d, n, S, R, G):
     import attention_bca_attend_amd as bca
-    fp8 = kv == "fp8"
+    fp8 = kv in ("fp8", "fp8_block")
     log(f"graph replay {kv} L {L} H {H} d {d} n {n} S {S} R {R} G {G}")
     A = bca.Cache(L, H, d, n, S, has_ref=R, kv_dtype=kv)
     B = bca.Cache(L, H, d, n, S, has_ref=R, kv_dtype=kv)
+    # the whole memory is compared below, including bytes no call writes (the
+    # padding after a block-scaled cache's scale table)
+    A.mem.zero_()
+    B.mem.zero_()
     for c in (A, B):
-        if fp8:
+        if kv == "fp8":
             for l in range(L):
                 c.set_kv_scales(l, [8.0 / 448.0] * H, [8.0 / 448.0] * H)
         for l in range(L):
@@ -74,7 +79,7 @@ def test_replayed_chunk_step_equals_eager(kv, L, H, d, n, S, R, G):
     # every kernel the graph holds runs once before the capture (code objects
     # load on first launch), on B's spare twin so that A and B stay equal
     scratch = bca.Cache(L, H, d, n, S, has_ref=R, kv_dtype=kv)
-    if fp8:
+    if kv == "fp8":
         scratch.set_kv_scales(0, [8.0 / 448.0] * H, [8.0 / 448.0] * H)
     dummy = torch.full((1,), -1, dtype=torch.int64, device="cuda")
     q, k, v = _chunk(n, H, d, 0, 0, fp8)
