@@ -981,7 +981,9 @@ template <int D, bool BLK>
 __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
   using C = F8Cfg<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::NSTAGE * C::STAGE];
-  __shared__ float sc_k[kMaxBlocks], sc_v[kMaxBlocks];  // BLK: the unit's block scales
+  // BLK: the unit's K scale per block, and per block the exponent offset
+  // log2(s_V / s_ref) and the row-sum factor s_ref / s_V
+  __shared__ float sc_k[kMaxBlocks], sc_off[kMaxBlocks], sc_fac[kMaxBlocks];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1075,15 +1077,23 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
     float sv_ref = 1.f;
     if constexpr (BLK) {
       // the visible blocks' scales of this head, then the current chunk's
+      float svj = 0.f;
       if (tid <= a.nvis_cache) {
         const bool cur = tid == a.nvis_cache;
         const int64_t e = cur ? h : (int64_t)a.vis_blk[tid] * a.H + h;
         sc_k[tid] = cur ? a.cur_sc[e] : a.ksc[e];
-        sc_v[tid] = cur ? a.cur_sc[a.H + e] : a.vsc[e];
+        svj = cur ? a.cur_sc[a.H + e] : a.vsc[e];
+        sc_fac[tid] = svj;
       }
       __syncthreads();
-      sv_ref = sc_v[0];
-      for (int j = 1; j <= a.nvis_cache; ++j) sv_ref = fmaxf(sv_ref, sc_v[j]);
+      sv_ref = sc_fac[0];
+      for (int j = 1; j <= a.nvis_cache; ++j) sv_ref = fmaxf(sv_ref, sc_fac[j]);
+      __syncthreads();
+      if (tid <= a.nvis_cache) {
+        sc_off[tid] = __log2f(svj / sv_ref);
+        sc_fac[tid] = sv_ref / svj;
+      }
+      __syncthreads();
     }
 
     F8State<D> st;
@@ -1096,15 +1106,21 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
     st.m_run = -INFINITY;
     st.l_run = 0.f;
 
-    // softmax of tile tt (BLK: with its block's scales)
+    // softmax of tile tt (BLK: with its block's scales). Each wave visits the
+    // unit's tiles in increasing order, so the block of a cache tile is
+    // tracked from the unit's first tile on instead of divided out per tile.
+    int blk_j = BLK ? t0 / a.tpb : 0, blk_end = BLK ? (blk_j + 1) * a.tpb : 0;
     auto softmax_tile = [&](int tt) {
       if constexpr (BLK) {
         const bool cache_tile = tt < a.cache_tiles;
-        const int j = cache_tile ? tt / a.tpb : a.nvis_cache;
-        const int lim = cache_tile ? min(C::BN, a.n - C::BN * (tt - j * a.tpb))
+        while (tt >= blk_end) {
+          ++blk_j;
+          blk_end += a.tpb;
+        }
+        const int j = cache_tile ? blk_j : a.nvis_cache;
+        const int lim = cache_tile ? min(C::BN, a.n - C::BN * (tt - (blk_end - a.tpb)))
                                    : tile_valid(a, tt, C::BN);
-        const float ratio = sc_v[j] / sv_ref;
-        f8_softmax<D>(st, lim, hi, c * sc_k[j], __log2f(ratio), 1.0f / ratio);
+        f8_softmax<D>(st, lim, hi, c * sc_k[j], sc_off[j], sc_fac[j]);
       } else {
         f8_softmax<D>(st, tile_valid(a, tt, C::BN), hi, c);
       }
@@ -1630,30 +1646,42 @@ __device__ __forceinline__ int append_scale_block(const AppendArgs& a) {
 
 // Scales of an FP8_E4M3_BLOCK append (and of the current chunk's e4m3 copy):
 // per head, scale = (largest |x| of the chunk's rows of that head) / 448,
-// 1 when that maximum is 0 or not finite. One work group per (head, K|V);
-// blockIdx.y selects K (0) or V (1).
+// 1 when that maximum is 0 or not finite. One work group of 1024 threads per
+// (head, K|V), each thread with up to 8 row loads in flight; blockIdx.y
+// selects K (0) or V (1).
 template <int D>
-__global__ __launch_bounds__(256) void append_amax_kernel(const AppendArgs a) {
-  constexpr int G = D / 8;
+__global__ __launch_bounds__(1024) void append_amax_kernel(const AppendArgs a) {
+  constexpr int G = D / 8, NT = 1024, U = 8;
   const int h = blockIdx.x;
   const bool isv = blockIdx.y == 1;
   const int bi = append_scale_block(a);
   if (bi < 0) return;
   const __bf16* src = static_cast<const __bf16*>(isv ? a.v : a.k);
+  const int64_t total = (int64_t)a.n * G;
   float amax = 0.f;
-  for (int64_t i = threadIdx.x; i < (int64_t)a.n * G; i += 256) {
-    const int r = (int)(i / G), g = (int)(i % G);
-    const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(src + ((int64_t)r * a.H + h) * D + 8 * g);
+  for (int64_t i0 = threadIdx.x; i0 < total; i0 += (int64_t)NT * U) {
+    bf16x8_t v[U];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[e]));
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + (int64_t)u * NT;
+      const int64_t r = i / G, g = i % G;
+      v[u] = i < total ? *reinterpret_cast<const bf16x8_t*>(src + (r * a.H + h) * D + 8 * g)
+                       : bf16x8_t{};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[u][e]));
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  __shared__ float wmax[4];
+  __shared__ float wmax[NT / 64];
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
   __syncthreads();
   if (threadIdx.x == 0) {
-    const float m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    float m = wmax[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) m = fmaxf(m, wmax[w]);
     const float sc = (m > 0.f && m <= 3.402823466e38f) ? m / 448.0f : 1.0f;
     (isv ? a.vsc : a.ksc)[(int64_t)bi * a.H + h] = sc;
   }
@@ -1774,7 +1802,7 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
           q.host_blk = 0;
           q.ksc = const_cast<float*>(a.cur_sc);
           q.vsc = const_cast<float*>(a.cur_sc) + a.H;
-          hipLaunchKernelGGL(append_amax_kernel<D>, dim3((unsigned)a.H, 2), dim3(256), 0, s, q);
+          hipLaunchKernelGGL(append_amax_kernel<D>, dim3((unsigned)a.H, 2), dim3(1024), 0, s, q);
         }
         const int64_t total = (int64_t)a.n * a.H * (D / 8);
         hipLaunchKernelGGL(append_fp8_kernel<D>, dim3((unsigned)((total + 255) / 256), 2),
@@ -1863,7 +1891,7 @@ int launch_append(bca_dtype in, bca_dtype kv, int head_dim, const AppendArgs& a,
   if (kv == BCA_FP8_E4M3 || kv == BCA_FP8_E4M3_BLOCK) {
     if (head_dim != 128 || in != BCA_BF16) return -1;
     if (a.dev_scales)
-      hipLaunchKernelGGL(append_amax_kernel<128>, dim3((unsigned)a.H, 2), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(append_amax_kernel<128>, dim3((unsigned)a.H, 2), dim3(1024), 0, s, a);
     hipLaunchKernelGGL(append_fp8_kernel<128>, grid, dim3(256), 0, s, a, kv0);
     if (a.rope) hipLaunchKernelGGL((append_rope_k_kernel<128, true>), rgrid, dim3(128), 0, s, a, 1);
   } else {
