@@ -137,7 +137,9 @@ bca_status bca_cache_set_kv_scales(bca_cache* cache, int32_t layer, const float*
  * prerequisite "causal autoregression and KV cache"; WanToFight review, rolling
  * KV cache, updated after each chunk).
  * in_dtype: F32 for an F32 cache, BF16 for BF16 and FP8_E4M3 caches (quantised
- * on the fly with the layer's scales).
+ * on the fly with the layer's scales) and for FP8_E4M3_BLOCK caches (the
+ * block's per-head scales are first taken from this chunk, then it is
+ * quantised with them; no rotary form).
  * Ordering: per layer, ring chunk ids are non-decreasing; an id equal to the
  * last one re-writes that chunk in place; a smaller id returns
  * BCA_ERR_OUT_OF_ORDER. chunk_id >= 0. For is_ref the id is recorded only. */
@@ -170,7 +172,10 @@ size_t bca_attend_workspace_bytes(const bca_cache* cache, const bca_window_spec*
  * as two e4m3 terms (value and rounding residual), which keeps the result
  * within 5e-2 of attention over the stored K/V on data with 8-sigma outliers.
  * The K scale and the row's Q scale fold into the softmax scale, the V scale
- * into the output normalisation.
+ * into the output normalisation. FP8_E4M3_BLOCK: the current chunk is
+ * quantised with its own per-head scales, every visible block is padded to
+ * whole 64-key tiles so that each tile has one block's scales, and the
+ * workspace also holds the chunk's scales ([K|V][H] fp32).
  * Errors: BCA_ERR_OUT_OF_ORDER when a chunk of the window may already have been
  * overwritten (the layer's newest ring id >= t - W + S).
  * The visible set is resolved on the host from the slot table's chunk ids each
