@@ -324,7 +324,9 @@ bca_status bca_cache_slot_chunk(const bca_cache* cache, int32_t layer, int32_t s
 /* Declares the content of a slot without touching device memory, for callers
  * that filled the cache memory themselves (restoring a saved cache). Slot S
  * (with has_ref) is the reference block. chunk_id -1 empties the slot. The
- * layer's newest id is recomputed from the table. */
+ * layer's newest id is recomputed from the table. For an FP8_E4M3_BLOCK cache
+ * the block's scales (the table after the blocks) are part of what the
+ * caller restores. */
 bca_status bca_cache_set_slot_chunk(bca_cache* cache, int32_t layer, int32_t slot,
                                     int64_t chunk_id);
 
