@@ -457,3 +457,24 @@ def test_block_scaled_fp8_cache_on_the_host():
                             bca.bca_attend_rope_workspace_bytes(h, spec), 0)
     assert e.value.status == -4
     bca.bca_cache_destroy(h)
+
+
+def test_header_compiles_as_c99_and_links(tmp_path):
+    """include/bca.h is plain C: a C99 program using it compiles with warnings
+    as errors, links against libbca.so and makes host-only calls."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    exe = os.path.join(tmp_path, "abi_host_calls")
+    libdir = os.path.dirname(bca.LIB_PATH)
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic",
+           "-I", os.path.join(root, "include"), os.path.join(root, "tests", "c", "abi_host_calls.c"),
+           "-o", exe, "-L", libdir, "-l:libbca.so", "-Wl,-rpath," + libdir,
+           "-Wl,-rpath-link,/opt/rocm/lib", "-Wl,--allow-shlib-undefined"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "ok" in r.stdout, r.stdout + r.stderr
