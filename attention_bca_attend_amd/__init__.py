@@ -23,7 +23,7 @@ __all__ = [
     "bca_cache_slot_chunk", "bca_cache_set_slot_chunk", "bca_attend_plan", "bca_status_string",
     "bca_last_error", "bca_sequence_spec", "bca_attend_sequence_workspace_bytes",
     "bca_attend_sequence", "attend_sequence", "bca_append_chunk_dev",
-    "bca_chunk_counter_advance", "bca_attend_replayable", "Cache", "LIB_PATH", "load_library",
+    "bca_chunk_counter_advance", "bca_attend_replayable", "bca_attend_dev", "Cache", "LIB_PATH", "load_library",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbca.so")
@@ -124,6 +124,8 @@ def load_library(path: str = LIB_PATH):
     lib.bca_chunk_counter_advance.restype = I32
     lib.bca_attend_replayable.argtypes = [P, I32, spec_p, ctypes.POINTER(I32)]
     lib.bca_attend_replayable.restype = I32
+    lib.bca_attend_dev.argtypes = [P, I32, spec_p, P, P, P, P, I32, P, P, P, SZ, P]
+    lib.bca_attend_dev.restype = I32
     lib.bca_cache_slot_chunk.argtypes = [P, I32, I32, ctypes.POINTER(I64)]
     lib.bca_cache_slot_chunk.restype = I32
     lib.bca_cache_set_slot_chunk.argtypes = [P, I32, I32, I64]
@@ -302,6 +304,17 @@ def bca_attend_replayable(handle: int, layer: int, spec) -> bool:
     return bool(out.value)
 
 
+def bca_attend_dev(handle: int, layer: int, spec, d_q_chunk_id: int, q: int, k_cur: int,
+                   v_cur: int, qkv_dtype: int, o: int, lse: int, workspace: int,
+                   workspace_bytes: int, stream: int = 0) -> None:
+    _check(_lib.bca_attend_dev(ctypes.c_void_p(handle), layer, ctypes.byref(_spec(spec)),
+                               ctypes.c_void_p(d_q_chunk_id), ctypes.c_void_p(q),
+                               ctypes.c_void_p(k_cur), ctypes.c_void_p(v_cur), qkv_dtype,
+                               ctypes.c_void_p(o), ctypes.c_void_p(lse),
+                               ctypes.c_void_p(workspace), workspace_bytes,
+                               ctypes.c_void_p(stream)))
+
+
 def bca_cache_slot_chunk(handle: int, layer: int, slot: int) -> int:
     out = ctypes.c_int64()
     _check(_lib.bca_cache_slot_chunk(ctypes.c_void_p(handle), layer, slot, ctypes.byref(out)))
@@ -461,6 +474,20 @@ class Cache:
             raise BcaError(-1, "d_chunk_id must be an int64 device tensor")
         bca_append_chunk_dev(self.handle, layer, d_chunk_id.data_ptr(), k.data_ptr(),
                              v.data_ptr(), _DT[self.qkv_dtype], self._stream(stream))
+
+    def attend_dev(self, layer: int, d_q_chunk_id, q, k_cur, v_cur, spec, out, lse, workspace,
+                   stream=None):
+        """bca_attend_dev: the query chunk id is read from the int64 device tensor
+        d_q_chunk_id when the kernel runs; spec.q_chunk_id is the chunk the call
+        is made (or captured) for."""
+        import torch
+        self._check_qkv(q, k_cur, v_cur)
+        if d_q_chunk_id.dtype != torch.int64 or not d_q_chunk_id.is_cuda:
+            raise BcaError(-1, "d_q_chunk_id must be an int64 device tensor")
+        bca_attend_dev(self.handle, layer, spec, d_q_chunk_id.data_ptr(), q.data_ptr(),
+                       k_cur.data_ptr(), v_cur.data_ptr(), _DT[self.qkv_dtype], out.data_ptr(),
+                       lse.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                       self._stream(stream))
 
     @staticmethod
     def advance_counter(d_chunk_id, stream=None):

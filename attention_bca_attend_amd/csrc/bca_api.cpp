@@ -624,10 +624,30 @@ size_t rope_stage_bytes(const bca_cache_desc& d, int32_t qkv_dtype) {
 bca_status attend_impl(const bca_cache* c, int32_t layer, const bca_window_spec* s,
                        const void* q, const void* k_cur, const void* v_cur, int32_t qkv_dtype,
                        void* o, float* lse, void* workspace, size_t workspace_bytes,
-                       bca_stream_t stream, const RopeArg* rope) {
+                       bca_stream_t stream, const RopeArg* rope, const int64_t* dev_t = nullptr) {
   Plan p;
   bca_status st = make_plan(c, layer, s, qkv_dtype, p);
   if (st != BCA_OK) return st;
+  if (dev_t) {
+    // the chunk id comes from the device: only the bf16 ring path, with a ring
+    // that holds the S chunks before spec->q_chunk_id (then every later chunk
+    // of a consecutive stream sees W blocks, in slots the kernel derives)
+    if (c->d.kv_dtype != BCA_BF16)
+      return fail(BCA_ERR_UNSUPPORTED, "device-side chunk ids need a BF16 cache");
+    if (!aligned(dev_t, 8))
+      return fail(BCA_ERR_INVALID_ARG, "d_q_chunk_id must be 8-byte aligned");
+    const int S = c->d.ring_slots;
+    for (int sl = 0; sl < S; ++sl) {
+      const int64_t id = c->slot[(size_t)layer * S + sl];
+      if (id < s->q_chunk_id - S || id > s->q_chunk_id - 1)
+        return fail(BCA_ERR_INVALID_ARG,
+                    "ring slot %d holds chunk %lld, not one of the %d chunks before %lld", sl,
+                    (long long)id, S, (long long)s->q_chunk_id);
+    }
+    if (s->use_ref && !c->ref_valid[layer])
+      return fail(BCA_ERR_INVALID_ARG, "use_ref set but no reference chunk was appended");
+    p.devt = 1;
+  }
   if (!q || !k_cur || !v_cur || !o)
     return fail(BCA_ERR_INVALID_ARG, "q, k_cur, v_cur and o must not be NULL");
   if (!aligned(q, 16) || !aligned(k_cur, 16) || !aligned(v_cur, 16) || !aligned(o, 16) ||
@@ -704,6 +724,12 @@ bca_status attend_impl(const bca_cache* c, int32_t layer, const bca_window_spec*
   a.scale_log2 = (float)((double)s->scale * 1.4426950408889634);
   a.xcd_remap = (p.wgs % 8 == 0) ? 1 : 0;
   a.upc = p.units;  // one chunk
+  if (p.devt) {
+    a.dev_t = dev_t;
+    a.dev_W = s->history;
+    a.dev_S = d.ring_slots;
+    a.dev_ref = s->use_ref ? 1 : 0;
+  }
   a.nruns = p.nruns;
   for (int i = 0; i < p.nruns; ++i) a.runs[i] = p.runs[i];
   if (d.kv_dtype == BCA_FP8_E4M3)
@@ -913,6 +939,15 @@ bca_status bca_attend(const bca_cache* c, int32_t layer, const bca_window_spec* 
                       bca_stream_t stream) {
   return attend_impl(c, layer, s, q, k_cur, v_cur, qkv_dtype, o, lse, workspace,
                      workspace_bytes, stream, nullptr);
+}
+
+bca_status bca_attend_dev(const bca_cache* c, int32_t layer, const bca_window_spec* s,
+                          const int64_t* d_q_chunk_id, const void* q, const void* k_cur,
+                          const void* v_cur, int32_t qkv_dtype, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes, bca_stream_t stream) {
+  if (!d_q_chunk_id) return fail(BCA_ERR_INVALID_ARG, "d_q_chunk_id is NULL");
+  return attend_impl(c, layer, s, q, k_cur, v_cur, qkv_dtype, o, lse, workspace,
+                     workspace_bytes, stream, nullptr, d_q_chunk_id);
 }
 
 size_t bca_attend_rope_workspace_bytes(const bca_cache* c, const bca_window_spec* s) {

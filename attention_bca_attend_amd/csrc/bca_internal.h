@@ -52,6 +52,7 @@ inline TileShape tile_shape(Kern k) {
 struct Plan {
   Kern kern;
   int32_t seq;                      // 1: a bca_attend_sequence launch (token-major cache rows)
+  int32_t devt;                     // 1: visible slots derived on the device (bca_attend_dev)
   int32_t blk;                      // 1: FP8_E4M3_BLOCK cache (tiles aligned to blocks)
   int32_t tpb;                      // key tiles per block when blk
   int32_t nvis;                     // visible blocks, current included
@@ -97,6 +98,11 @@ struct AttnArgs {
   // o start chunk_elems elements further per chunk, lse chunk_lse floats, and
   // whose moving runs start chunk_rows rows further. upc = units otherwise.
   int32_t upc;
+  // Query chunk id read on the device (bca_attend_dev): the kernel derives
+  // the visible ring slots from *dev_t, W = dev_W and S = dev_S (the ring
+  // holding consecutive ids), plus the reference block when dev_ref.
+  const int64_t* dev_t;
+  int32_t dev_W, dev_S, dev_ref;
   int32_t chunk_rows;
   int64_t chunk_elems;
   int64_t chunk_lse;

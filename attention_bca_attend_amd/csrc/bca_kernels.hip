@@ -267,13 +267,57 @@ struct FetchRun {
   int shift;  // rows a moving run is displaced by (the unit's chunk in a batched launch)
 };
 
+// Runs of a launch whose visible slots the kernel derives itself
+// (bca_attend_dev): built once per work group in LDS.
+__shared__ Run dev_runs[4];
+__shared__ int dev_nruns;
+
+template <bool DEVT>
+__device__ __forceinline__ Run run_of(const AttnArgs& a, int ri) {
+  if constexpr (DEVT) return dev_runs[ri];
+  else return a.runs[ri];
+}
+template <bool DEVT>
+__device__ __forceinline__ int nruns_of(const AttnArgs& a) {
+  if constexpr (DEVT) return dev_nruns;
+  else return a.nruns;
+}
+
+// The visible ring slots of query chunk t = *a.dev_t when the ring holds
+// consecutive ids: chunks t-W .. t-1 sit in slots (t-W) mod S .. (t-1) mod S.
+// The runs are built as the host builds them (ascending physical blocks,
+// adjacent blocks merged, the reference block S last), so the launch
+// computes exactly what a host-planned call for the same chunk computes.
+__device__ __forceinline__ void build_dev_runs(const AttnArgs& a) {
+  const int64_t t = *a.dev_t;
+  const int S = a.dev_S, W = a.dev_W, n = a.n;
+  const int s0 = (int)((((t - W) % S) + S) % S);
+  int nr = 0, nb = 0;
+  auto add = [&](int b) {
+    if (nr > 0 && dev_runs[nr - 1].phys + dev_runs[nr - 1].len == b * n) {
+      dev_runs[nr - 1].len += n;
+    } else {
+      dev_runs[nr] = Run{nb * n, n, b * n, 0};
+      ++nr;
+    }
+    ++nb;
+  };
+  const int wrap = s0 + W - S;  // slots 0 .. wrap-1 when the window wraps
+  for (int b = 0; b < wrap; ++b) add(b);
+  for (int b = s0; b < s0 + W && b < S; ++b) add(b);
+  if (a.dev_ref) add(S);
+  dev_nruns = nr;
+}
+
+template <bool DEVT = false>
 __device__ __forceinline__ FetchRun fetch_run_at(const AttnArgs& a, int ri, int shift = 0) {
+  const Run R = run_of<DEVT>(a, ri);
   FetchRun f;
   f.ri = ri;
   f.shift = shift;
-  f.vstart = a.runs[ri].vstart;
-  f.vend = f.vstart + a.runs[ri].len;
-  f.phys = a.runs[ri].phys + (a.runs[ri].moves ? shift : 0);
+  f.vstart = R.vstart;
+  f.vend = f.vstart + R.len;
+  f.phys = R.phys + (R.moves ? shift : 0);
   return f;
 }
 
@@ -308,7 +352,7 @@ __device__ __forceinline__ FetchLane<D> fetch_lane(int wave, int lane, int rowb)
 // Wave w's load q fills the 1 KB of the stage at (w IPW + q) KB. SEQ: cache
 // rows are a token-major sequence (row pitch a.cache_row_elems); otherwise
 // the ring's head-major rows of d elements.
-template <int D, bool SEQ>
+template <int D, bool SEQ, bool DEVT>
 __device__ __forceinline__ void bf16_fetch_tile(const AttnArgs& a, const HeadSrc& ks,
                                                 const HeadSrc& vs, int tile, FetchRun& fr,
                                                 const FetchLane<D>& fl, unsigned char* stage,
@@ -318,7 +362,8 @@ __device__ __forceinline__ void bf16_fetch_tile(const AttnArgs& a, const HeadSrc
   unsigned char* vdst = kdst + C::TILE_BYTES;
   if (tile < a.cache_tiles) {
     const int j0 = tile * C::BN;
-    while (j0 >= fr.vend && fr.ri + 1 < a.nruns) fr = fetch_run_at(a, fr.ri + 1, fr.shift);
+    while (j0 >= fr.vend && fr.ri + 1 < nruns_of<DEVT>(a))
+      fr = fetch_run_at<DEVT>(a, fr.ri + 1, fr.shift);
     const int rowb = SEQ ? a.cache_row_elems * 2 : C::ROWB;
     if (j0 + C::BN <= fr.vend) {
       // the whole tile lies in one run
@@ -335,8 +380,8 @@ __device__ __forceinline__ void bf16_fetch_tile(const AttnArgs& a, const HeadSrc
       for (int q = 0; q < C::IPW; ++q) {
         const int j = j0 + fl.r[q];
         int phys = -1;
-        for (int rr = fr.ri; rr < a.nruns; ++rr) {
-          const Run R = a.runs[rr];
+        for (int rr = fr.ri; rr < nruns_of<DEVT>(a); ++rr) {
+          const Run R = run_of<DEVT>(a, rr);
           if (R.vstart >= j0 + C::BN) break;
           if (j >= R.vstart && j < R.vstart + R.len)
             phys = R.phys + (SEQ && R.moves ? fr.shift : 0) + j - R.vstart;
@@ -496,7 +541,9 @@ __device__ __forceinline__ void pp_softmax(PPState<D>& st, int lim, int hi, floa
 // SEQ: a launch of bca_attend_sequence (token-major cache rows, units of
 // several chunks); otherwise a ring-cache call, where that generality would
 // only cost scalar registers.
-template <int D, bool SEQ>
+// DEVT: a bca_attend_dev launch; the work group derives the visible slots
+// from the device-side chunk id first (build_dev_runs).
+template <int D, bool SEQ, bool DEVT>
 __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
   using C = Bf16Cfg<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::NSTAGE * C::STAGE];
@@ -529,6 +576,10 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
                  (ai & 1) * 8;
   }
   const FetchLane<D> fl = fetch_lane<D>(wave, lane, SEQ ? a.cache_row_elems * 2 : C::ROWB);
+  if constexpr (DEVT) {
+    if (tid == 0) build_dev_runs(a);
+    __syncthreads();
+  }
 
   while (it < it_end) {
     const int u = (int)(it / a.T);
@@ -546,9 +597,9 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
     const HeadSrc vsrc = head_src(a.vc, static_cast<const __bf16*>(a.vcur) + cel, a, h, D, 2, 2);
     const float c = a.scale_log2;  // base-2 softmax scale
 
-    FetchRun fr = fetch_run_at(a, 0, SEQ ? ci * a.chunk_rows : 0);
-    bf16_fetch_tile<D, SEQ>(a, ksrc, vsrc, t0, fr, fl, smem, wave);
-    if (nt > 1) bf16_fetch_tile<D, SEQ>(a, ksrc, vsrc, t0 + 1, fr, fl, smem + C::STAGE, wave);
+    FetchRun fr = fetch_run_at<DEVT>(a, 0, SEQ ? ci * a.chunk_rows : 0);
+    bf16_fetch_tile<D, SEQ, DEVT>(a, ksrc, vsrc, t0, fr, fl, smem, wave);
+    if (nt > 1) bf16_fetch_tile<D, SEQ, DEVT>(a, ksrc, vsrc, t0 + 1, fr, fl, smem + C::STAGE, wave);
 
     // Q^T fragments (B operand): lane holds query q0+l32, dims 16kk+8hi .. +7;
     // rows past the chunk read as zeros (out-of-range buffer offsets).
@@ -585,7 +636,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
     auto begin_phase = [&](int k) {
       const int r = k >> 1;
       if ((k & 1) == 0 && r + 2 < nt)
-        bf16_fetch_tile<D, SEQ>(a, ksrc, vsrc, t0 + r + 2, fr, fl, smem + ((r + 2) & 3) * C::STAGE,
+        bf16_fetch_tile<D, SEQ, DEVT>(a, ksrc, vsrc, t0 + r + 2, fr, fl, smem + ((r + 2) & 3) * C::STAGE,
                            wave);
     };
     auto end_phase = [&](int k) {
@@ -1776,9 +1827,11 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
   switch (p.kern) {
     case Kern::BF16:
       if (p.seq)
-        hipLaunchKernelGGL((attn_bf16_kernel<D, true>), dim3(p.wgs), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<D, true, false>), dim3(p.wgs), dim3(512), 0, s, a);
+      else if (p.devt)
+        hipLaunchKernelGGL((attn_bf16_kernel<D, false, true>), dim3(p.wgs), dim3(512), 0, s, a);
       else
-        hipLaunchKernelGGL((attn_bf16_kernel<D, false>), dim3(p.wgs), dim3(512), 0, s, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<D, false, false>), dim3(p.wgs), dim3(512), 0, s, a);
       break;
     case Kern::FP8:
       if constexpr (D == 128) {

@@ -315,6 +315,23 @@ bca_status bca_chunk_counter_advance(int64_t* d_chunk_id, bca_stream_t stream);
 bca_status bca_attend_replayable(const bca_cache* cache, int32_t layer,
                                  const bca_window_spec* spec, int32_t* replayable);
 
+/* bca_attend for windows smaller than the ring, replayable: the query chunk id
+ * is read from *d_q_chunk_id (device int64) when the kernel runs, and the
+ * kernel takes the visible ring slots from it: chunks t-W .. t-1 in slots
+ * (t-W) mod S .. (t-1) mod S, plus the reference block when use_ref. Valid
+ * while the ring holds consecutive ids, as a stream that appends every chunk
+ * in order keeps it (bca_append_chunk_dev with the same counter, advanced
+ * after the appends). spec->q_chunk_id is the chunk the call is made (or
+ * captured) for: the host plans with it and requires every ring slot to hold
+ * one of the S chunks before it. BF16 caches only (BCA_ERR_UNSUPPORTED
+ * otherwise); other arguments and errors as for bca_attend, plus
+ * BCA_ERR_INVALID_ARG for a NULL or misaligned d_q_chunk_id or a ring that
+ * does not hold the S chunks before spec->q_chunk_id. */
+bca_status bca_attend_dev(const bca_cache* cache, int32_t layer, const bca_window_spec* spec,
+                          const int64_t* d_q_chunk_id, const void* q, const void* k_cur,
+                          const void* v_cur, int32_t qkv_dtype, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes, bca_stream_t stream);
+
 /* Host-side slot table query: chunk id held by ring slot `slot` (0 <= slot < S)
  * of `layer`, -1 if empty. slot == S (with has_ref) reports the reference block
  * (its recorded id, or -1). */

@@ -478,3 +478,31 @@ def test_header_compiles_as_c99_and_links(tmp_path):
     assert r.returncode == 0, r.stdout + r.stderr
     r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and "ok" in r.stdout, r.stdout + r.stderr
+
+
+def test_attend_dev_validates_before_launch():
+    P = FAKE
+    h, _ = make(S=3, R=0, dt=bca.BF16, d=128, H=2, n=16)
+    spec = bca.bca_window_spec(3, 2, 0, 0, 0.1)
+    ws = bca.bca_attend_workspace_bytes(h, spec)
+    with pytest.raises(BcaError) as e:  # ring not yet holding chunks 0..2
+        bca.bca_attend_dev(h, 0, spec, P, P, P, P, bca.BF16, P, 0, P, ws, 0)
+    assert e.value.status == -1
+    for sl in range(3):
+        bca.bca_cache_set_slot_chunk(h, 0, sl, sl)
+    for ptr in (0, P + 4):
+        with pytest.raises(BcaError) as e:
+            bca.bca_attend_dev(h, 0, spec, ptr, P, P, P, bca.BF16, P, 0, P, ws, 0)
+        assert e.value.status == -1
+    assert ws > 0  # two units spread over the chip: split, so partials need room
+    with pytest.raises(BcaError) as e:  # the workspace checks of bca_attend still apply
+        bca.bca_attend_dev(h, 0, spec, P, P, P, P, bca.BF16, P, 0, P + 16, ws, 0)
+    assert e.value.status == -3
+    bca.bca_cache_destroy(h)
+    h8, _ = make(S=3, R=0, dt=bca.FP8_E4M3, d=128, H=2, n=16)
+    for sl in range(3):
+        bca.bca_cache_set_slot_chunk(h8, 0, sl, sl)
+    with pytest.raises(BcaError) as e:
+        bca.bca_attend_dev(h8, 0, spec, P, P, P, P, bca.BF16, P, 0, P, 1 << 30, 0)
+    assert e.value.status == -4
+    bca.bca_cache_destroy(h8)

@@ -143,3 +143,77 @@ def test_device_chunk_id_negative_writes_nothing():
     assert torch.equal(c.mem, ref.mem)
     assert np.array_equal(c.blocks(0)[0][:, 1].float().cpu().numpy(),
                           k.float().cpu().numpy().transpose(1, 0, 2))
+
+
+@pytest.mark.parametrize("L,H,d,n,S,W,R,G", [(2, 2, 128, 100, 3, 2, False, 0),
+                                             (2, 3, 64, 64, 4, 1, True, 2),
+                                             (1, 2, 128, 405, 20, 19, True, 4)])
+def test_replayed_step_with_window_smaller_than_ring(L, H, d, n, S, W, R, G):
+    """Windows smaller than the ring see different slots from chunk to chunk:
+    the captured attends read the chunk id from the device counter and take
+    the visible slots from it (bca_attend_dev). Every replay must equal a
+    host-planned bca_attend of the same chunk on a twin cache, bit for bit."""
+    import attention_bca_attend_amd as bca
+    log(f"graph replay, window {W} < ring {S}: L {L} H {H} d {d} n {n} R {R} G {G}")
+    A = bca.Cache(L, H, d, n, S, has_ref=R, kv_dtype="bf16")
+    B = bca.Cache(L, H, d, n, S, has_ref=R, kv_dtype="bf16")
+    A.mem.zero_()
+    B.mem.zero_()
+    for c in (A, B):
+        for l in range(L):
+            if R:
+                _, k, v = _chunk(n, H, d, l, 1000, False)
+                c.append_chunk(l, 0, k, v, is_ref=True)
+            for t in range(S):
+                _, k, v = _chunk(n, H, d, l, t, False)
+                c.append_chunk(l, t, k, v)
+    Q = [torch.empty((n, H, d), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    K = [torch.empty_like(Q[0]) for _ in range(L)]
+    V = [torch.empty_like(Q[0]) for _ in range(L)]
+    O = [torch.empty_like(Q[0]) for _ in range(L)]
+    LSE = [torch.empty((H, n), dtype=torch.float32, device="cuda") for _ in range(L)]
+    t0 = S
+    spec0 = A.spec(t0, W, use_ref=R, num_segments=G)
+    assert not A.replayable(0, spec0)  # a captured bca_attend would be wrong later
+    ws = A.workspace(spec0)
+    d_chunk = torch.full((1,), t0, dtype=torch.int64, device="cuda")
+    # code objects load on first launch: one eager run on a scratch cache first
+    scratch = bca.Cache(1, H, d, n, S, has_ref=R, kv_dtype="bf16")
+    for t in range(S):
+        _, k, v = _chunk(n, H, d, 0, t, False)
+        scratch.append_chunk(0, t, k, v)
+    if R:
+        scratch.append_chunk(0, 0, k, v, is_ref=True)
+    q, k, v = _chunk(n, H, d, 0, S, False)
+    scratch.attend_dev(0, d_chunk, q, k, v, spec0, O[0], LSE[0], ws)
+    torch.cuda.synchronize()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for l in range(L):
+            A.attend_dev(l, d_chunk, Q[l], K[l], V[l], spec0, O[l], LSE[l], ws)
+            A.append_chunk_dev(l, d_chunk, K[l], V[l])
+        bca.Cache.advance_counter(d_chunk)
+    torch.cuda.synchronize()
+
+    for t in range(t0, t0 + 2 * S + 3):
+        for l in range(L):
+            q, k, v = _chunk(n, H, d, l, t, False)
+            Q[l].copy_(q)
+            K[l].copy_(k)
+            V[l].copy_(v)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for l in range(L):
+            A.set_slot_chunk(l, t % S, t)
+        assert int(d_chunk.item()) == t + 1
+        spec = B.spec(t, W, use_ref=R, num_segments=G)
+        for l in range(L):
+            o, lse = B.attend(l, Q[l], K[l], V[l], spec)
+            torch.cuda.synchronize()
+            assert torch.equal(o, O[l]) and torch.equal(lse, LSE[l]), (t, l)
+            B.append_chunk(l, t, K[l], V[l])
+        torch.cuda.synchronize()
+        assert torch.equal(A.mem, B.mem), f"cache bytes differ after chunk {t}"
+    log(f"window {W} < ring {S}: chunks {t0}..{t} bit-identical to host-planned calls")
