@@ -632,8 +632,9 @@ bca_status attend_impl(const bca_cache* c, int32_t layer, const bca_window_spec*
     // the chunk id comes from the device: only the bf16 ring path, with a ring
     // that holds the S chunks before spec->q_chunk_id (then every later chunk
     // of a consecutive stream sees W blocks, in slots the kernel derives)
-    if (c->d.kv_dtype != BCA_BF16)
-      return fail(BCA_ERR_UNSUPPORTED, "device-side chunk ids need a BF16 cache");
+    if (c->d.kv_dtype != BCA_BF16 && c->d.kv_dtype != BCA_FP8_E4M3)
+      return fail(BCA_ERR_UNSUPPORTED,
+                  "device-side chunk ids need a BF16 or FP8_E4M3 (per-head scales) cache");
     if (!aligned(dev_t, 8))
       return fail(BCA_ERR_INVALID_ARG, "d_q_chunk_id must be 8-byte aligned");
     const int S = c->d.ring_slots;

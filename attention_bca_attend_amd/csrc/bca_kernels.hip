@@ -842,7 +842,7 @@ __device__ __forceinline__ F8Src f8_src(const AttnArgs& a, int h) {
   return f;
 }
 
-template <int D>
+template <int D, bool DEVT>
 __device__ __forceinline__ void f8_fetch_tile(const AttnArgs& a, const F8Src& src, int tile,
                                               FetchRun& fr, unsigned char* stage, int wave,
                                               int lane) {
@@ -854,15 +854,15 @@ __device__ __forceinline__ void f8_fetch_tile(const AttnArgs& a, const F8Src& sr
   unsigned char* vdst = kdst + C::TILE_BYTES;
   if (tile < a.cache_tiles) {
     const int j0 = tile * C::BN;
-    while (j0 >= fr.vend && fr.ri + 1 < a.nruns) fr = fetch_run_at(a, fr.ri + 1);
+    while (j0 >= fr.vend && fr.ri + 1 < nruns_of<DEVT>(a)) fr = fetch_run_at<DEVT>(a, fr.ri + 1);
     int phys;
     if (j0 + C::BN <= fr.vend) {
       phys = fr.phys + j0 - fr.vstart + r;
     } else {
       const int j = j0 + r;
       phys = -1;
-      for (int rr = fr.ri; rr < a.nruns; ++rr) {
-        const Run R = a.runs[rr];
+      for (int rr = fr.ri; rr < nruns_of<DEVT>(a); ++rr) {
+        const Run R = run_of<DEVT>(a, rr);
         if (R.vstart >= j0 + C::BN) break;
         if (j >= R.vstart && j < R.vstart + R.len) phys = R.phys + j - R.vstart;
       }
@@ -1028,7 +1028,7 @@ __device__ __forceinline__ void f8_softmax(F8State<D>& st, int lim, int hi, floa
 // multiplies the tile's softmax constant, and the V scale relative to the
 // unit's largest (s_ref) enters P as an exponent offset, with the row sum
 // corrected per tile and s_ref applied at normalisation.
-template <int D, bool BLK>
+template <int D, bool BLK, bool DEVT>
 __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
   using C = F8Cfg<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::NSTAGE * C::STAGE];
@@ -1064,6 +1064,10 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
       voff[db] = C::TILE_BYTES + key * C::ROWB + (((2 * db + g2) ^ f8_vswz(key)) << 4) + 8 * sx;
   }
 
+  if constexpr (DEVT) {
+    if (tid == 0) build_dev_runs(a);
+    __syncthreads();
+  }
   while (it < it_end) {
     const int u = (int)(it / a.T);
     const int t0 = (int)(it - (int64_t)u * a.T);
@@ -1074,10 +1078,10 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
     const int q0 = qt * C::BM + (wave & 7) * 32;
     const bool wave_rows = q0 < a.n;
 
-    FetchRun fr = fetch_run_at(a, 0);
+    FetchRun fr = fetch_run_at<DEVT>(a, 0);
     const F8Src src = f8_src<D>(a, h);
-    f8_fetch_tile<D>(a, src, t0, fr, smem, wave, lane);
-    if (nt > 1) f8_fetch_tile<D>(a, src, t0 + 1, fr, smem + C::STAGE, wave, lane);
+    f8_fetch_tile<D, DEVT>(a, src, t0, fr, smem, wave, lane);
+    if (nt > 1) f8_fetch_tile<D, DEVT>(a, src, t0 + 1, fr, smem + C::STAGE, wave, lane);
 
     // Q: lane holds row q0 + l32, dims 64 ks + 32 hi .. + 31 (bf16); rows
     // past the chunk read as zeros. Quantised with the row's scale amax/448.
@@ -1181,7 +1185,7 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
     // waiting for this wave's requests of tile q (read from phase 2q on).
     auto begin_phase = [&](int k) {
       if ((k & 1) == 0 && (k >> 1) + 2 < nt)
-        f8_fetch_tile<D>(a, src, t0 + (k >> 1) + 2, fr, smem + (((k >> 1) + 2) & 3) * C::STAGE,
+        f8_fetch_tile<D, DEVT>(a, src, t0 + (k >> 1) + 2, fr, smem + (((k >> 1) + 2) & 3) * C::STAGE,
                          wave, lane);
     };
     auto end_phase = [&](int k) {
@@ -1861,9 +1865,11 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(append_fp8_kernel<D>, dim3((unsigned)((total + 255) / 256), 2),
                            dim3(256), 0, s, q, 0);
         if (a.blk)
-          hipLaunchKernelGGL((attn_fp8_kernel<D, true>), dim3(p.wgs), dim3(512), 0, s, a);
+          hipLaunchKernelGGL((attn_fp8_kernel<D, true, false>), dim3(p.wgs), dim3(512), 0, s, a);
+        else if (p.devt)
+          hipLaunchKernelGGL((attn_fp8_kernel<D, false, true>), dim3(p.wgs), dim3(512), 0, s, a);
         else
-          hipLaunchKernelGGL((attn_fp8_kernel<D, false>), dim3(p.wgs), dim3(512), 0, s, a);
+          hipLaunchKernelGGL((attn_fp8_kernel<D, false, false>), dim3(p.wgs), dim3(512), 0, s, a);
       } else {
         return -1;
       }

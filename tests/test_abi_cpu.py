@@ -499,7 +499,7 @@ def test_attend_dev_validates_before_launch():
         bca.bca_attend_dev(h, 0, spec, P, P, P, P, bca.BF16, P, 0, P + 16, ws, 0)
     assert e.value.status == -3
     bca.bca_cache_destroy(h)
-    h8, _ = make(S=3, R=0, dt=bca.FP8_E4M3, d=128, H=2, n=16)
+    h8, _ = make(S=3, R=0, dt=bca.FP8_E4M3_BLOCK, d=128, H=2, n=16)
     for sl in range(3):
         bca.bca_cache_set_slot_chunk(h8, 0, sl, sl)
     with pytest.raises(BcaError) as e:

@@ -145,27 +145,31 @@ def test_device_chunk_id_negative_writes_nothing():
                           k.float().cpu().numpy().transpose(1, 0, 2))
 
 
-@pytest.mark.parametrize("L,H,d,n,S,W,R,G", [(2, 2, 128, 100, 3, 2, False, 0),
-                                             (2, 3, 64, 64, 4, 1, True, 2),
-                                             (1, 2, 128, 405, 20, 19, True, 4)])
-def test_replayed_step_with_window_smaller_than_ring(L, H, d, n, S, W, R, G):
+@pytest.mark.parametrize("kv,L,H,d,n,S,W,R,G", [("bf16", 2, 2, 128, 100, 3, 2, False, 0),
+                                                ("bf16", 2, 3, 64, 64, 4, 1, True, 2),
+                                                ("bf16", 1, 2, 128, 405, 20, 19, True, 4),
+                                                ("fp8", 2, 2, 128, 96, 3, 2, True, 0)])
+def test_replayed_step_with_window_smaller_than_ring(kv, L, H, d, n, S, W, R, G):
     """Windows smaller than the ring see different slots from chunk to chunk:
     the captured attends read the chunk id from the device counter and take
     the visible slots from it (bca_attend_dev). Every replay must equal a
     host-planned bca_attend of the same chunk on a twin cache, bit for bit."""
     import attention_bca_attend_amd as bca
-    log(f"graph replay, window {W} < ring {S}: L {L} H {H} d {d} n {n} R {R} G {G}")
-    A = bca.Cache(L, H, d, n, S, has_ref=R, kv_dtype="bf16")
-    B = bca.Cache(L, H, d, n, S, has_ref=R, kv_dtype="bf16")
+    log(f"graph replay, window {W} < ring {S}: {kv} L {L} H {H} d {d} n {n} R {R} G {G}")
+    fp8 = kv == "fp8"
+    A = bca.Cache(L, H, d, n, S, has_ref=R, kv_dtype=kv)
+    B = bca.Cache(L, H, d, n, S, has_ref=R, kv_dtype=kv)
     A.mem.zero_()
     B.mem.zero_()
     for c in (A, B):
         for l in range(L):
+            if fp8:
+                c.set_kv_scales(l, [8.0 / 448.0] * H, [8.0 / 448.0] * H)
             if R:
-                _, k, v = _chunk(n, H, d, l, 1000, False)
+                _, k, v = _chunk(n, H, d, l, 1000, fp8)
                 c.append_chunk(l, 0, k, v, is_ref=True)
             for t in range(S):
-                _, k, v = _chunk(n, H, d, l, t, False)
+                _, k, v = _chunk(n, H, d, l, t, fp8)
                 c.append_chunk(l, t, k, v)
     Q = [torch.empty((n, H, d), dtype=torch.bfloat16, device="cuda") for _ in range(L)]
     K = [torch.empty_like(Q[0]) for _ in range(L)]
@@ -178,7 +182,9 @@ def test_replayed_step_with_window_smaller_than_ring(L, H, d, n, S, W, R, G):
     ws = A.workspace(spec0)
     d_chunk = torch.full((1,), t0, dtype=torch.int64, device="cuda")
     # code objects load on first launch: one eager run on a scratch cache first
-    scratch = bca.Cache(1, H, d, n, S, has_ref=R, kv_dtype="bf16")
+    scratch = bca.Cache(1, H, d, n, S, has_ref=R, kv_dtype=kv)
+    if fp8:
+        scratch.set_kv_scales(0, [8.0 / 448.0] * H, [8.0 / 448.0] * H)
     for t in range(S):
         _, k, v = _chunk(n, H, d, 0, t, False)
         scratch.append_chunk(0, t, k, v)
@@ -198,7 +204,7 @@ def test_replayed_step_with_window_smaller_than_ring(L, H, d, n, S, W, R, G):
 
     for t in range(t0, t0 + 2 * S + 3):
         for l in range(L):
-            q, k, v = _chunk(n, H, d, l, t, False)
+            q, k, v = _chunk(n, H, d, l, t, fp8)
             Q[l].copy_(q)
             K[l].copy_(k)
             V[l].copy_(v)
