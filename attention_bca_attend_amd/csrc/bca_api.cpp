@@ -559,7 +559,8 @@ bca_status bca_attend_replayable(const bca_cache* c, int32_t layer, const bca_wi
   bool ok = s->history >= S && (!s->use_ref || c->ref_valid[layer]);
   for (int sl = 0; ok && sl < S; ++sl) {
     const int64_t id = c->slot[(size_t)layer * S + sl];
-    ok = id >= t - S && id <= t - 1;
+    // an empty slot (-1) never qualifies, also when t < S makes t - S negative
+    ok = id >= 0 && id >= t - S && id <= t - 1;
   }
   *replayable = ok ? 1 : 0;
   g_err.clear();
@@ -640,7 +641,8 @@ bca_status attend_impl(const bca_cache* c, int32_t layer, const bca_window_spec*
     const int S = c->d.ring_slots;
     for (int sl = 0; sl < S; ++sl) {
       const int64_t id = c->slot[(size_t)layer * S + sl];
-      if (id < s->q_chunk_id - S || id > s->q_chunk_id - 1)
+      // empty slots (-1) are refused too: with t < S, t - S is negative
+      if (id < 0 || id < s->q_chunk_id - S || id > s->q_chunk_id - 1)
         return fail(BCA_ERR_INVALID_ARG,
                     "ring slot %d holds chunk %lld, not one of the %d chunks before %lld", sl,
                     (long long)id, S, (long long)s->q_chunk_id);

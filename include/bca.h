@@ -296,8 +296,8 @@ bca_status bca_attend_sequence(const bca_sequence_spec* spec, const void* q, con
  * bca_attend_replayable: sets *replayable to 1 when a bca_attend of this spec
  * captured now stays right for every later chunk of a stream that appends
  * consecutive ids: the window covers the whole ring (history >= S), every
- * ring slot holds one of the chunks t-S .. t-1, and a requested reference is
- * present. The plan (visible blocks, tiles, work groups) is then the same
+ * ring slot holds one of the chunks t-S .. t-1 (so an empty slot, and with it
+ * any t < S, gives 0), and a requested reference is present. The plan (visible blocks, tiles, work groups) is then the same
  * for every such chunk, and the captured launch reads whatever the slots hold
  * when it runs. Otherwise 0 (a smaller window sees different slots from
  * chunk to chunk). Errors as for bca_attend's checks of cache, layer and spec.
@@ -323,7 +323,7 @@ bca_status bca_attend_replayable(const bca_cache* cache, int32_t layer,
  * in order keeps it (bca_append_chunk_dev with the same counter, advanced
  * after the appends). spec->q_chunk_id is the chunk the call is made (or
  * captured) for: the host plans with it and requires every ring slot to hold
- * one of the S chunks before it. BF16 and FP8_E4M3 caches
+ * one of the S chunks before it (no slot empty, hence t >= S). BF16 and FP8_E4M3 caches
  * (BCA_ERR_UNSUPPORTED for the others); other arguments and errors as for bca_attend, plus
  * BCA_ERR_INVALID_ARG for a NULL or misaligned d_q_chunk_id or a ring that
  * does not hold the S chunks before spec->q_chunk_id. */

@@ -418,6 +418,32 @@ def test_attend_replayable_rule():
     bca.bca_cache_destroy(h)
 
 
+def test_replay_guards_refuse_empty_slots_at_the_stream_start():
+    # With t < S the lower bound t - S is negative, so an empty slot (-1) must
+    # be refused on its own: a plan captured there would hold fewer blocks
+    # than every later chunk sees.
+    h, _ = make(S=2, R=0, dt=bca.BF16, d=128, H=2, n=16)
+    spec = lambda t, W: bca.bca_window_spec(t, W, 0, 0, 0.1)  # noqa: E731
+    assert not bca.bca_attend_replayable(h, 0, spec(0, 2))  # empty ring, t = 0
+    assert not bca.bca_attend_replayable(h, 0, spec(1, 2))  # empty ring, t = 1
+    bca.bca_cache_set_slot_chunk(h, 0, 0, 0)
+    assert not bca.bca_attend_replayable(h, 0, spec(1, 2))  # slot 1 still empty
+    bca.bca_cache_set_slot_chunk(h, 0, 1, 1)
+    assert bca.bca_attend_replayable(h, 0, spec(2, 2))
+    bca.bca_cache_destroy(h)
+    P = FAKE
+    h, _ = make(S=3, R=0, dt=bca.BF16, d=128, H=2, n=16)
+    for t, filled in ((0, 0), (1, 0), (1, 1), (2, 2)):
+        for sl in range(3):
+            bca.bca_cache_set_slot_chunk(h, 0, sl, sl if sl < filled else -1)
+        sp = bca.bca_window_spec(t, 2, 0, 0, 0.1)
+        ws = bca.bca_attend_workspace_bytes(h, sp)
+        with pytest.raises(BcaError) as e:
+            bca.bca_attend_dev(h, 0, sp, P, P, P, P, bca.BF16, P, 0, P, ws, 0)
+        assert e.value.status == -1, (t, filled)
+    bca.bca_cache_destroy(h)
+
+
 def test_descriptor_limits_of_32_bit_offsets():
     # one head's cache blocks: (S+R) * n * d * es bytes must stay below 2 GiB
     over = bca.bca_cache_desc(1, 1, 128, 140000, 62, 0, bca.BF16)  # 62 * 140000 * 256 B ≈ 2.22 GB
