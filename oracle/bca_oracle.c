@@ -42,6 +42,7 @@
  *    the block-causal mask, only by the split test's empty pieces) gets O = 0,
  *    LSE = -inf, and an -inf piece gets weight 0 in the merge.
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -178,12 +179,32 @@ static void sort_by_id(int* idx, int count, const int64_t* ids) {
  *   3-4. bca_oracle_attend_masked (scores of admitted keys, two-pass softmax).
  * Returns 0, or a negative value on a bad argument.
  */
+int bca_oracle_attend_rows(int H, int d, int n, int nq, int n_hist, const int64_t* hist_ids,
+                           const double* hist_k, const double* hist_v, int has_ref,
+                           const double* ref_k, const double* ref_v, const double* q,
+                           const double* k_cur, const double* v_cur, int64_t t, int W,
+                           int use_ref, double scale, int literal, double* o, double* lse);
+
 int bca_oracle_attend(int H, int d, int n, int n_hist, const int64_t* hist_ids,
                       const double* hist_k, const double* hist_v, int has_ref,
                       const double* ref_k, const double* ref_v, const double* q,
                       const double* k_cur, const double* v_cur, int64_t t, int W, int use_ref,
                       double scale, int literal, double* o, double* lse) {
-  if (H < 1 || d < 1 || n < 1 || n_hist < 0 || W < 0 || t < 0) return -1;
+  return bca_oracle_attend_rows(H, d, n, n, n_hist, hist_ids, hist_k, hist_v, has_ref, ref_k,
+                                ref_v, q, k_cur, v_cur, t, W, use_ref, scale, literal, o, lse);
+}
+
+/*
+ * The same for nq query rows of chunk t (any subset of its n rows, q
+ * [nq][H][d], o [nq][H][d], lse [H][nq]): every row of a chunk sees the same
+ * keys, so the mask has nq identical rows.
+ */
+int bca_oracle_attend_rows(int H, int d, int n, int nq, int n_hist, const int64_t* hist_ids,
+                           const double* hist_k, const double* hist_v, int has_ref,
+                           const double* ref_k, const double* ref_v, const double* q,
+                           const double* k_cur, const double* v_cur, int64_t t, int W,
+                           int use_ref, double scale, int literal, double* o, double* lse) {
+  if (H < 1 || d < 1 || n < 1 || nq < 1 || n_hist < 0 || W < 0 || t < 0) return -1;
   for (int a = 0; a < n_hist; ++a)
     if (hist_ids[a] < 0) return -1;
   int with_ref = (use_ref && has_ref) ? 1 : 0;
@@ -196,7 +217,7 @@ int bca_oracle_attend(int H, int d, int n, int n_hist, const int64_t* hist_ids,
   int64_t* block_id = (int64_t*)malloc(sizeof(int64_t) * nblocks);
   double* K = (double*)malloc(sizeof(double) * (size_t)nk * row);
   double* V = (double*)malloc(sizeof(double) * (size_t)nk * row);
-  uint8_t* M = (uint8_t*)malloc((size_t)n * nk);
+  uint8_t* M = (uint8_t*)malloc((size_t)nq * nk);
   if (!order || !block_id || !K || !V || !M) {
     free(order), free(block_id), free(K), free(V), free(M);
     return -2;
@@ -221,11 +242,11 @@ int bca_oracle_attend(int H, int d, int n, int n_hist, const int64_t* hist_ids,
   block_id[b++] = ORACLE_CUR_ID;
 
   /* step 2: the dense mask, one byte per (query row, key) */
-  for (int i = 0; i < n; ++i)
+  for (int i = 0; i < nq; ++i)
     for (int j = 0; j < nk; ++j) M[(size_t)i * nk + j] = (uint8_t)visible(block_id[j / n], t, W);
 
   /* steps 3-4 */
-  int rc = bca_oracle_attend_masked(n, nk, H, d, q, K, V, M, scale, literal, o, lse);
+  int rc = bca_oracle_attend_masked(nq, nk, H, d, q, K, V, M, scale, literal, o, lse);
   free(order), free(block_id), free(K), free(V), free(M);
   return rc;
 }
@@ -384,6 +405,52 @@ void bca_oracle_quant_e4m3(const float* x, long count, float scale, uint8_t* out
   for (long i = 0; i < count; ++i) {
     float y = x[i] / scale;
     out[i] = bca_oracle_e4m3_encode(y);
+  }
+}
+
+/*
+ * Per-interval scale of an 8-bit cache block [MG4 technical novelty: the
+ * window is held as intervals of 8-bit K/V, and only the interval that
+ * changed is re-quantised]. The pages fix neither the interval nor the rule;
+ * the reading: an interval is one cache block (a chunk), and its scale per
+ * head is the largest magnitude of the chunk's values in that head divided by
+ * the largest code (448 for e4m3, 127 for int8), in single precision; 1 when
+ * that maximum is 0 or not finite. x is [n][H][d] (fp32 values); out[H].
+ */
+void bca_oracle_block_scales(const float* x, int n, int H, int d, float qmax, float* out) {
+  for (int h = 0; h < H; ++h) {
+    float a = 0.0f;
+    for (int r = 0; r < n; ++r)
+      for (int j = 0; j < d; ++j) {
+        float v = fabsf(x[((size_t)r * H + h) * d + j]);
+        if (v > a || v != v) a = v;
+      }
+    out[h] = (a > 0.0f && a <= FLT_MAX) ? a / qmax : 1.0f;
+  }
+}
+
+/*
+ * Symmetric int8 code of a value with one scale [MG4 technical novelty: INT8
+ * keys]: code = round to nearest even of fp32(x / scale), clamped to
+ * [-127, 127] (the code -128 is never produced, so the range is symmetric);
+ * NaN gives 0. The value a code stands for is code * scale.
+ */
+void bca_oracle_quant_int8(const float* x, long count, float scale, int8_t* out) {
+#pragma omp parallel for schedule(static)
+  for (long i = 0; i < count; ++i) {
+    float y = x[i] / scale;
+    if (y != y) {
+      out[i] = 0;
+      continue;
+    }
+    if (y > 127.0f) y = 127.0f;
+    if (y < -127.0f) y = -127.0f;
+    /* round half to even, written out: nearest integer below, then compare
+       the remainder with one half */
+    double f = floor((double)y), rem = (double)y - f;
+    long q = (long)f;
+    if (rem > 0.5 || (rem == 0.5 && (q & 1))) q += 1;
+    out[i] = (int8_t)q;
   }
 }
 

@@ -56,6 +56,11 @@ class OracleLib:
                                            ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                            ctypes.c_double, ctypes.c_int, P, P])
         lib.bca_oracle_attend.restype = ctypes.c_int
+        lib.bca_oracle_attend_rows.argtypes = ([ctypes.c_int] * 5 +
+                                               [P, P, P, ctypes.c_int, P, P, P, P, P,
+                                                ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_double, ctypes.c_int, P, P])
+        lib.bca_oracle_attend_rows.restype = ctypes.c_int
         lib.bca_oracle_lse_merge.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P,
                                              P, P]
         lib.bca_oracle_lse_merge.restype = ctypes.c_int
@@ -65,6 +70,11 @@ class OracleLib:
         lib.bca_oracle_e4m3_encode.restype = ctypes.c_uint8
         lib.bca_oracle_quant_e4m3.argtypes = [P, ctypes.c_long, ctypes.c_float, P]
         lib.bca_oracle_quant_e4m3.restype = None
+        lib.bca_oracle_block_scales.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_float, P]
+        lib.bca_oracle_block_scales.restype = None
+        lib.bca_oracle_quant_int8.argtypes = [P, ctypes.c_long, ctypes.c_float, P]
+        lib.bca_oracle_quant_int8.restype = None
         lib.bca_oracle_threads.argtypes = []
         lib.bca_oracle_threads.restype = ctypes.c_int
         lib.bca_oracle_set_threads.argtypes = [ctypes.c_int]
@@ -105,14 +115,20 @@ class OracleLib:
         return o, lse
 
     def attend(self, q, k_cur, v_cur, history: dict, t: int, W: int, scale: float, ref=None,
-               use_ref: bool = False, literal: bool = False):
+               use_ref: bool = False, literal: bool = False, rows=None):
         """Block-causal attention of query chunk ``t``.
 
         history: {chunk_id: (k, v)} with every committed chunk (k, v [n][H][d]);
-        ref: (k, v) of the reference chunk or None. Returns (o [n][H][d], lse [H][n]).
+        ref: (k, v) of the reference chunk or None. Returns (o [n][H][d], lse [H][n]);
+        with ``rows`` (indices into the chunk's n query rows) only those rows:
+        (o [len(rows)][H][d], lse [H][len(rows)]).
         """
         q, k_cur, v_cur = _f64(q), _f64(k_cur), _f64(v_cur)
-        n, H, d = q.shape
+        n, H, d = k_cur.shape
+        if rows is not None:
+            q = np.ascontiguousarray(q[np.asarray(rows)])
+        nq = q.shape[0]
+        assert q.shape[1:] == (H, d)
         ids = sorted(history.keys())
         nh = len(ids)
         hid = np.array(ids, dtype=np.int64) if nh else np.zeros(1, dtype=np.int64)
@@ -125,12 +141,13 @@ class OracleLib:
         has_ref = ref is not None
         rk = _f64(ref[0]) if has_ref else np.zeros(1, dtype=np.float64)
         rv = _f64(ref[1]) if has_ref else np.zeros(1, dtype=np.float64)
-        o = np.empty((n, H, d), dtype=np.float64)
-        lse = np.empty((H, n), dtype=np.float64)
-        rc = self.lib.bca_oracle_attend(H, d, n, nh, _ptr(hid), _ptr(hk), _ptr(hv),
-                                        int(has_ref), _ptr(rk), _ptr(rv), _ptr(q), _ptr(k_cur),
-                                        _ptr(v_cur), int(t), int(W), int(bool(use_ref)),
-                                        float(scale), int(bool(literal)), _ptr(o), _ptr(lse))
+        o = np.empty((nq, H, d), dtype=np.float64)
+        lse = np.empty((H, nq), dtype=np.float64)
+        rc = self.lib.bca_oracle_attend_rows(H, d, n, nq, nh, _ptr(hid), _ptr(hk), _ptr(hv),
+                                             int(has_ref), _ptr(rk), _ptr(rv), _ptr(q),
+                                             _ptr(k_cur), _ptr(v_cur), int(t), int(W),
+                                             int(bool(use_ref)), float(scale),
+                                             int(bool(literal)), _ptr(o), _ptr(lse))
         if rc != 0:
             raise RuntimeError(f"bca_oracle_attend failed ({rc})")
         return o, lse
@@ -192,6 +209,22 @@ class OracleLib:
         self.lib.bca_oracle_quant_e4m3(_ptr(a), a.size, float(scale), _ptr(out))
         return out
 
+    def block_scales(self, x, qmax: float = 448.0) -> np.ndarray:
+        """Per-head scales of a cache block x [n][H][d]: fp32 max |x| / qmax
+        (1 when the maximum is 0 or not finite), float32 [H]."""
+        a = np.ascontiguousarray(x, dtype=np.float32)
+        n, H, d = a.shape
+        out = np.empty(H, dtype=np.float32)
+        self.lib.bca_oracle_block_scales(_ptr(a), n, H, d, float(qmax), _ptr(out))
+        return out
+
+    def quant_int8(self, x, scale: float) -> np.ndarray:
+        """int8 codes clamp(rne(fp32(x / scale)), -127, 127) for a float32 array."""
+        a = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty(a.shape, dtype=np.int8)
+        self.lib.bca_oracle_quant_int8(_ptr(a), a.size, float(scale), _ptr(out))
+        return out
+
 
 _default = None
 
@@ -243,3 +276,11 @@ def attend_sequence(*a, **k):
 
 def quant_e4m3(*a, **k):
     return default().quant_e4m3(*a, **k)
+
+
+def block_scales(*a, **k):
+    return default().block_scales(*a, **k)
+
+
+def quant_int8(*a, **k):
+    return default().quant_int8(*a, **k)

@@ -134,6 +134,22 @@ def tensor(shape, *ids: int, dtype: str = "bf16", scale: float = 1.0,
     return out.reshape(shape)
 
 
+def tensor_rows(shape, rows, *ids: int, dtype: str = "bf16", seed: int = BASE_SEED) -> np.ndarray:
+    """Rows ``rows`` (indices along the first axis) of ``tensor(shape, *ids)``
+    without outliers, drawing only their counters: row r of a [R][...] tensor
+    holds elements r*m .. r*m + m - 1 (m = product of the other axes), i.e.
+    uniform draws 2 r m .. 2 (r + 1) m - 1 of the stream."""
+    m = int(np.prod(shape[1:]))
+    key = stream_key(*ids, seed=seed)
+    out = np.empty((len(rows),) + tuple(shape[1:]), dtype=np.float32)
+    for i, r in enumerate(rows):
+        u = uniform(key, 2 * m, start=2 * int(r) * m)
+        z = np.sqrt(-2.0 * np.log1p(-u[0::2])) * np.cos(2.0 * np.pi * u[1::2])
+        x = round_fp32(z) if dtype == "fp32" else round_bf16(z)
+        out[i] = x.reshape(shape[1:])
+    return out
+
+
 def qkv(n: int, H: int, d: int, layer: int, chunk: int, step: int, dtype: str = "bf16",
         outlier_frac: float = 0.0, seed: int = BASE_SEED):
     """Q, K, V of one chunk of one layer at one denoise step, each [n][H][d].

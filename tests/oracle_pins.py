@@ -328,6 +328,80 @@ def pin_e4m3_codec(lib):
     assert np.array_equal(q, lib.e4m3_encode((x / 60.0).astype(np.float32) / s))
 
 
+def pin_row_subset(lib):
+    """Every query row of a chunk sees the same keys, so the oracle on a subset
+    of the rows gives exactly those rows of the full result."""
+    n, H, d = 12, 2, 8
+    hist = _chunks(n, H, d, 3, 60)
+    k, v = _chunks(n, H, d, 1, 61)[0]
+    q = synth.tensor((n, H, d), synth.TAG_Q, 62, dtype="fp32").astype(np.float64)
+    full_o, full_l = lib.attend(q, k, v, hist, t=3, W=2, scale=0.3)
+    rows = [0, 5, 11, 7]
+    o, l = lib.attend(q, k, v, hist, t=3, W=2, scale=0.3, rows=rows)
+    assert np.array_equal(o, full_o[rows]) and np.array_equal(l, full_l[:, rows])
+
+
+def pin_block_scales(lib):
+    """Per-interval scale rule of an 8-bit cache block: per head, the largest
+    magnitude over the block's rows and dims divided by the largest code, in
+    single precision; 1 for a maximum of 0, infinity or NaN."""
+    x = np.zeros((5, 4, 3), dtype=np.float32)
+    x[2, 0, 1] = -7.0           # head 0: largest magnitude 7 (negative)
+    x[4, 1, 2] = 448.0          # head 1: 448
+    x[0, 1, 0] = 100.0
+    x[3, 3, 0] = np.inf         # head 3: not finite; head 2 stays all zero
+    s = lib.block_scales(x)
+    assert s.dtype == np.float32 and s.shape == (4,)
+    assert s[0] == np.float32(2.0 ** -6) and s[1] == 1.0 and s[2] == 1.0 and s[3] == 1.0, s
+    x[3, 3, 0] = np.nan
+    assert lib.block_scales(x)[3] == 1.0
+    assert lib.block_scales(x, qmax=127.0)[0] == np.float32(7.0) / np.float32(127.0)
+    # one head's maximum never leaks into another head's scale
+    y = synth.tensor((16, 3, 8), synth.TAG_MISC, 40, dtype="fp32")
+    y[:, 1, :] *= 50.0
+    sy = lib.block_scales(y)
+    for h in range(3):
+        assert sy[h] == np.float32(np.abs(y[:, h, :]).max()) / np.float32(448.0), h
+    # exact under powers of two
+    for k in (-3, 5):
+        assert np.array_equal(lib.block_scales(y * np.float32(2.0 ** k)),
+                              sy * np.float32(2.0 ** k))
+    # quantising with its own scale puts the largest magnitude on the largest
+    # code (448) and nothing beyond
+    for h in range(3):
+        codes = lib.quant_e4m3(y[:, h, :], float(sy[h]))
+        vals = np.abs(lib.e4m3_decode(codes.reshape(-1)))
+        assert vals.max() == 448.0 and np.all(vals <= 448.0), h
+
+
+def pin_int8_codec(lib):
+    """Symmetric int8 codes: round to nearest even of fp32(x / scale), clamped
+    to [-127, 127]; NaN gives 0."""
+    c = np.arange(-127, 128, dtype=np.float32)
+    assert np.array_equal(lib.quant_int8(c, 1.0), c.astype(np.int8))  # every code round-trips
+    s = np.float32(0.0625)
+    assert np.array_equal(lib.quant_int8(c * s, float(s)), c.astype(np.int8))
+    # ties go to the even neighbour
+    half = np.arange(-128, 127, dtype=np.float32) + np.float32(0.5)
+    want = np.where(np.floor(half) % 2 == 0, np.floor(half), np.floor(half) + 1)
+    want = np.clip(want, -127, 127)
+    assert np.array_equal(lib.quant_int8(half, 1.0), want.astype(np.int8))
+    # off-tie values go to the nearest integer
+    for x, q in ((0.49, 0), (0.51, 1), (-0.51, -1), (2.4999, 2), (-2.5001, -3)):
+        assert lib.quant_int8(np.array([x], np.float32), 1.0)[0] == q, x
+    # clamping and NaN
+    for x, q in ((127.4, 127), (127.5, 127), (300.0, 127), (-300.0, -127), (np.inf, 127),
+                 (-np.inf, -127), (np.nan, 0)):
+        assert lib.quant_int8(np.array([x], np.float32), 1.0)[0] == q, x
+    # the division is in single precision: 1 / fp32(0.3) = 3.3333333 -> 3
+    assert lib.quant_int8(np.array([1.0], np.float32), float(np.float32(0.3)))[0] == 3
+    z = synth.tensor((3000,), synth.TAG_MISC, 41, dtype="fp32", scale=3.0)
+    sc = np.float32(np.abs(z).max()) / np.float32(127.0)
+    q = lib.quant_int8(z, float(sc)).astype(np.float64)
+    assert np.abs(q).max() == 127.0
+    assert np.all(np.abs(q * float(sc) - z) <= float(sc) / 2 * (1 + 1e-6))
+
+
 def pin_rope(lib):
     """Rotary embedding: position 0 is the identity, every pair keeps its
     length, rotations compose (position a then b equals a + b), query-key
@@ -465,5 +539,6 @@ def pin_sequence_q_zero_and_invariance(lib):
 ALL_PINS = [pin_hand_cases, pin_q_zero_closed_form, pin_one_hot_probe, pin_window_invariance,
             pin_split_merge, pin_merge_closed_forms, pin_constant_and_affine_v,
             pin_reduces_to_library_attention, pin_token_level_sliding_window, pin_large_logits,
-            pin_e4m3_codec, pin_rope, pin_sequence_reduces_to_library_attention,
+            pin_e4m3_codec, pin_row_subset, pin_block_scales, pin_int8_codec, pin_rope,
+            pin_sequence_reduces_to_library_attention,
             pin_sequence_matches_chunk_by_chunk, pin_sequence_q_zero_and_invariance]

@@ -2,10 +2,12 @@
 appended chunk (FP8_E4M3_BLOCK) against the CPU oracle.
 
 Bars: the scale table and the codes an append writes are bit-exact against
-the rule written out on the CPU (fp32 max |x| / 448; the oracle's e4m3
-quantiser); attention is held to the fp8 bar (5e-2) against the oracle run
-on exactly what the cache holds, the current chunk quantised by the same
-rule with its own scales.
+the oracle's rule (oracle.block_scales: fp32 max |x| / 448) and e4m3
+quantiser; attention is held to the oracle run on exactly what the cache
+holds (the current chunk quantised by the same rule with its own scales),
+and to the oracle on the unquantised seeded inputs: at the Matrix-Game size
+at the benchmark spec's 5e-2, on small shapes at the quantisation's own error
+plus the kernel's bar (bca_harness.assert_fp8).
 """
 import math
 
@@ -13,7 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
-from bca_harness import TOL, Sequence, assert_close, block_scales_of, log, to_dev
+from bca_harness import Sequence, assert_fp8, log, to_dev
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -54,7 +56,7 @@ def test_block_append_scales_and_codes_exact():
         latest[blk] = (k, v)  # later appends overwrite the slot
     for blk, (k, v) in latest.items():
         for x, codes, scales in ((k, K, KS), (v, V, VS)):
-            want_s = block_scales_of(x)
+            want_s = oracle.block_scales(x)
             got_s = scales[blk].cpu().numpy()
             assert np.array_equal(got_s, want_s), (blk, got_s, want_s)
             got = codes[:, blk].cpu().numpy()  # [H][n][d]
@@ -64,11 +66,12 @@ def test_block_append_scales_and_codes_exact():
     log("fp8 block: scale table and codes bit-exact for every block")
 
 
-@pytest.mark.parametrize("G", [0, 1, 3])
-def test_block_sequence(G):
+@pytest.mark.parametrize("G,outliers", [(0, True), (1, True), (3, True), (0, False)])
+def test_block_sequence(G, outliers):
     H, d, n, S, W = 4, 128, 100, 3, 2
     cache = new_cache(1, H, d, n, S, R=True)
-    seq = Sequence(cache, H, d, n, "fp8_block", seed_layer=42, outlier_frac=0.01)
+    seq = Sequence(cache, H, d, n, "fp8_block", seed_layer=42 if outliers else 45,
+                   outlier_frac=0.01 if outliers else 0.0)
     _, rk, rv = seq.chunk(80_000)
     seq.append(0, 0, rk, rv, is_ref=True)
     for t in range(1, 7):
@@ -77,8 +80,7 @@ def test_block_sequence(G):
             k, v = k * np.float32(0.5), v * np.float32(4.0)  # blocks of different ranges
         use_ref = t % 2 == 0
         o, lse, _ = seq.attend(0, t, q, k, v, W, use_ref=use_ref, G=G)
-        eo, el = seq.expected(t, q, k, v, W, use_ref=use_ref)
-        assert_close(o, lse, eo, el, TOL["fp8_block"], f"fp8 block G={G} t={t}")
+        assert_fp8(seq, o, lse, t, q, k, v, W, use_ref=use_ref, what=f"fp8 block G={G} t={t}")
         seq.append(0, t, k, v)
 
 
@@ -91,8 +93,7 @@ def test_block_ragged_and_small_chunks():
         for t in range(4):
             q, k, v = seq.chunk(t)
             o, lse, _ = seq.attend(0, t, q, k, v, W)
-            eo, el = seq.expected(t, q, k, v, W)
-            assert_close(o, lse, eo, el, TOL["fp8_block"], f"fp8 block n={n} t={t}")
+            assert_fp8(seq, o, lse, t, q, k, v, W, what=f"fp8 block n={n} t={t}")
             seq.append(0, t, k, v)
 
 
@@ -111,10 +112,14 @@ def test_block_full_size_matrix_game_shape():
     plan = cache.plan(0, cache.spec(25, W, use_ref=True, num_segments=4))
     assert plan["kv_tiles"] == 22 * math.ceil(n / 64), plan  # every block padded to whole tiles
     log("fp8 block full size: oracle ...")
-    eo, el = seq.expected(25, q, k, v, W, use_ref=True)
     for G in (4, 0):
         o, lse, _ = seq.attend(0, 25, q, k, v, W, use_ref=True, G=G)
-        assert_close(o, lse, eo, el, TOL["fp8_block"], f"fp8 block full size G={G}")
+        # Every block's largest value is an 8-sigma outlier, so the per-block
+        # scales equal the per-head ones and the codes are those of the e4m3
+        # workload; on these seeded inputs e4m3 alone moves O by 6.7e-2
+        # against the raw values (4.6e-2 on the e4m3 workload's seeds): the
+        # raw bar is that quantisation error plus the kernel's.
+        assert_fp8(seq, o, lse, 25, q, k, v, W, use_ref=True, what=f"fp8 block full size G={G}")
 
 
 def test_block_refused_calls():

@@ -4,16 +4,21 @@ captured bca_attend calls) against the same loop run eagerly on a second
 cache with the same contents.
 
 Both run the same kernels with the same plans on the same inputs, so every
-replay must give bit-identical outputs, LSE and cache bytes; the eager loop is
-itself held to the oracle by the parity tests. Each replay is separated from
-the next by eager work (new inputs copied in, the eager loop, comparisons)
-and a synchronisation.
+replay must give bit-identical outputs, LSE and cache bytes. Two replayed
+chunks per case (the first and the last, one layer each end) are also held to
+the CPU oracle directly, on the seeded inputs they were computed from. Each
+replay is separated from the next by eager work (new inputs copied in, the
+eager loop, comparisons) and a synchronisation.
 """
+import math
+
 import numpy as np
 import pytest
 
+import oracle
 import synth
-from bca_harness import log, to_dev
+from bca_harness import (FP8_CACHE_ABS, FP8_CACHE_REL, TOL, assert_close, fp8_stored, log,
+                         max_err, to_dev, to_np)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -31,6 +36,52 @@ def _chunk(n, H, d, layer, t, fp8):
     q, k, v = synth.qkv(n, H, d, 70 + layer, t, 0, dtype="bf16",
                         outlier_frac=0.01 if fp8 else 0.0)
     return to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+
+
+def _np_chunk(n, H, d, layer, t, fp8):
+    return synth.qkv(n, H, d, 70 + layer, t, 0, dtype="bf16", outlier_frac=0.01 if fp8 else 0.0)
+
+
+def _oracle_check(kv, H, d, n, layer, t, W, R, o, lse, what):
+    """A replayed chunk against the oracle on the seeded inputs it was computed
+    from: the chunks t-W .. t-1 (and the reference chunk, id 1000) as the
+    history, chunk t as the query chunk. On an 8-bit cache against what the
+    cache holds, at the kernel's bar, and against the unquantised inputs within
+    the quantisation's own error plus that bar."""
+    fp8 = kv in ("fp8", "fp8_block")
+
+    def stored(k, v):
+        if kv == "fp8":
+            s = [8.0 / 448.0] * H
+            return fp8_stored(k, s), fp8_stored(v, s)
+        if kv == "fp8_block":
+            return fp8_stored(k, oracle.block_scales(k)), fp8_stored(v, oracle.block_scales(v))
+        return k.astype(np.float64), v.astype(np.float64)
+
+    hist, hraw = {}, {}
+    for c in range(max(0, t - W), t):
+        _, k, v = _np_chunk(n, H, d, layer, c, fp8)
+        hist[c], hraw[c] = stored(k, v), (k.astype(np.float64), v.astype(np.float64))
+    ref = ref_raw = None
+    if R:
+        _, rk, rv = _np_chunk(n, H, d, layer, 1000, fp8)
+        ref, ref_raw = stored(rk, rv), (rk.astype(np.float64), rv.astype(np.float64))
+    q, k, v = _np_chunk(n, H, d, layer, t, fp8)
+    kk, vv = stored(k, v)
+    scale = 1.0 / math.sqrt(d)
+    eo, el = oracle.attend(q, kk, vv, hist, t=t, W=W, scale=scale, ref=ref, use_ref=R)
+    go, gl = to_np(o), to_np(lse)
+    if not fp8:
+        assert_close(go, gl, eo, el, TOL["bf16"], what)
+        return
+    ro, rl = oracle.attend(q, k, v, hraw, t=t, W=W, scale=scale, ref=ref_raw, use_ref=R)
+    quant = max_err(eo, ro)
+    log(f"{what}: vs stored max|dO| {max_err(go, eo):.3e}, vs raw {max_err(go, ro):.3e} "
+        f"(quantisation alone {quant:.3e})")
+    assert np.all(np.abs(go - eo) <= FP8_CACHE_ABS + FP8_CACHE_REL * np.abs(eo)), what
+    assert max_err(gl, el) <= FP8_CACHE_ABS, what
+    assert max_err(go, ro) <= quant + FP8_CACHE_ABS + FP8_CACHE_REL * np.abs(eo).max(), what
+    assert max_err(gl, rl) <= max_err(el, rl) + FP8_CACHE_ABS, what
 
 
 CASES = [
@@ -97,7 +148,8 @@ def test_replayed_chunk_step_equals_eager(kv, L, H, d, n, S, R, G):
         bca.Cache.advance_counter(d_chunk)
     torch.cuda.synchronize()
 
-    for t in range(t0, t0 + 2 * S + 3):  # wraps the ring more than twice
+    t_end = t0 + 2 * S + 3  # wraps the ring more than twice
+    for t in range(t0, t_end):
         for l in range(L):
             q, k, v = _chunk(n, H, d, l, t, fp8)
             Q[l].copy_(q)
@@ -109,6 +161,9 @@ def test_replayed_chunk_step_equals_eager(kv, L, H, d, n, S, R, G):
         for l in range(L):
             A.set_slot_chunk(l, t % S, t)
         assert int(d_chunk.item()) == t + 1
+        if t in (t0, t_end - 1):
+            l = 0 if t == t0 else L - 1
+            _oracle_check(kv, H, d, n, l, t, S, R, O[l], LSE[l], f"replay {kv} chunk {t} layer {l}")
         spec = B.spec(t, S, use_ref=R, num_segments=G)
         for l in range(L):
             o, lse = B.attend(l, Q[l], K[l], V[l], spec)
@@ -202,7 +257,8 @@ def test_replayed_step_with_window_smaller_than_ring(kv, L, H, d, n, S, W, R, G)
         bca.Cache.advance_counter(d_chunk)
     torch.cuda.synchronize()
 
-    for t in range(t0, t0 + 2 * S + 3):
+    t_end = t0 + 2 * S + 3
+    for t in range(t0, t_end):
         for l in range(L):
             q, k, v = _chunk(n, H, d, l, t, fp8)
             Q[l].copy_(q)
@@ -214,6 +270,11 @@ def test_replayed_step_with_window_smaller_than_ring(kv, L, H, d, n, S, W, R, G)
         for l in range(L):
             A.set_slot_chunk(l, t % S, t)
         assert int(d_chunk.item()) == t + 1
+        if t in (t0, t_end - 1):
+            # a replay of bca_attend_dev (visible slots from the device-side id)
+            l = 0 if t == t0 else L - 1
+            _oracle_check(kv, H, d, n, l, t, W, R, O[l], LSE[l],
+                          f"replay (device id) {kv} chunk {t} layer {l}")
         spec = B.spec(t, W, use_ref=R, num_segments=G)
         for l in range(L):
             o, lse = B.attend(l, Q[l], K[l], V[l], spec)

@@ -4,7 +4,7 @@ most a plan holds), 64 segments, and 64 heads on an e4m3 cache."""
 import numpy as np
 import pytest
 
-from bca_harness import TOL, Sequence, assert_close, log
+from bca_harness import TOL, Sequence, assert_close, log, assert_fp8
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -69,7 +69,6 @@ def test_fp8_with_64_heads(dtype):
     for t in range(4):
         q, k, v = seq.chunk(t)
         o, lse, _ = seq.attend(0, t, q, k, v, W)
-        eo, el = seq.expected(t, q, k, v, W)
-        assert_close(o, lse, eo, el, TOL[dtype], f"{dtype} 64 heads t={t}")
+        assert_fp8(seq, o, lse, t, q, k, v, W, what=f"{dtype} 64 heads t={t}")
         seq.append(0, t, k, v)
     log(f"{dtype}: 64 heads within the bar")

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import synth
-from bca_harness import TOL, Sequence, assert_close, log, max_err, to_dev, to_np
+from bca_harness import TOL, Sequence, assert_close, assert_fp8, log, max_err, to_dev, to_np
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -242,43 +242,34 @@ def test_append_fp8_codes_match_oracle_quantiser():
 # ---------------------------------------------------------------------------
 # fp8 e4m3 K/V cache with per-head scales: the cache holds decode(quant(x/s))*s
 # and the chunk attends at that precision, its own keys and values included.
-# The oracle attends over the same inputs the kernel does, the cache contents.
-# The kernel contracts on the fp8 matrix cores, so Q (per query row) and P
-# (scaled by 2^8) are rounded to e4m3 as well: each rounding is relative
-# 2^-4 at most, and their effect on O averages over the keys of a row. The
-# bar is the fp8 bound, 5e-2. How far the quantised attention is from
-# attention over the unquantised values is e4m3's own error, not the
-# kernel's: it is logged, not asserted.
+# Every result is held to the oracle twice (bca_harness.assert_fp8): on the
+# cache contents (the kernel's own error: Q and P rounded to two e4m3 terms,
+# the bf16 output) and on the unquantised seeded inputs. On the second the
+# the benchmark spec's 5e-2 is asserted at the Matrix-Game size (8910 keys); on the
+# small shapes below (a few hundred keys) e4m3's 3-bit mantissa alone moves
+# O by more than that (a row dominated by one key inherits its rounding, up to
+# 6 % of an 8-sigma value), so there the bar is the quantisation's own error
+# (oracle on cache contents against oracle on raw inputs) plus the kernel's.
 def fp8_scales(H, kmax=8.0, vmax=8.0):
     return ([kmax / 448.0 * (1.0 + 0.1 * h) for h in range(H)],
             [vmax / 448.0 * (1.0 + 0.05 * h) for h in range(H)])
 
 
-def fp8_cache_tol(seq, v):
-    return TOL["fp8"]
-
-
-def log_quantisation_error(o, lse, ro, rl, what):
-    log(f"{what}: e4m3 quantisation moves O by {max_err(o, ro):.3e}, LSE by "
-        f"{max_err(lse, rl):.3e} against the unquantised values (reported, not asserted)")
-
-
-@pytest.mark.parametrize("G", [0, 1, 3])
-def test_fp8_sequence(G):
+@pytest.mark.parametrize("G,outliers", [(0, True), (1, True), (3, True), (0, False), (3, False)])
+def test_fp8_sequence(G, outliers):
     H, d, n, S, W = 4, 128, 100, 3, 2
     cache = new_cache(1, H, d, n, S, R=True, dtype="fp8")
-    seq = Sequence(cache, H, d, n, "fp8", seed_layer=21, outlier_frac=0.01,
-                   scales=fp8_scales(H))
+    seq = Sequence(cache, H, d, n, "fp8", seed_layer=21 if outliers else 22,
+                   outlier_frac=0.01 if outliers else 0.0,
+                   scales=fp8_scales(H) if outliers else fp8_scales(H, 6.0, 6.0))
     _, rk, rv = seq.chunk(90_000)
     seq.append(0, 0, rk, rv, is_ref=True)
     for t in range(1, 7):
         q, k, v = seq.chunk(t)
         use_ref = t % 2 == 0
         o, lse, _ = seq.attend(0, t, q, k, v, W, use_ref=use_ref, G=G)
-        eo, el = seq.expected(t, q, k, v, W, use_ref=use_ref)
-        assert_close(o, lse, eo, el, fp8_cache_tol(seq, v), f"fp8 G={G} t={t} (cache precision)")
-        ro, rl = seq.expected(t, q, k, v, W, use_ref=use_ref, raw=True)
-        log_quantisation_error(o, lse, ro, rl, f"fp8 G={G} t={t}")
+        assert_fp8(seq, o, lse, t, q, k, v, W, use_ref=use_ref,
+                   what=f"fp8 G={G} outliers={outliers} t={t}")
         seq.append(0, t, k, v)
 
 
@@ -295,8 +286,7 @@ def test_fp8_stream_k_ranges_cross_units():
     plan = cache.plan(0, cache.spec(1, W))
     assert plan["units"] > plan["workgroups"] and plan["merge"] == 1, plan
     o, lse, _ = seq.attend(0, 1, q, k, v, W)
-    eo, el = seq.expected(1, q, k, v, W)
-    assert_close(o, lse, eo, el, fp8_cache_tol(seq, v), f"fp8 stream-K {plan['units']} units")
+    assert_fp8(seq, o, lse, 1, q, k, v, W, what=f"fp8 stream-K {plan['units']} units")
 
 
 def test_fp8_workspace_holds_the_chunk_copy():
@@ -321,13 +311,11 @@ def test_cfg4_full_size():
         seq.append(0, t, k, v)
     q, k, v = seq.chunk(25)
     log("cfg4: oracle ...")
-    eo, el = seq.expected(25, q, k, v, W, use_ref=True)
-    ro, rl = seq.expected(25, q, k, v, W, use_ref=True, raw=True)
-    tol = fp8_cache_tol(seq, v)
     for G in (4, 0):
         o, lse, _ = seq.attend(0, 25, q, k, v, W, use_ref=True, G=G)
-        assert_close(o, lse, eo, el, tol, f"cfg4 full size G={G} (cache precision)")
-        log_quantisation_error(o, lse, ro, rl, f"cfg4 full size G={G}")
+        # the benchmark spec's fp8 bar, against the unquantised seeded inputs
+        assert_fp8(seq, o, lse, 25, q, k, v, W, use_ref=True, raw_tol=TOL["fp8"],
+                   what=f"cfg4 full size G={G}")
 
 
 def test_slot_table_over_64_chunks():
@@ -377,21 +365,65 @@ def test_cfg2_full_size():
         assert_close(o, lse, eo, el, TOL["bf16"], f"cfg2 full size G={G}")
 
 
-def test_cfg3_streaming_wraparound():
-    # config-1 shapes streamed: every chunk attends, then is appended; the ring of
-    # 2 slots wraps many times. The oracle checks a sample of chunks, including the
-    # first ones (ring not full) and late ones (after wraparound).
-    H, d, n, S, W = 12, 128, 1536, 2, 2
-    cache = new_cache(1, H, d, n, S)
-    seq = Sequence(cache, H, d, n, "bf16", seed_layer=1)
-    check = {0, 1, 2, 3, 17}
-    for t in range(18):
-        q, k, v = seq.chunk(t)
-        o, lse, _ = seq.attend(0, t, q, k, v, W, G=0)
-        if t in check:
-            hist = {c: seq.history[c] for c in range(max(0, t - 3), t)}
-            eo, el = seq.expected(t, q, k, v, W, history=hist)
-            assert_close(o, lse, eo, el, TOL["bf16"], f"cfg3 stream t={t}")
-        seq.append(0, t, k, v)
-        assert cache.slot_chunk(0, t % S) == t
-        seq.history.pop(t - 4, None)
+def test_cfg3_64_chunks_first_and_last_layer():
+    """Config-1 shapes streamed over 64 chunks through a 30-layer cache: per
+    chunk every layer runs 4 denoise-step attends and then appends the
+    chunk's K/V into ring slot id mod 2 (31 wraparounds). Layers 0 and 29 are
+    held to the oracle at the last step of every chunk: on 49 rows of every
+    head for chunks 0 .. 62, on every row for chunk 63. Every row of a chunk
+    sees the same keys, so the sampled rows' queries are drawn from the seeded
+    generator and the other rows hold arbitrary values."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    H, d, n, S, W, L, C = 12, 128, 1536, 2, 2, 30, 64
+    check = (0, L - 1)
+    cache = new_cache(L, H, d, n, S)
+    rows = list(range(0, n, 32)) + [n - 1]
+    scale = 1.0 / math.sqrt(d)
+
+    def committed(l, t):
+        return (synth.tensor((n, H, d), synth.TAG_K, l, t, 3),
+                synth.tensor((n, H, d), synth.TAG_V, l, t, 3))
+
+    pool = ThreadPoolExecutor(8)
+    futs = {(l, t): pool.submit(committed, l, t) for t in range(C) for l in check}
+    g = torch.Generator(device="cuda").manual_seed(3)
+    filler = [torch.randn((n, H, d), generator=g, device="cuda").to(torch.bfloat16)
+              for _ in range(3)]
+    hist = {l: {} for l in check}
+    worst = 0.0
+    for t in range(C):
+        spec = cache.spec(t, W, num_segments=0)
+        for l in range(L):
+            if l in check:
+                k, v = futs.pop((l, t)).result()
+                kd, vd = to_dev(k, "bf16"), to_dev(v, "bf16")
+            else:
+                kd, vd = filler[1], filler[2]
+            for step in range(4):
+                if l in check and step == 3:
+                    if t == C - 1:
+                        q = synth.tensor((n, H, d), synth.TAG_Q, l, t, 3)
+                        qd, want = to_dev(q, "bf16"), list(range(n))
+                    else:
+                        q = synth.tensor_rows((n, H, d), rows, synth.TAG_Q, l, t, 3)
+                        qd, want = filler[0].clone(), rows
+                        qd[rows] = to_dev(q, "bf16")
+                    o, lse = cache.attend(l, qd, kd, vd, spec)
+                    h = {c: hist[l][c] for c in range(max(0, t - 3), t)}  # t-3: masked
+                    eo, el = oracle.attend(q, k, v, h, t=t, W=W, scale=scale,
+                                           rows=None if t == C - 1 else list(range(len(rows))))
+                    go, gl = to_np(o)[want], to_np(lse)[:, want]
+                    assert_close(go, gl, eo, el, TOL["bf16"], f"cfg3 chunk {t} layer {l}"
+                                 if t in (0, 1, 2, C - 1) or t % 16 == 0 else None)
+                    worst = max(worst, max_err(go, eo), max_err(gl, el))
+                else:
+                    cache.attend(l, filler[0], kd, vd, spec)
+            cache.append_chunk(l, t, kd, vd)
+            if l in check:
+                hist[l][t] = (k, v)
+                hist[l].pop(t - 4, None)
+        for l in check:
+            assert cache.slot_chunk(l, t % S) == t
+    log(f"cfg3: 64 chunks, layers {check}, every chunk within {worst:.3e} of the oracle")

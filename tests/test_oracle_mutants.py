@@ -48,6 +48,13 @@ MUTANTS = [
      "admit = (cj >= ci - W) && (cj <= ci + 1);"),
     ("sequence_prefix_dropped", "        admit = 1;\n      } else {", "        admit = 0;\n      } else {"),
     ("sequence_chunk_of_key_ignores_prefix", "int cj = (j - P) / n;", "int cj = j / n;"),
+    ("block_scale_fixed_code", "? a / qmax : 1.0f;", "? a / 448.0f : 1.0f;"),
+    ("block_scale_over_all_heads", "float v = fabsf(x[((size_t)r * H + h) * d + j]);",
+     "float v = fabsf(x[((size_t)r * H + 0) * d + j]);"),
+    ("int8_ties_away", "if (rem > 0.5 || (rem == 0.5 && (q & 1))) q += 1;",
+     "if (rem >= 0.5) q += 1;"),
+    ("int8_truncates", "if (rem > 0.5 || (rem == 0.5 && (q & 1))) q += 1;", ""),
+    ("int8_clamp_128", "if (y > 127.0f) y = 127.0f;", "if (y > 128.0f) y = 128.0f;"),
 ]
 
 

@@ -46,3 +46,13 @@ def test_outliers_fraction_and_value():
     out = np.abs(x) == 8.0
     assert 0.008 < out.mean() < 0.012
     assert np.abs(x[~out]).max() < 8.0
+
+
+def test_rows_of_a_tensor_drawn_alone():
+    shape = (37, 3, 16)
+    full = synth.tensor(shape, synth.TAG_Q, 2, 9, 1)
+    rows = [0, 5, 36, 17]
+    assert np.array_equal(synth.tensor_rows(shape, rows, synth.TAG_Q, 2, 9, 1), full[rows])
+    full32 = synth.tensor(shape, synth.TAG_Q, 2, 9, 1, dtype="fp32")
+    assert np.array_equal(synth.tensor_rows(shape, rows, synth.TAG_Q, 2, 9, 1, dtype="fp32"),
+                          full32[rows])
