@@ -23,7 +23,8 @@ __all__ = [
     "bca_cache_slot_chunk", "bca_cache_set_slot_chunk", "bca_attend_plan", "bca_status_string",
     "bca_last_error", "bca_sequence_spec", "bca_attend_sequence_workspace_bytes",
     "bca_attend_sequence", "attend_sequence", "bca_append_chunk_dev",
-    "bca_chunk_counter_advance", "bca_attend_replayable", "bca_attend_dev", "Cache", "LIB_PATH", "load_library",
+    "bca_chunk_counter_advance", "bca_attend_replayable", "bca_attend_dev", "bca_attend_noalloc",
+    "NOALLOC_SCRATCH_BYTES", "Cache", "LIB_PATH", "load_library",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbca.so")
@@ -126,6 +127,8 @@ def load_library(path: str = LIB_PATH):
     lib.bca_attend_replayable.restype = I32
     lib.bca_attend_dev.argtypes = [P, I32, spec_p, P, P, P, P, I32, P, P, P, SZ, P]
     lib.bca_attend_dev.restype = I32
+    lib.bca_attend_noalloc.argtypes = [P, I32, spec_p, P, P, P, I32, P, P, P]
+    lib.bca_attend_noalloc.restype = I32
     lib.bca_cache_slot_chunk.argtypes = [P, I32, I32, ctypes.POINTER(I64)]
     lib.bca_cache_slot_chunk.restype = I32
     lib.bca_cache_set_slot_chunk.argtypes = [P, I32, I32, I64]
@@ -313,6 +316,18 @@ def bca_attend_dev(handle: int, layer: int, spec, d_q_chunk_id: int, q: int, k_c
                                ctypes.c_void_p(o), ctypes.c_void_p(lse),
                                ctypes.c_void_p(workspace), workspace_bytes,
                                ctypes.c_void_p(stream)))
+
+
+# Scratch bytes per GPU behind bca_attend_noalloc (BCA_NOALLOC_SCRATCH_BYTES in bca.h).
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def bca_attend_noalloc(handle: int, layer: int, spec, q: int, k_cur: int, v_cur: int,
+                       qkv_dtype: int, o: int, lse: int, stream: int = 0) -> None:
+    _check(_lib.bca_attend_noalloc(ctypes.c_void_p(handle), layer, ctypes.byref(_spec(spec)),
+                                   ctypes.c_void_p(q), ctypes.c_void_p(k_cur),
+                                   ctypes.c_void_p(v_cur), qkv_dtype, ctypes.c_void_p(o),
+                                   ctypes.c_void_p(lse), ctypes.c_void_p(stream)))
 
 
 def bca_cache_slot_chunk(handle: int, layer: int, slot: int) -> int:

@@ -944,6 +944,26 @@ bca_status bca_attend(const bca_cache* c, int32_t layer, const bca_window_spec* 
                      workspace_bytes, stream, nullptr);
 }
 
+bca_status bca_attend_noalloc(const bca_cache* c, int32_t layer, const bca_window_spec* s,
+                              const void* q, const void* k_cur, const void* v_cur,
+                              int32_t qkv_dtype, void* o, float* lse, bca_stream_t stream) {
+  Plan p;
+  bca_status st = make_plan(c, layer, s, qkv_dtype, p);
+  if (st != BCA_OK) return st;
+  if (p.ws_bytes > (size_t)BCA_NOALLOC_SCRATCH_BYTES)
+    return fail(BCA_ERR_WORKSPACE,
+                "bca_attend_noalloc: this call needs %zu bytes of scratch, more than the "
+                "library's %zu (use bca_attend with a workspace)",
+                p.ws_bytes, (size_t)BCA_NOALLOC_SCRATCH_BYTES);
+  void* scratch = nullptr;
+  if (p.ws_bytes > 0) {
+    const int err = noalloc_scratch(&scratch);
+    if (err != 0) return fail(BCA_ERR_HIP, "scratch address lookup failed (hip error %d)", err);
+  }
+  return attend_impl(c, layer, s, q, k_cur, v_cur, qkv_dtype, o, lse, scratch,
+                     p.ws_bytes > 0 ? (size_t)BCA_NOALLOC_SCRATCH_BYTES : 0, stream, nullptr);
+}
+
 bca_status bca_attend_dev(const bca_cache* c, int32_t layer, const bca_window_spec* s,
                           const int64_t* d_q_chunk_id, const void* q, const void* k_cur,
                           const void* v_cur, int32_t qkv_dtype, void* o, float* lse,

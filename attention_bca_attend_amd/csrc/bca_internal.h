@@ -177,5 +177,9 @@ int launch_rope_stage(bca_dtype dt, int head_dim, const RopeStageArgs& args, voi
 int launch_counter_advance(int64_t* counter, void* stream);
 // Compute units of the current device, or 0 when it cannot be queried.
 int device_compute_units();
+// Device address of the current device's bca_attend_noalloc scratch
+// (BCA_NOALLOC_SCRATCH_BYTES bytes), looked up on the first call per device.
+// Returns the HIP error code (0 = success).
+int noalloc_scratch(void** out);
 
 }  // namespace bca

@@ -33,6 +33,8 @@
 // segments; otherwise ranges cross unit boundaries, "stream-K" style.)
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "bca_internal.h"
 
 namespace bca {
@@ -1979,6 +1981,37 @@ int launch_counter_advance(int64_t* counter, void* stream) {
                      static_cast<hipStream_t>(stream), counter);
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? 0 : (int)e;
+}
+
+// Scratch of bca_attend_noalloc: device memory the library owns, for callers
+// that cannot allocate. One copy per GPU the library runs on, held until the
+// process ends. In host code `scratch` names a host-side stand-in, not device
+// memory: the device address comes from hipGetSymbolAddress, looked up once
+// per device (with that device current) and kept.
+static __device__ __align__(256) unsigned char scratch[BCA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+int noalloc_scratch(void** out) {
+  *out = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!p) return (int)hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return 0;
 }
 
 int device_compute_units() {

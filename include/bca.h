@@ -186,6 +186,28 @@ bca_status bca_attend(const bca_cache* cache, int32_t layer, const bca_window_sp
                       void* o, float* lse, void* workspace, size_t workspace_bytes,
                       bca_stream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * bca_attend without a workspace argument. What the workspace holds (the
+ * partial outputs of a split window; on an FP8_E4M3 cache the e4m3 copy of the
+ * current chunk, and its scales on an FP8_E4M3_BLOCK cache) goes to scratch
+ * memory the library owns: one array of BCA_NOALLOC_SCRATCH_BYTES bytes per
+ * GPU, set up on the first call on that GPU and held until the process ends.
+ * The call allocates nothing. Every call on one GPU uses the same scratch
+ * (nothing in it needs to start at zero, and its content after a call is
+ * irrelevant), so calls that may run at the same time on one GPU (on
+ * different streams, or on one stream from different host threads without
+ * ordering) race and must not overlap. Arguments, results and errors as for
+ * bca_attend, plus BCA_ERR_WORKSPACE when the call would need more scratch
+ * than BCA_NOALLOC_SCRATCH_BYTES (the Wan- and Matrix-Game-shaped calls need
+ * under 32 MiB), and BCA_ERR_HIP when the scratch address cannot be looked
+ * up. */
+#define BCA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+bca_status bca_attend_noalloc(const bca_cache* cache, int32_t layer, const bca_window_spec* spec,
+                              const void* q, const void* k_cur, const void* v_cur,
+                              int32_t qkv_dtype, void* o, float* lse, bca_stream_t stream);
+
 /* Rotary position embedding (RoPE) fused into the path. The pages name the step
  * only ("Matrix-Game 4.0" summary, experimental results: a RoPE fusion kernel;
  * "WorldPlay2" summary, inference optimisations: QKRoPE); the form used is the
