@@ -36,6 +36,7 @@
 #include <mutex>
 
 #include "bca_internal.h"
+#include "../../include/bca_probe.h"
 
 namespace bca {
 namespace {
@@ -2028,3 +2029,86 @@ int device_compute_units() {
 }
 
 }  // namespace bca
+
+// ---------------------------------------------------------------------------
+// Measurement hooks (include/bca_probe.h; not part of the attention path): the
+// matrix cores' dense bf16 and fp8 rates at the clock the chip runs at under load. Every wave issues
+// v_mfma_f32_32x32x16_bf16 back to back into four independent accumulators;
+// 8 waves per work group (two per SIMD), one work group per compute unit.
+// The benchmark times the launch with events on the stream it runs on and
+// reports the measured rate beside the published peak.
+namespace bca {
+namespace {
+
+__global__ __launch_bounds__(512) void mfma_peak_kernel(float* out, int iters) {
+  typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+  b8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(1.0f + 1e-3f * (float)((threadIdx.x + i) & 7));
+    b[i] = (__bf16)(1.0f - 1e-3f * (float)((threadIdx.x * 3 + i) & 7));
+  }
+  f32x16_t acc0 = {}, acc1 = {}, acc2 = {}, acc3 = {};
+  for (int it = 0; it < iters; ++it) {
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc1, 0, 0, 0);
+    acc2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc2, 0, 0, 0);
+    acc3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc3, 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) s += acc0[e] + acc1[e] + acc2[e] + acc3[e];
+  // one value per wave reaches memory, so the products cannot be dropped
+  if ((threadIdx.x & 63) == 0) out[blockIdx.x * 8 + (threadIdx.x >> 6)] = s;
+}
+
+// The same with v_mfma_f32_32x32x64_f8f6f4 on e4m3 operands (the fp8 rate).
+__global__ __launch_bounds__(512) void mfma_peak_fp8_kernel(float* out, int iters) {
+  i32x8_t a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = 0x38383838 + (int)((threadIdx.x + i) & 3);   // e4m3 values near 1
+    b[i] = 0x38383838 + (int)((threadIdx.x * 3 + i) & 3);
+  }
+  f32x16_t acc0 = {}, acc1 = {}, acc2 = {}, acc3 = {};
+  for (int it = 0; it < iters; ++it) {
+    acc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc0, 0, 0, 0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc1, 0, 0, 0, 0, 0, 0);
+    acc2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc2, 0, 0, 0, 0, 0, 0);
+    acc3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc3, 0, 0, 0, 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) s += acc0[e] + acc1[e] + acc2[e] + acc3[e];
+  if ((threadIdx.x & 63) == 0) out[blockIdx.x * 8 + (threadIdx.x >> 6)] = s;
+}
+
+}  // namespace
+}  // namespace bca
+
+// FLOP of one probe launch: wgs * 8 waves * iters * 4 MFMAs * 32*32*16*2.
+extern "C" double bca_probe_mfma_bf16_flops(int wgs, int iters) {
+  return (double)wgs * 8.0 * (double)iters * 4.0 * 32768.0;
+}
+
+// FLOP of one fp8 probe launch: wgs * 8 waves * iters * 4 MFMAs * 32*32*64*2.
+extern "C" double bca_probe_mfma_fp8_flops(int wgs, int iters) {
+  return (double)wgs * 8.0 * (double)iters * 4.0 * 131072.0;
+}
+
+extern "C" int bca_probe_mfma_fp8(int wgs, int iters, float* out, void* stream) {
+  if (wgs < 1 || iters < 1 || !out) return -1;
+  hipLaunchKernelGGL(bca::mfma_peak_fp8_kernel, dim3((unsigned)wgs), dim3(512), 0,
+                     static_cast<hipStream_t>(stream), out, iters);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? 0 : (int)e;
+}
+
+// Launches the probe on `stream`; `out` is device memory of wgs * 8 floats.
+extern "C" int bca_probe_mfma_bf16(int wgs, int iters, float* out, void* stream) {
+  if (wgs < 1 || iters < 1 || !out) return -1;
+  hipLaunchKernelGGL(bca::mfma_peak_kernel, dim3((unsigned)wgs), dim3(512), 0,
+                     static_cast<hipStream_t>(stream), out, iters);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? 0 : (int)e;
+}

@@ -145,10 +145,113 @@ def cpu_baseline(cache, cfg, q0, k0, v0, t):
         reps = max(1, int(math.ceil(10.0 / max(dt, 1e-3))))
         dt = dt + sum(run(hs) for _ in range(reps - 1))
     flops = 4.0 * hs * n * nk * d * reps
+    v1, r1, d1 = cpu_baseline_one_core(run, lambda h: 4.0 * h * n * nk * d,
+                                       dt / (hs * reps) * oracle.threads())
+    model, nproc = host_cpu()
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
             "kind": "oracle",
             "sample": f"layer 0 chunk-layer, {hs} of {H} heads x {n} query rows x {nk} keys, "
-                      f"{reps} time(s) (fp64 dense-mask oracle, {dt:.1f} s in all)"}
+                      f"{reps} time(s) (fp64 dense-mask oracle, {dt:.1f} s in all)",
+            "value_1core": v1,
+            "sample_1core": (f"1 of {H} heads, {r1} time(s) on one thread ({d1:.1f} s)"
+                             if v1 is not None else "left out: over 40 s on one thread"),
+            "cpu_model": model, "nproc": nproc}
+
+
+def host_cpu():
+    """The host's CPU model (from /proc/cpuinfo, what lscpu reports as Model
+    name) and the number of cores this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:
+        nproc = os.cpu_count() or 1
+    return model, nproc
+
+
+def cpu_baseline_one_core(run_sample, flops_of, est_s):
+    """The same oracle sample on one thread: run_sample(hs) times the oracle
+    on hs heads; repeated until about 5 s of CPU work. est_s estimates one
+    head on one thread (from the threaded run); above 40 s the one-thread run
+    is left out (None) so the benchmark stays within minutes."""
+    import oracle
+    if est_s > 40.0:
+        return None, 0, 0.0
+    before = oracle.threads()
+    oracle.set_threads(1)
+    try:
+        dt, reps = run_sample(1), 1
+        while dt < 5.0 and reps < 64:
+            dt += run_sample(1)
+            reps += 1
+    finally:
+        oracle.set_threads(before)
+    return flops_of(1) * reps / dt / 1e12, reps, dt
+
+
+_PEAK_MEASURED = {}
+
+
+def measure_mfma_peak(kind="bf16"):
+    """Dense MFMA rate measured on this GPU at the clock it runs at under load:
+    the library's probe kernel issues 32x32 MFMAs back to back (bf16
+    32x32x16, or e4m3 32x32x64 for kind "fp8") on every SIMD, one work group of
+    8 waves per compute unit, timed with events on the stream it runs on; best
+    of three launches after a first that loads the code."""
+    if kind in _PEAK_MEASURED:
+        return _PEAK_MEASURED[kind]
+    import ctypes
+
+    import torch
+
+    import attention_bca_attend_amd as bca
+    lib = bca.load_library()
+    name = "bf16" if kind == "bf16" else "fp8"
+    launch = getattr(lib, f"bca_probe_mfma_{name}")
+    flops = getattr(lib, f"bca_probe_mfma_{name}_flops")
+    launch.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    launch.restype = ctypes.c_int
+    flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    flops.restype = ctypes.c_double
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty((cus * 8,), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    iters = 20000
+    best = 0.0
+    for rep in range(4):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = launch(cus, iters, ctypes.c_void_p(out.data_ptr()),
+                    ctypes.c_void_p(stream.cuda_stream))
+        e1.record(stream)
+        if rc != 0:
+            raise RuntimeError(f"MFMA probe launch failed ({rc})")
+        torch.cuda.synchronize()
+        if rep == 0:
+            continue
+        best = max(best, flops(cus, iters) / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    _PEAK_MEASURED[kind] = round(best, 1)
+    return _PEAK_MEASURED[kind]
+
+
+def roofline_mfma(achieved, kind, traffic, kernel):
+    """The roofline object of an MFMA-bound kernel: the published dense peak of
+    its operand type, and beside it the rate the probe measures on this GPU."""
+    peak = PEAK_TFLOPS[kind]
+    meas = measure_mfma_peak("bf16" if kind == "bf16" else "fp8")
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+            "kernel": kernel, "peak_measured": meas,
+            "frac_measured": round(achieved / meas, 4) if meas > 0 else None}
 
 
 def sequence_flops(H, d, n, C, W, P):
@@ -176,10 +279,17 @@ def cpu_baseline_sequence(cfg, q, k, v):
         hs = min(H, max(2, int(math.ceil(10.0 / max(dt, 1e-3)))))
         dt = run(hs)
     flops = sequence_flops(hs, d, n, C, W, P)
+    v1, r1, d1 = cpu_baseline_one_core(run, lambda h: sequence_flops(h, d, n, C, W, P),
+                                       dt / hs * oracle.threads())
+    model, nproc = host_cpu()
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
             "kind": "oracle",
             "sample": f"layer 0 whole sequence, {hs} of {H} heads x {C} chunks of {n} tokens "
-                      f"(fp64 dense-mask oracle, {dt:.1f} s)"}
+                      f"(fp64 dense-mask oracle, {dt:.1f} s)",
+            "value_1core": v1,
+            "sample_1core": (f"1 of {H} heads, {r1} time(s) on one thread ({d1:.1f} s)"
+                             if v1 is not None else "left out: over 40 s on one thread"),
+            "cpu_model": model, "nproc": nproc}
 
 
 def main_graph(args, cfg):
@@ -283,10 +393,9 @@ def main_graph(args, cfg):
         "pct_mfma_peak": round(100.0 * tflops / peak, 2),
         "chunk_ms_min_max": [round(min(chunk_ms), 4), round(max(chunk_ms), 4)],
         "host_ms_per_step": round(host_s * 1e3 / steps, 4),
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
-                     "traffic": measured_traffic(cfg["workload"]),
-                     "kernel": "replayed chunk step (attends with appends, whole-step time)"},
+        "roofline": roofline_mfma(tflops, "bf16", measured_traffic(cfg["workload"]),
+                                  "replayed chunk step (attends with appends, whole-step "
+                                  "time)"),
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
@@ -365,11 +474,9 @@ def main_sequence(args, cfg):
         "sequence_call_us": round(call_us, 3),
         "pct_mfma_peak": round(100.0 * tflops / peak, 2),
         "step_ms_min_max": [round(min(step_ms), 4), round(max(step_ms), 4)],
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
-                     "traffic": measured_traffic(cfg["workload"]),
-                     "kernel": f"bca_attend_sequence: {C} x (attn_bf16_kernel + merge_kernel "
-                               f"where split)"},
+        "roofline": roofline_mfma(tflops, "bf16", measured_traffic(cfg["workload"]),
+                                  f"bca_attend_sequence: {C} x (attn_bf16_kernel + "
+                                  f"merge_kernel where split)"),
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
@@ -563,17 +670,14 @@ def main():
         "pct_mfma_peak": round(100.0 * achieved / peak, 2),
         "chunk_ms_min_max": [round(min(chunk_ms), 4), round(max(chunk_ms), 4)],
         "host_ms_per_step": round(host_s * 1e3 / steps, 4),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(cfg["workload"]),
-                     "kernel": ("bca_attend_rope: rope_stage_kernel + " if rope_base
-                                else "bca_attend: ")
-                               + ("attn_fp8_kernel + append_fp8_kernel (chunk copy)"
-                                  if cfg["kv"] == "fp8" else
-                                  "attn_fp8_kernel (block scales) + append_amax_kernel + "
-                                  "append_fp8_kernel (chunk copy)" if fp8
-                                  else "attn_bf16_kernel")
-                               + (" + merge_kernel" if plan["merge"] else "")},
+        "roofline": roofline_mfma(
+            achieved, cfg["kv"], measured_traffic(cfg["workload"]),
+            ("bca_attend_rope: rope_stage_kernel + " if rope_base else "bca_attend: ")
+            + ("attn_fp8_kernel + append_fp8_kernel (chunk copy)" if cfg["kv"] == "fp8"
+               else "attn_fp8_kernel (block scales) + append_amax_kernel + "
+                    "append_fp8_kernel (chunk copy)" if fp8
+               else "attn_bf16_kernel")
+            + (" + merge_kernel" if plan["merge"] else "")),
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")

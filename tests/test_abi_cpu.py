@@ -19,7 +19,9 @@ FAKE = 1 << 40
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    inc = os.path.join(ROOT, "include")
+    text = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc))
+                   if f.endswith(".h"))
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(bca_[a-z_]+)\s*\(", text)))
 
