@@ -586,6 +586,9 @@ def main():
         for c in range(S):
             cache.append_chunk(l, c, gen((n, H, d), g, fp8), gen((n, H, d), g, fp8),
                                rope=rope(c))
+        if l % 10 == 9 or l == L - 1:
+            torch.cuda.synchronize()
+            log(f"set-up: ring of layers 0..{l} filled")
     torch.cuda.synchronize()
     t_chunk = S
     spec0 = cache.spec(t_chunk, W, use_ref=bool(R), num_segments=G)
