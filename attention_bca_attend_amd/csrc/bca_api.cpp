@@ -201,13 +201,19 @@ float* block_scales(const bca_cache* c, int32_t layer, int kv) {
   return t + ((size_t)layer * 2 + kv) * (d.ring_slots + d.has_ref) * d.num_heads;
 }
 
-size_t partial_bytes(int64_t units, int64_t jmax, int bm, int d) {
-  // part_o [units][jmax][bm][d] fp32, then part_lse [units][jmax][bm] fp32,
-  // each region 256-byte aligned
-  size_t po = (size_t)units * jmax * bm * d * 4;
-  size_t pl = (size_t)units * jmax * bm * 4;
-  po = (po + 255) & ~(size_t)255;
-  return po + ((pl + 255) & ~(size_t)255);
+// Partial-output slots per work group: 1 when every work group's range lies
+// within one unit (each unit cut into P / units equal ranges), else 2 (a range
+// can end one unit and start the next).
+int32_t slots_per_wg(int64_t units, int64_t P) { return (P >= units && P % units == 0) ? 1 : 2; }
+
+// Bytes of part_o [P][spw][bm][d] (sized for fp32), then part_lse [P][spw][bm]
+// fp32, each region 256-byte aligned.
+size_t part_o_bytes(int64_t P, int32_t spw, int bm, int d) {
+  return ((size_t)P * spw * bm * d * 4 + 255) & ~(size_t)255;
+}
+size_t partial_bytes(int64_t P, int32_t spw, int bm, int d) {
+  const size_t pl = (size_t)P * spw * bm * 4;
+  return part_o_bytes(P, spw, bm, d) + ((pl + 255) & ~(size_t)255);
 }
 
 // Window resolution and planning shared by bca_attend, bca_attend_plan and
@@ -312,7 +318,8 @@ bca_status make_plan(const bca_cache* c, int32_t layer, const bca_window_spec* s
   p.wgs = (int32_t)choose_wgs(c, p.kern, p.units, p.kv_tiles, s->num_segments);
   p.jmax = pieces_bound(p.units, p.kv_tiles, p.wgs);
   p.merge = p.jmax > 1 ? 1 : 0;
-  p.ws_bytes = p.merge ? partial_bytes(p.units, p.jmax, p.bm, d.head_dim) : 0;
+  p.spw = slots_per_wg(p.units, p.wgs);
+  p.ws_bytes = p.merge ? partial_bytes(p.wgs, p.spw, p.bm, d.head_dim) : 0;
   p.stage_off = p.ws_bytes;
   if (p.kern == Kern::FP8) p.ws_bytes += fp8_stage_bytes(d);
   if (p.blk) p.ws_bytes += cur_scale_bytes(d);
@@ -603,8 +610,8 @@ size_t bca_attend_workspace_bytes(const bca_cache* c, const bca_window_spec* s) 
                                    : (int64_t)(blocks - 1) * n;
     int64_t T = (cache_keys + ts.bn - 1) / ts.bn + (n + ts.bn - 1) / ts.bn;
     int64_t P = choose_wgs(c, k, units, T, s->num_segments);
-    int32_t jmax = pieces_bound(units, T, P);
-    if (jmax > 1) worst = std::max(worst, partial_bytes(units, jmax, ts.bm, c->d.head_dim));
+    if (pieces_bound(units, T, P) > 1)
+      worst = std::max(worst, partial_bytes(P, slots_per_wg(units, P), ts.bm, c->d.head_dim));
   }
   if (k == Kern::FP8) worst += fp8_stage_bytes(c->d);
   if (blk) worst += cur_scale_bytes(c->d);
@@ -706,10 +713,9 @@ bca_status attend_impl(const bca_cache* c, int32_t layer, const bca_window_spec*
   a.o = o;
   a.lse = lse;
   if (p.merge) {
-    size_t po = (size_t)p.units * p.jmax * p.bm * d.head_dim * 4;
-    po = (po + 255) & ~(size_t)255;
     a.part_o = static_cast<float*>(workspace);
-    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + po);
+    a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          part_o_bytes(p.wgs, p.spw, p.bm, d.head_dim));
   }
   a.cache_head_elems = (int64_t)(d.ring_slots + d.has_ref) * d.chunk_tokens * d.head_dim;
   a.cache_span_elems = a.cache_head_elems;
@@ -722,7 +728,7 @@ bca_status attend_impl(const bca_cache* c, int32_t layer, const bca_window_spec*
   a.QT = p.q_tiles;
   a.units = p.units;
   a.P = p.wgs;
-  a.jmax = p.jmax;
+  a.spw = p.spw;
   a.scale = s->scale;
   a.scale_log2 = (float)((double)s->scale * 1.4426950408889634);
   a.xcd_remap = (p.wgs % 8 == 0) ? 1 : 0;
@@ -816,7 +822,8 @@ void seq_plan(const bca_sequence_spec* s, int32_t qkv_dtype, int cus, int64_t c,
   p.wgs = (int32_t)choose_wgs_on(cus, p.kern, p.units, p.kv_tiles, s->num_segments);
   p.jmax = pieces_bound(p.units, p.kv_tiles, p.wgs);
   p.merge = p.jmax > 1 ? 1 : 0;
-  p.ws_bytes = p.merge ? partial_bytes(p.units, p.jmax, p.bm, s->head_dim) : 0;
+  p.spw = slots_per_wg(p.units, p.wgs);
+  p.ws_bytes = p.merge ? partial_bytes(p.wgs, p.spw, p.bm, s->head_dim) : 0;
 }
 
 // The launches of a sequence: (first chunk, chunk count). Chunks before the
@@ -895,10 +902,9 @@ bca_status attend_sequence_impl(const bca_sequence_spec* s, const void* q, const
     a.o = static_cast<char*>(o) + chunk_off;
     a.lse = lse ? lse + (size_t)(c * H * n) : nullptr;
     if (p.merge) {
-      size_t po = (size_t)p.units * p.jmax * p.bm * D * 4;
-      po = (po + 255) & ~(size_t)255;
       a.part_o = static_cast<float*>(workspace);
-      a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + po);
+      a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                            part_o_bytes(p.wgs, p.spw, p.bm, (int)D));
     }
     // the "cache" is the token-major K/V itself: heads d apart, rows H*d apart
     a.cache_head_elems = D;
@@ -912,7 +918,7 @@ bca_status attend_sequence_impl(const bca_sequence_spec* s, const void* q, const
     a.QT = p.q_tiles;
     a.units = p.units;
     a.P = p.wgs;
-    a.jmax = p.jmax;
+    a.spw = p.spw;
     a.scale = s->scale;
     a.scale_log2 = (float)((double)s->scale * 1.4426950408889634);
     a.xcd_remap = (p.wgs % 8 == 0) ? 1 : 0;

@@ -66,7 +66,8 @@ struct Plan {
   int32_t bm, bn;
   int32_t q_tiles, kv_tiles, units; // units = H * q_tiles
   int32_t wgs;                      // work groups (P)
-  int32_t jmax;                     // partial slots reserved per unit
+  int32_t jmax;                     // most work groups any unit is split over
+  int32_t spw;                      // partial-output slots per work group (1 or 2)
   int32_t merge;                    // 1: some unit is split over work groups
   size_t stage_off;                 // fp8 cache: offset of the current-chunk staging copy
   size_t ws_bytes;                  // workspace this call needs
@@ -83,13 +84,13 @@ struct AttnArgs {
   const void* vc;     // this layer's V blocks
   void* o;            // [n][H][d]
   float* lse;         // [H][n] or null
-  float* part_o;      // [units][jmax][bm][d] fp32
-  float* part_lse;    // [units][jmax][bm]
+  float* part_o;      // [P][spw][bm][d] (fp32, bf16 on the bf16 path)
+  float* part_lse;    // [P][spw][bm]
   int64_t cache_head_elems;  // elements between heads' first cache rows: (S+R)*n*d for the
                              // ring, d for a token-major sequence [rows][H][d]
   int64_t cache_span_elems;  // elements one head's cache rows span (buffer resource size)
   int32_t cache_row_elems;   // elements between consecutive cache rows: d (ring), H*d (sequence)
-  int32_t n, H, nk_cache, cache_tiles, T, QT, units, P, jmax;
+  int32_t n, H, nk_cache, cache_tiles, T, QT, units, P, spw;
   float scale;        // softmax scale
   float scale_log2;   // scale * log2(e)
   int32_t xcd_remap;  // 1: spread work-group ids so each XCD gets a contiguous range
@@ -126,7 +127,7 @@ struct MergeArgs {
   const float* part_lse;
   void* o;
   float* lse;
-  int32_t n, H, T, QT, units, P, jmax, bm;
+  int32_t n, H, T, QT, units, P, spw, bm;
   int32_t upc;          // units per chunk (see AttnArgs)
   int64_t chunk_elems;  // o elements per chunk
   int64_t chunk_lse;    // lse floats per chunk

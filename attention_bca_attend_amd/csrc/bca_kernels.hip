@@ -58,6 +58,16 @@ __device__ __forceinline__ int64_t first_wg_of(int64_t x, int64_t I, int64_t P) 
   return ((x + 1) * P + I - 1) / I - 1;
 }
 
+// Partial-output slot of work group w's part of unit u (T tiles per unit).
+// A range touches at most two units whose results stay partial: the one it
+// starts in and the one it ends in, so each work group owns spw <= 2 slots
+// (spw = 1 when every range lies within one unit) and the workspace is
+// bounded by the launch's work groups, not by its units.
+__device__ __forceinline__ int64_t part_slot(int64_t w, int64_t u, int64_t I, int64_t T,
+                                             int64_t P, int spw) {
+  return (int64_t)spw * w + (u != range_begin(w, I, P) / T ? 1 : 0);
+}
+
 // Work-group ids are handed to the 8 XCDs round robin (id % 8). Remapping so
 // that XCD x gets the contiguous range [x P/8, (x+1) P/8) keeps the work
 // groups that read the same head's K/V on one XCD and its L2.
@@ -747,8 +757,8 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
           if (hi == 0 && a.lse)
             a.lse[(SEQ ? ci * a.chunk_lse : 0) + (int64_t)h * a.n + row] = lse_val;
         } else {
-          const int64_t jslot = (int64_t)w - first_wg_of((int64_t)u * a.T, I, a.P);
-          const int64_t prow = ((int64_t)u * a.jmax + jslot) * C::BM + (wave & 7) * 32 + l32;
+          const int64_t prow =
+              part_slot(w, u, I, a.T, a.P, a.spw) * C::BM + (wave & 7) * 32 + l32;
           // bf16 partial outputs (normalised, so |O| stays within the values' range)
           __bf16* pp = reinterpret_cast<__bf16*>(a.part_o) + prow * D;
 #pragma unroll
@@ -1293,8 +1303,8 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
             }
           if (hi == 0 && a.lse) a.lse[(int64_t)h * a.n + row] = lse_val;
         } else {
-          const int64_t jslot = (int64_t)w - first_wg_of((int64_t)u * a.T, I, a.P);
-          const int64_t prow = ((int64_t)u * a.jmax + jslot) * C::BM + (wave & 7) * 32 + l32;
+          const int64_t prow =
+              part_slot(w, u, I, a.T, a.P, a.spw) * C::BM + (wave & 7) * 32 + l32;
           float* pp = a.part_o + prow * D;
 #pragma unroll
           for (int db = 0; db < D / 32; ++db)
@@ -1429,8 +1439,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(const AttnArgs a) {
         dst = static_cast<float*>(a.o) + ((int64_t)row * a.H + h) * D + half * HALF;
         if (half == 0 && a.lse) a.lse[(int64_t)h * a.n + row] = lse_val;
       } else {
-        const int64_t jslot = (int64_t)w - first_wg_of((int64_t)u * a.T, I, a.P);
-        const int64_t prow = ((int64_t)u * a.jmax + jslot) * BM + rloc;
+        const int64_t prow = part_slot(w, u, I, a.T, a.P, a.spw) * BM + rloc;
         dst = a.part_o + prow * D + half * HALF;
         if (half == 0) a.part_lse[prow] = lse_val;
       }
@@ -1466,15 +1475,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   const int blocks_per_unit = (a.bm + RPB - 1) / RPB;
   const int u = blockIdx.x / blocks_per_unit;
   const int rb = blockIdx.x - u * blocks_per_unit;
-  // pieces of unit u: P / units when every unit is cut alike, else from the ranges
-  int pieces;
-  if (a.P % a.units == 0) {
-    pieces = a.P / a.units;
-  } else {
-    const int64_t I = (int64_t)a.units * a.T;
-    pieces = (int)(first_wg_of((int64_t)(u + 1) * a.T - 1, I, a.P) -
-                   first_wg_of((int64_t)u * a.T, I, a.P) + 1);
-  }
+  // pieces of unit u: the work groups w0 .. w0 + pieces - 1 whose ranges meet it
+  const int64_t I = (int64_t)a.units * a.T;
+  const int64_t w0 = first_wg_of((int64_t)u * a.T, I, a.P);
+  const int pieces = (int)(first_wg_of((int64_t)(u + 1) * a.T - 1, I, a.P) - w0 + 1);
   if (pieces <= 1) return;  // written whole by the attention kernel
   const int rloc = rb * RPB + threadIdx.x / TPR;
   const int c4 = (threadIdx.x % TPR) * 4;
@@ -1483,7 +1487,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   const int h = ul / a.QT, qt = ul - h * a.QT;
   const int row = qt * a.bm + rloc;
   if (row >= a.n) return;
-  const int64_t prow0 = (int64_t)u * a.jmax * a.bm + rloc;  // piece j: prow0 + j bm
+  // piece j is work group w0 + j's part: a slot of its own for j >= 1 (that
+  // range starts inside unit u), part_slot's choice for j = 0
+  const int64_t prow0 = part_slot(w0, u, I, a.T, a.P, a.spw) * a.bm + rloc;
+  auto prow_of = [&](int j) -> int64_t {
+    return j == 0 ? prow0 : ((w0 + j) * a.spw) * a.bm + rloc;
+  };
   float M = -INFINITY;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
@@ -1494,7 +1503,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
       if (j < pieces) {
-        const int64_t prow = prow0 + (int64_t)j * a.bm;
+        const int64_t prow = prow_of(j);
         lj[j] = a.part_lse[prow];
         oj[j] = load_part4(reinterpret_cast<const PartT*>(a.part_o) + prow * D + c4);
       }
@@ -1513,10 +1522,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
       }
     }
   } else {
-    for (int j = 0; j < pieces; ++j) M = fmaxf(M, a.part_lse[prow0 + (int64_t)j * a.bm]);
+    for (int j = 0; j < pieces; ++j) M = fmaxf(M, a.part_lse[prow_of(j)]);
     if (M != -INFINITY) {
       for (int j = 0; j < pieces; ++j) {
-        const int64_t prow = prow0 + (int64_t)j * a.bm;
+        const int64_t prow = prow_of(j);
         const float lj = a.part_lse[prow];
         const float wj = (lj == -INFINITY) ? 0.f : expf(lj - M);
         wsum += wj;
@@ -1897,7 +1906,7 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
     m.QT = a.QT;
     m.units = a.units;
     m.P = a.P;
-    m.jmax = a.jmax;
+    m.spw = a.spw;
     m.bm = p.bm;
     m.upc = a.upc;
     m.chunk_elems = a.chunk_elems;

@@ -344,6 +344,64 @@ def test_rope_entry_points_validate_before_launch():
     bca.bca_cache_destroy(h)
 
 
+def test_sequence_workspace_bounded_by_work_groups():
+    """Partial outputs are indexed by work group (at most two per group), so a
+    whole clip's workspace does not grow with its number of chunks: 64
+    Wan-shaped chunks need what 8 need, below 200 MB."""
+    S = bca.bca_sequence_spec
+    need = {C: bca.bca_attend_sequence_workspace_bytes(S(12, 128, 1536, C, 0, 2, 0, 0.088),
+                                                      bca.BF16) for C in (8, 64)}
+    assert 0 < need[64] == need[8] < 200e6, need
+    # 256 work groups x 2 slots x 256 rows x (128 + 1) fp32
+    assert need[64] <= 256 * 2 * 256 * 129 * 4 + 512
+
+
+def test_partial_slots_fit_and_do_not_collide():
+    """The kernels' partial-output indexing, checked on the host: work group w
+    writes its part of unit u to slot spw*w + (u != first unit of w's range),
+    the merge reads piece j of unit u from work group first_wg(u T) + j. Every
+    slot written is below spw*P (the workspace holds spw*P slots), no two
+    parts share a slot, and the merge reads exactly the slots written."""
+    def rb(w, I, P):
+        return w * I // P
+
+    def first_wg(x, I, P):
+        return ((x + 1) * P + I - 1) // I - 1
+
+    cases = [(72, 72, 216), (48, 140, 192), (4464, 72, 256), (312, 8, 256), (7, 5, 33),
+             (100, 3, 256), (1, 9, 9), (3, 4, 5), (256, 1, 256), (30, 7, 64)]
+    for units, T, P in cases:
+        I = units * T
+        assert P <= I
+        spw = 1 if (P >= units and P % units == 0) else 2
+        written = {}
+        for w in range(P):
+            a, b = rb(w, I, P), rb(w + 1, I, P)
+            u0 = a // T
+            it = a
+            while it < b:
+                u = it // T
+                t0 = it - u * T
+                t1 = min(T, t0 + (b - it))
+                if not (t0 == 0 and t1 == T):
+                    slot = spw * w + (1 if u != u0 else 0)
+                    assert slot < spw * P, (units, T, P, w, u)
+                    assert slot not in written, (units, T, P, w, u)
+                    written[slot] = (w, u)
+                it += t1 - t0
+        read = {}
+        for u in range(units):
+            w0 = first_wg(u * T, I, P)
+            pieces = first_wg((u + 1) * T - 1, I, P) - w0 + 1
+            if pieces <= 1:
+                continue
+            for j in range(pieces):
+                slot = (spw * w0 + (1 if u != rb(w0, I, P) // T else 0)) if j == 0 \
+                    else spw * (w0 + j)
+                read[slot] = (w0 + j, u)
+        assert read == written, (units, T, P)
+
+
 def test_sequence_entry_point_validates_before_launch():
     P = FAKE
     S = bca.bca_sequence_spec

@@ -122,6 +122,48 @@ def test_sequence_full_size_wan_shape():
         assert_close(o[:, hs], lse[:, hs], eo, el, TOL["bf16"], f"Wan-shaped sequence head {h}")
 
 
+def test_sequence_64_chunk_wan_clip():
+    """A 64-chunk Wan-shaped clip (12 heads x 1536 tokens, window 2) in one
+    call: its workspace is bounded by the launches' work groups (below 200 MB;
+    the steady launch covers 62 chunks = 4464 units on 256 work groups, whose
+    key-tile ranges end one unit and start the next), and chunks 0, 1, 31 and
+    63 match the oracle on 49 rows of every head. Only the rows and chunks the
+    oracle sees are seeded draws; the rest are device random numbers."""
+    import attention_bca_attend_amd as bca
+    H, d, n, C, W = 12, 128, 1536, 64, 2
+    spec = bca.bca_sequence_spec(H, d, n, C, 0, W, 0, 1.0 / math.sqrt(d))
+    need = bca.bca_attend_sequence_workspace_bytes(spec, bca.BF16)
+    log(f"64-chunk Wan clip: workspace {need / 1e6:.1f} MB")
+    assert 0 < need < 200e6
+    g = torch.Generator(device="cuda").manual_seed(64)
+    qd = torch.randn((C * n, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    kd = torch.randn((C * n, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    vd = torch.randn((C * n, H, d), generator=g, device="cuda").to(torch.bfloat16)
+    checked = (0, 1, 31, 63)
+    kv = {}
+    for c in sorted({x for t in checked for x in range(max(0, t - W), t + 1)}):
+        kc = synth.tensor((n, H, d), synth.TAG_K, 64, c, 0)
+        vc = synth.tensor((n, H, d), synth.TAG_V, 64, c, 0)
+        kd[c * n:(c + 1) * n] = to_dev(kc, "bf16")
+        vd[c * n:(c + 1) * n] = to_dev(vc, "bf16")
+        kv[c] = (kc, vc)
+    rows = list(range(0, n, 32)) + [n - 1]
+    qs = {}
+    for c in checked:
+        qs[c] = synth.tensor_rows((n, H, d), rows, synth.TAG_Q, 64, c, 0)
+        qd[[c * n + r for r in rows]] = to_dev(qs[c], "bf16")
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    o, lse = bca.attend_sequence(qd, kd, vd, n, W, workspace=ws)
+    torch.cuda.synchronize()
+    for c in checked:
+        hist = {x: kv[x] for x in range(max(0, c - W), c)}
+        eo, el = oracle.attend(qs[c], kv[c][0], kv[c][1], hist, t=c, W=W,
+                               scale=1.0 / math.sqrt(d), rows=list(range(len(rows))))
+        go = to_np(o[c * n:(c + 1) * n])[rows]
+        gl = to_np(lse[c])[:, rows]
+        assert_close(go, gl, eo, el, TOL["bf16"], f"64-chunk clip, chunk {c}")
+
+
 def test_sequence_refused_calls():
     import attention_bca_attend_amd as bca
     q = torch.zeros((32, 2, 64), dtype=torch.bfloat16, device="cuda")
