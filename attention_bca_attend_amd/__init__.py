@@ -16,7 +16,7 @@ import math
 import os
 
 __all__ = [
-    "F32", "BF16", "FP8_E4M3", "FP8_E4M3_BLOCK", "BcaError", "bca_cache_desc", "bca_window_spec",
+    "F32", "BF16", "FP8_E4M3", "FP8_E4M3_BLOCK", "INT8K_FP8V_BLOCK", "BcaError", "bca_cache_desc", "bca_window_spec",
     "bca_plan_info", "bca_cache_bytes", "bca_cache_create", "bca_cache_destroy",
     "bca_cache_set_kv_scales", "bca_append_chunk", "bca_attend_workspace_bytes", "bca_attend",
     "bca_append_chunk_rope", "bca_attend_rope_workspace_bytes", "bca_attend_rope",
@@ -29,7 +29,7 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbca.so")
 
-F32, BF16, FP8_E4M3, FP8_E4M3_BLOCK = 0, 1, 2, 3
+F32, BF16, FP8_E4M3, FP8_E4M3_BLOCK, INT8K_FP8V_BLOCK = 0, 1, 2, 3, 4
 BCA_OK = 0
 STATUS = {0: "BCA_OK", -1: "BCA_ERR_INVALID_ARG", -2: "BCA_ERR_OUT_OF_ORDER",
           -3: "BCA_ERR_WORKSPACE", -4: "BCA_ERR_UNSUPPORTED", -5: "BCA_ERR_HIP"}
@@ -356,7 +356,7 @@ def bca_attend_plan(handle: int, layer: int, spec) -> dict:
 
 
 _DT = {"fp32": F32, "f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "fp8_e4m3": FP8_E4M3,
-       "fp8_block": FP8_E4M3_BLOCK}
+       "fp8_block": FP8_E4M3_BLOCK, "int8k_block": INT8K_FP8V_BLOCK}
 
 
 class Cache:
@@ -394,8 +394,8 @@ class Cache:
         d = self.desc
         nb = d.ring_slots + d.has_ref
         tdt = {F32: torch.float32, BF16: torch.bfloat16, FP8_E4M3: torch.uint8,
-               FP8_E4M3_BLOCK: torch.uint8}[d.kv_dtype]
-        es = {F32: 4, BF16: 2, FP8_E4M3: 1, FP8_E4M3_BLOCK: 1}[d.kv_dtype]
+               FP8_E4M3_BLOCK: torch.uint8, INT8K_FP8V_BLOCK: torch.uint8}[d.kv_dtype]
+        es = {F32: 4, BF16: 2, FP8_E4M3: 1, FP8_E4M3_BLOCK: 1, INT8K_FP8V_BLOCK: 1}[d.kv_dtype]
         half = d.num_heads * nb * d.chunk_tokens * d.head_dim * es
         base = 2 * layer * half
         k = self.mem[base:base + half].view(tdt).view(d.num_heads, nb, d.chunk_tokens, d.head_dim)
@@ -404,12 +404,13 @@ class Cache:
         return k, v
 
     def block_scales(self, layer: int):
-        """FP8_E4M3_BLOCK caches: (K, V) scale views of one layer, fp32 [S+R][H]
-        (the table after the blocks: [L][K|V][S+R][H])."""
+        """Per-block caches (FP8_E4M3_BLOCK, INT8K_FP8V_BLOCK): (K, V) scale
+        views of one layer, fp32 [S+R][H] (the table after the blocks:
+        [L][K|V][S+R][H])."""
         import torch
         d = self.desc
-        if d.kv_dtype != FP8_E4M3_BLOCK:
-            raise BcaError(-1, "only FP8_E4M3_BLOCK caches keep scales per block")
+        if d.kv_dtype not in (FP8_E4M3_BLOCK, INT8K_FP8V_BLOCK):
+            raise BcaError(-1, "only per-block caches keep scales per block")
         nb = d.ring_slots + d.has_ref
         base = 2 * d.num_layers * d.num_heads * nb * d.chunk_tokens * d.head_dim
         per = nb * d.num_heads * 4

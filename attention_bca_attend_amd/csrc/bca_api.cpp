@@ -64,11 +64,15 @@ size_t elem_size(int32_t dt) {
     case BCA_BF16: return 2;
     case BCA_FP8_E4M3: return 1;
     case BCA_FP8_E4M3_BLOCK: return 1;
+    case BCA_INT8K_FP8V_BLOCK: return 1;
   }
   return 0;
 }
 
-bool is_fp8(int32_t kv) { return kv == BCA_FP8_E4M3 || kv == BCA_FP8_E4M3_BLOCK; }
+// Caches with one scale per (layer, block, head), taken from each appended chunk.
+bool is_blk(int32_t kv) { return kv == BCA_FP8_E4M3_BLOCK || kv == BCA_INT8K_FP8V_BLOCK; }
+// 8-bit caches (served by the fp8 attention kernel).
+bool is_fp8(int32_t kv) { return kv == BCA_FP8_E4M3 || is_blk(kv); }
 
 bool desc_ok(const bca_cache_desc* d, std::string* why) {
   auto bad = [&](const char* m) {
@@ -111,14 +115,14 @@ size_t half_layer_bytes(const bca_cache_desc& d) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// FP8_E4M3_BLOCK: the scale table after the blocks, fp32 [L][K|V][S+R][H].
+// Per-block caches: the scale table after the blocks, fp32 [L][K|V][S+R][H].
 size_t block_scale_bytes(const bca_cache_desc& d) {
-  if (d.kv_dtype != BCA_FP8_E4M3_BLOCK) return 0;
+  if (!is_blk(d.kv_dtype)) return 0;
   const size_t n = (size_t)d.num_layers * 2 * (d.ring_slots + d.has_ref) * d.num_heads * 4;
   return (n + 255) & ~(size_t)255;
 }
 
-// Key tiles of one block: FP8_E4M3_BLOCK pads every visible block to whole
+// Key tiles of one block: per-block caches pad every visible block to whole
 // tiles, so that each tile has one block's scales.
 int block_tiles(const bca_cache_desc& d) { return (d.chunk_tokens + 63) / 64; }
 
@@ -134,7 +138,7 @@ Kern kernel_for(int32_t qkv, int32_t kv) {
 
 bool pair_supported(int32_t qkv, int32_t kv) {
   return (qkv == BCA_F32 && kv == BCA_F32) || (qkv == BCA_BF16 && kv == BCA_BF16) ||
-         (qkv == BCA_BF16 && kv == BCA_FP8_E4M3) || (qkv == BCA_BF16 && kv == BCA_FP8_E4M3_BLOCK);
+         (qkv == BCA_BF16 && is_fp8(kv));
 }
 
 int wgs_per_cu(Kern k) {
@@ -189,12 +193,12 @@ size_t fp8_stage_bytes(const bca_cache_desc& d) {
   return 2 * one;
 }
 
-// FP8_E4M3_BLOCK: the current chunk's own scales [K|V][H] after its copy.
+// Per-block caches: the current chunk's own scales [K|V][H] after its copy.
 size_t cur_scale_bytes(const bca_cache_desc& d) {
   return ((size_t)2 * d.num_heads * 4 + 255) & ~(size_t)255;
 }
 
-// FP8_E4M3_BLOCK scale table of one layer's K (kv 0) or V (kv 1): [S+R][H].
+// Per-block scale table of one layer's K (kv 0) or V (kv 1): [S+R][H].
 float* block_scales(const bca_cache* c, int32_t layer, int kv) {
   const bca_cache_desc& d = c->d;
   float* t = reinterpret_cast<float*>(c->mem + 2 * (size_t)d.num_layers * half_layer_bytes(d));
@@ -271,9 +275,10 @@ bca_status make_plan(const bca_cache* c, int32_t layer, const bca_window_spec* s
   p.nk = p.nvis * n;
 
   // runs of the cache part: consecutive physical blocks share one run
-  // (FP8_E4M3_BLOCK: one run per block, each padded to whole key tiles)
+  // (per-block caches: one run per block, each padded to whole key tiles)
   p.nruns = 0;
-  p.blk = d.kv_dtype == BCA_FP8_E4M3_BLOCK ? 1 : 0;
+  p.blk = is_blk(d.kv_dtype) ? 1 : 0;
+  p.i8k = d.kv_dtype == BCA_INT8K_FP8V_BLOCK ? 1 : 0;
   p.tpb = block_tiles(d);
   if (p.blk) {
     for (int i = 0; i + 1 < p.nvis; ++i) {
@@ -373,8 +378,8 @@ bca_status bca_cache_destroy(bca_cache* cache) {
 bca_status bca_cache_set_kv_scales(bca_cache* c, int32_t layer, const float* k_scale,
                                    const float* v_scale) {
   if (!c) return fail(BCA_ERR_INVALID_ARG, "cache is NULL");
-  if (c->d.kv_dtype == BCA_FP8_E4M3_BLOCK)
-    return fail(BCA_ERR_UNSUPPORTED, "FP8_E4M3_BLOCK caches take their scales from the appends");
+  if (is_blk(c->d.kv_dtype))
+    return fail(BCA_ERR_UNSUPPORTED, "per-block caches take their scales from the appends");
   if (c->d.kv_dtype != BCA_FP8_E4M3)
     return fail(BCA_ERR_INVALID_ARG, "scales apply to FP8_E4M3 caches only");
   if (!layer_ok(c, layer)) return fail(BCA_ERR_INVALID_ARG, "layer %d out of range", layer);
@@ -461,10 +466,11 @@ bca_status append_impl(bca_cache* c, int32_t layer, int64_t chunk_id, int32_t is
       a.k_scale[h] = c->k_scale[(size_t)layer * d.num_heads + h];
       a.v_scale[h] = c->v_scale[(size_t)layer * d.num_heads + h];
     }
-  if (kv == BCA_FP8_E4M3_BLOCK) {
+  if (is_blk(kv)) {
     if (rope)
-      return fail(BCA_ERR_UNSUPPORTED, "no rotary append into an FP8_E4M3_BLOCK cache");
+      return fail(BCA_ERR_UNSUPPORTED, "no rotary append into a per-block 8-bit cache");
     a.dev_scales = 1;
+    a.k_int8 = kv == BCA_INT8K_FP8V_BLOCK ? 1 : 0;
     a.host_blk = blk;
     a.ksc = block_scales(c, layer, 0);
     a.vsc = block_scales(c, layer, 1);
@@ -529,8 +535,9 @@ bca_status bca_append_chunk_dev(bca_cache* c, int32_t layer, const int64_t* d_ch
       a.k_scale[h] = c->k_scale[(size_t)layer * d.num_heads + h];
       a.v_scale[h] = c->v_scale[(size_t)layer * d.num_heads + h];
     }
-  if (kv == BCA_FP8_E4M3_BLOCK) {
+  if (is_blk(kv)) {
     a.dev_scales = 1;
+    a.k_int8 = kv == BCA_INT8K_FP8V_BLOCK ? 1 : 0;
     a.ksc = block_scales(c, layer, 0);
     a.vsc = block_scales(c, layer, 1);
   }
@@ -604,7 +611,7 @@ size_t bca_attend_workspace_bytes(const bca_cache* c, const bca_window_spec* s) 
   // all ring slots, the reference and the current chunk.
   size_t worst = 0;
   const int max_blocks = S + c->d.has_ref + 1;
-  const bool blk = c->d.kv_dtype == BCA_FP8_E4M3_BLOCK;
+  const bool blk = is_blk(c->d.kv_dtype);
   for (int blocks = 1; blocks <= max_blocks; ++blocks) {
     const int64_t cache_keys = blk ? (int64_t)(blocks - 1) * block_tiles(c->d) * 64
                                    : (int64_t)(blocks - 1) * n;
@@ -675,8 +682,8 @@ bca_status attend_impl(const bca_cache* c, int32_t layer, const bca_window_spec*
       return fail(BCA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
                   need);
   }
-  if (rope && d.kv_dtype == BCA_FP8_E4M3_BLOCK)
-    return fail(BCA_ERR_UNSUPPORTED, "no rotary attention over an FP8_E4M3_BLOCK cache");
+  if (rope && is_blk(d.kv_dtype))
+    return fail(BCA_ERR_UNSUPPORTED, "no rotary attention over a per-block 8-bit cache");
   if (rope) {
     RopeStageArgs r;
     std::memset(&r, 0, sizeof r);
@@ -748,6 +755,7 @@ bca_status attend_impl(const bca_cache* c, int32_t layer, const bca_window_spec*
     }
   if (p.blk) {
     a.blk = 1;
+    a.i8k = p.i8k;
     a.tpb = p.tpb;
     a.nvis_cache = p.nvis - 1;
     a.ksc = block_scales(c, layer, 0);

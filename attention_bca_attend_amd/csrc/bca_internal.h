@@ -53,7 +53,8 @@ struct Plan {
   Kern kern;
   int32_t seq;                      // 1: a bca_attend_sequence launch (token-major cache rows)
   int32_t devt;                     // 1: visible slots derived on the device (bca_attend_dev)
-  int32_t blk;                      // 1: FP8_E4M3_BLOCK cache (tiles aligned to blocks)
+  int32_t blk;                      // 1: per-block 8-bit cache (tiles aligned to blocks)
+  int32_t i8k;                      // 1: INT8K_FP8V_BLOCK (K int8, Q K^T on int8 MFMA)
   int32_t tpb;                      // key tiles per block when blk
   int32_t nvis;                     // visible blocks, current included
   int32_t vis_block[kMaxBlocks];    // physical block (S = reference, -1 = current)
@@ -111,11 +112,11 @@ struct AttnArgs {
   Run runs[kMaxBlocks];
   float k_scale[kMaxHeadsFp8];  // fp8 cache: dequantisation scale per head
   float v_scale[kMaxHeadsFp8];
-  // FP8_E4M3_BLOCK: every visible cache block is its own run, padded to tpb
+  // Per-block caches: every visible cache block is its own run, padded to tpb
   // whole key tiles; ksc/vsc are the layer's scale tables [S+R][H], cur_sc the
   // current chunk's scales [K|V][H]; vis_blk the physical block of each of the
   // nvis_cache visible cache blocks.
-  int32_t blk, tpb, nvis_cache;
+  int32_t blk, i8k, tpb, nvis_cache;
   const float* ksc;
   const float* vsc;
   const float* cur_sc;
@@ -149,10 +150,11 @@ struct AppendArgs {
   const int64_t* dev_chunk;
   int32_t slots;
   int64_t block_elems;
-  // Scales from device memory (FP8_E4M3_BLOCK, and the current chunk's copy):
+  // Scales from device memory (per-block caches, and the current chunk's copy):
   // ksc/vsc point at [blocks][H] tables; the block is host_blk, or
   // (id mod slots) with dev_chunk. append_amax_kernel writes them first.
   int32_t dev_scales;
+  int32_t k_int8;          // 1: K codes are int8 (scale = max |x| / 127), V stays e4m3
   int32_t host_blk;
   float* ksc;
   float* vsc;

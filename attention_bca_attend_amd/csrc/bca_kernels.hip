@@ -974,6 +974,119 @@ __device__ __forceinline__ void f8_gemm(F8State<D>& st, const unsigned char* SV,
   }
 }
 
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
+
+// INT8K_FP8V_BLOCK: the same phase with Q K^T on the int8 matrix cores
+// (v_mfma_i32_32x32x32_i8, 16 bytes of A and B per lane). The 32 K bytes a
+// lane holds per key block and 64-dim step (dims 64 ks + 32 h .. + 31, as for
+// e4m3) feed two 32-deep MFMAs against the same dims of the Q terms. Pass 1
+// takes Q's hi term into int32 accumulators, which are then shifted by 8 (lo
+// counts 2^-8 of hi's unit); pass 2 adds the lo term. A score is thus
+// sum_d k (256 hi + lo), exact in int32 (at most 127 * 32639 * D < 2^31 for
+// D = 128), and is converted to float once. P V is the fp8 kernel's.
+template <int D, bool PV, bool QK>
+__device__ __forceinline__ void i8_gemm(F8State<D>& st, const unsigned char* SV,
+                                        const unsigned char* SK, const int (&koff)[2 * (D / 64)],
+                                        const int (&voff)[D / 32],
+                                        const i32x8_t (&qf)[2][D / 64]) {
+  using C = F8Cfg<D>;
+  constexpr int NPV = PV ? D / 32 : 0;
+  constexpr int NQK = QK ? 2 * C::KS : 0;
+  constexpr int NSTEP = NPV > NQK ? NPV : NQK;
+  i32x8_t vf[NSTEP + 1], kf[NSTEP + 1];
+  auto load_v = [&](int i) {
+    if (i < NPV) {
+      const unsigned char* vp = SV + voff[i];
+      i32x2_t t4[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        t4[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(vp + 2048 * t));
+      vf[i] = i32x8_t{t4[0][0], t4[0][1], t4[1][0], t4[1][1],
+                      t4[2][0], t4[2][1], t4[3][0], t4[3][1]};
+    }
+  };
+  auto load_k = [&](int i) {
+    if (i < NQK) {
+      const int kb = i & 1, ks = i >> 1;
+      const unsigned char* kp = SK + kb * 32 * C::ROWB;
+      const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(kp + koff[2 * ks]);
+      const i32x4_t h4 = *reinterpret_cast<const i32x4_t*>(kp + koff[2 * ks + 1]);
+      kf[i] = i32x8_t{lo[0], lo[1], lo[2], lo[3], h4[0], h4[1], h4[2], h4[3]};
+    }
+  };
+  auto mf = [](const i32x8_t& x, const i32x8_t& y, const f32x16_t& c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x, y, c, 0, 0, 0, 0, 0, 0);
+  };
+  // the two 16-byte halves of a lane's 32 bytes: dims +0..15 and +16..31
+  auto mi = [](const i32x8_t& x, const i32x8_t& y, int half, const i32x16_t& c) {
+    const i32x4_t xa = half ? i32x4_t{x[4], x[5], x[6], x[7]} : i32x4_t{x[0], x[1], x[2], x[3]};
+    const i32x4_t ya = half ? i32x4_t{y[4], y[5], y[6], y[7]} : i32x4_t{y[0], y[1], y[2], y[3]};
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(xa, ya, c, 0, 0, 0);
+  };
+  i32x16_t acc0 = i32x16_t{}, acc1 = i32x16_t{};
+  load_v(0);
+  load_k(0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < NSTEP; ++i) {
+    load_v(i + 1);
+    load_k(i + 1);
+#pragma unroll
+    for (int part = 0; part < 2; ++part) {
+      if (i < NPV) st.o[i] = mf(vf[i], st.pf[part], st.o[i]);
+      if (i < NQK) {
+        if (i & 1)
+          acc1 = mi(kf[i], qf[0][i >> 1], part, acc1);
+        else
+          acc0 = mi(kf[i], qf[0][i >> 1], part, acc0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (QK) {
+    // pass 2 reads the K fragments from LDS again (the stage stays valid until
+    // the phase's barrier) rather than holding all of them in registers
+    i32x8_t kg[NQK + 1];
+    auto reload_k = [&](int i) {
+      if (i < NQK) {
+        const int kb = i & 1, ks = i >> 1;
+        const unsigned char* kp = SK + kb * 32 * C::ROWB;
+        const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(kp + koff[2 * ks]);
+        const i32x4_t h4 = *reinterpret_cast<const i32x4_t*>(kp + koff[2 * ks + 1]);
+        kg[i] = i32x8_t{lo[0], lo[1], lo[2], lo[3], h4[0], h4[1], h4[2], h4[3]};
+      }
+    };
+    reload_k(0);
+    acc0 <<= 8;
+    acc1 <<= 8;
+#pragma unroll
+    for (int i = 0; i < NQK; ++i) {
+      reload_k(i + 1);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        if (i & 1)
+          acc1 = mi(kg[i], qf[1][i >> 1], half, acc1);
+        else
+          acc0 = mi(kg[i], qf[1][i >> 1], half, acc0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    st.s[0] = __builtin_convertvector(acc0, f32x16_t);
+    st.s[1] = __builtin_convertvector(acc1, f32x16_t);
+  }
+}
+
+template <int D, bool I8K, bool PV, bool QK>
+__device__ __forceinline__ void x8_gemm(F8State<D>& st, const unsigned char* SV,
+                                        const unsigned char* SK, const int (&koff)[2 * (D / 64)],
+                                        const int (&voff)[D / 32],
+                                        const i32x8_t (&qf)[2][D / 64]) {
+  if constexpr (I8K)
+    i8_gemm<D, PV, QK>(st, SV, SK, koff, voff, qf);
+  else
+    f8_gemm<D, PV, QK>(st, SV, SK, koff, voff, qf);
+}
+
 // Online softmax of the fp8 kernel's tile, c per lane (the query row's scale
 // included). The running maximum moves only when a tile exceeds it by more
 // than 4; P is scaled by 2^4, so P <= 2^8 stays within e4m3 and values down
@@ -1041,8 +1154,9 @@ __device__ __forceinline__ void f8_softmax(F8State<D>& st, int lim, int hi, floa
 // multiplies the tile's softmax constant, and the V scale relative to the
 // unit's largest (s_ref) enters P as an exponent offset, with the row sum
 // corrected per tile and s_ref applied at normalisation.
-template <int D, bool BLK, bool DEVT>
+template <int D, bool BLK, bool DEVT, bool I8K = false>
 __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
+  static_assert(!I8K || (BLK && !DEVT), "int8 K comes with per-block scales");
   using C = F8Cfg<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::NSTAGE * C::STAGE];
   // BLK: the unit's K scale per block, and per block the exponent offset
@@ -1120,26 +1234,55 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
         for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[e]));
       }
       amax = xhalf_max(amax);
-      const float qs = amax > 0.f ? amax * (1.0f / 448.0f) : 1.0f;
-      const float qinv = amax > 0.f ? 448.0f / amax : 1.0f;
+      if constexpr (I8K) {
+        // two int8 terms per element: y = x 127 / amax, hi = rne(y), lo =
+        // rne(256 (y - hi)) (y - hi is exact), so x = (amax / 127)(hi + lo / 256)
+        // to within 2^-9 of the row's code unit
+        const float qs = amax > 0.f ? amax / 127.0f : 1.0f;
+        const float qinv = amax > 0.f ? 127.0f / amax : 1.0f;
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks)
+        for (int ks = 0; ks < C::KS; ++ks)
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const bf16x8_t v = __builtin_bit_cast(bf16x8_t, raw[4 * ks + x]);
-          float f[8];
+          for (int x = 0; x < 4; ++x) {
+            const bf16x8_t v = __builtin_bit_cast(bf16x8_t, raw[4 * ks + x]);
+            unsigned wh[2] = {0u, 0u}, wl[2] = {0u, 0u};
 #pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] = fminf(fmaxf((float)v[e] * qinv, -448.f), 448.f);
-          const i32x2_t lo4 = split_e4m3x4(f[0], f[1], f[2], f[3]);
-          const i32x2_t hi4 = split_e4m3x4(f[4], f[5], f[6], f[7]);
-          qf[0][ks][2 * x] = lo4[0];
-          qf[1][ks][2 * x] = lo4[1];
-          qf[0][ks][2 * x + 1] = hi4[0];
-          qf[1][ks][2 * x + 1] = hi4[1];
-        }
-      // base-2 scale of the raw products: softmax scale, K scale, Q row scale
-      // (BLK: the K scale comes per tile)
-      c = BLK ? a.scale_log2 * qs : a.scale_log2 * a.k_scale[h] * qs;
+            for (int e = 0; e < 8; ++e) {
+              const float y = fminf(fmaxf((float)v[e] * qinv, -127.f), 127.f);
+              const float hq = __builtin_rintf(y);
+              const float lq = fminf(fmaxf(__builtin_rintf((y - hq) * 256.0f), -127.f), 127.f);
+              wh[e >> 2] |= ((unsigned)(int)hq & 0xffu) << (8 * (e & 3));
+              wl[e >> 2] |= ((unsigned)(int)lq & 0xffu) << (8 * (e & 3));
+            }
+            qf[0][ks][2 * x] = (int)wh[0];
+            qf[0][ks][2 * x + 1] = (int)wh[1];
+            qf[1][ks][2 * x] = (int)wl[0];
+            qf[1][ks][2 * x + 1] = (int)wl[1];
+          }
+        // an int32 score is 256 / qs times the products in the K codes' unit
+        c = a.scale_log2 * qs * (1.0f / 256.0f);
+      } else {
+        const float qs = amax > 0.f ? amax * (1.0f / 448.0f) : 1.0f;
+        const float qinv = amax > 0.f ? 448.0f / amax : 1.0f;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const bf16x8_t v = __builtin_bit_cast(bf16x8_t, raw[4 * ks + x]);
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = fminf(fmaxf((float)v[e] * qinv, -448.f), 448.f);
+            const i32x2_t lo4 = split_e4m3x4(f[0], f[1], f[2], f[3]);
+            const i32x2_t hi4 = split_e4m3x4(f[4], f[5], f[6], f[7]);
+            qf[0][ks][2 * x] = lo4[0];
+            qf[1][ks][2 * x] = lo4[1];
+            qf[0][ks][2 * x + 1] = hi4[0];
+            qf[1][ks][2 * x + 1] = hi4[1];
+          }
+        // base-2 scale of the raw products: softmax scale, K scale, Q row scale
+        // (BLK: the K scale comes per tile)
+        c = BLK ? a.scale_log2 * qs : a.scale_log2 * a.k_scale[h] * qs;
+      }
     }
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     float sv_ref = 1.f;
@@ -1219,7 +1362,7 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
       begin_phase(0);
       if (wave_rows) {
         __builtin_amdgcn_s_setprio(1);
-        f8_gemm<D, false, true>(st, nullptr, stage(0), koff, voff, qf);
+        x8_gemm<D, I8K, false, true>(st, nullptr, stage(0), koff, voff, qf);
         __builtin_amdgcn_s_setprio(0);
       }
       end_phase(0);
@@ -1230,7 +1373,7 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
         begin_phase(2 * r);
         if (wave_rows) {
           __builtin_amdgcn_s_setprio(1);
-          f8_gemm<D, true, true>(st, stage(r - 1), stage(r), koff, voff, qf);
+          x8_gemm<D, I8K, true, true>(st, stage(r - 1), stage(r), koff, voff, qf);
           __builtin_amdgcn_s_setprio(0);
         }
         end_phase(2 * r);
@@ -1241,7 +1384,7 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
       begin_phase(2 * nt);
       if (wave_rows) {
         __builtin_amdgcn_s_setprio(1);
-        f8_gemm<D, true, false>(st, stage(nt - 1), nullptr, koff, voff, qf);
+        x8_gemm<D, I8K, true, false>(st, stage(nt - 1), nullptr, koff, voff, qf);
         __builtin_amdgcn_s_setprio(0);
       }
       end_phase(2 * nt);
@@ -1253,7 +1396,7 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
       begin_phase(1);
       if (wave_rows) {
         __builtin_amdgcn_s_setprio(1);
-        f8_gemm<D, false, true>(st, nullptr, stage(0), koff, voff, qf);
+        x8_gemm<D, I8K, false, true>(st, nullptr, stage(0), koff, voff, qf);
         __builtin_amdgcn_s_setprio(0);
       }
       end_phase(1);
@@ -1264,7 +1407,7 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
         begin_phase(2 * r + 1);
         if (wave_rows) {
           __builtin_amdgcn_s_setprio(1);
-          f8_gemm<D, true, true>(st, stage(r - 1), stage(r), koff, voff, qf);
+          x8_gemm<D, I8K, true, true>(st, stage(r - 1), stage(r), koff, voff, qf);
           __builtin_amdgcn_s_setprio(0);
         }
         end_phase(2 * r + 1);
@@ -1275,7 +1418,7 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
       begin_phase(2 * nt + 1);
       if (wave_rows) {
         __builtin_amdgcn_s_setprio(1);
-        f8_gemm<D, true, false>(st, stage(nt - 1), nullptr, koff, voff, qf);
+        x8_gemm<D, I8K, true, false>(st, stage(nt - 1), nullptr, koff, voff, qf);
         __builtin_amdgcn_s_setprio(0);
       }
       end_phase(2 * nt + 1);
@@ -1703,6 +1846,19 @@ __device__ __forceinline__ uint2 e4m3x8(const float (&x)[8], float s) {
   return make_uint2((unsigned)lo, (unsigned)hi);
 }
 
+// bf16 -> symmetric int8 with the head's scale: code = round_to_nearest_even(
+// x / s) clamped to [-127, 127], NaN -> 0; byte i = element i.
+__device__ __forceinline__ uint2 int8x8(const float (&x)[8], float s) {
+  unsigned w[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float t = x[i] / s;
+    const float r = t == t ? fminf(fmaxf(__builtin_rintf(t), -127.0f), 127.0f) : 0.0f;
+    w[i >> 2] |= ((unsigned)(int)r & 0xffu) << (8 * (i & 3));
+  }
+  return make_uint2(w[0], w[1]);
+}
+
 // Block index of an append's scales: host_blk, or (id mod slots) for a
 // device-side chunk id (negative ids write nothing, as for the codes).
 __device__ __forceinline__ int append_scale_block(const AppendArgs& a) {
@@ -1711,9 +1867,9 @@ __device__ __forceinline__ int append_scale_block(const AppendArgs& a) {
   return id < 0 ? -1 : (int)(id % a.slots);
 }
 
-// Scales of an FP8_E4M3_BLOCK append (and of the current chunk's e4m3 copy):
-// per head, scale = (largest |x| of the chunk's rows of that head) / 448,
-// 1 when that maximum is 0 or not finite. One work group of 1024 threads per
+// Scales of a per-block append (and of the current chunk's 8-bit copy): per
+// head, scale = (largest |x| of the chunk's rows of that head) / 448 (/ 127
+// for int8 K), 1 when that maximum is 0 or not finite (any NaN or infinity). One work group of 1024 threads per
 // (head, K|V), each thread with up to 8 row loads in flight; blockIdx.y
 // selects K (0) or V (1).
 template <int D>
@@ -1738,7 +1894,12 @@ __global__ __launch_bounds__(1024) void append_amax_kernel(const AppendArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)v[u][e]));
+      for (int e = 0; e < 8; ++e) {
+        // a NaN counts as an infinite magnitude: the maximum is then not
+        // finite and the scale 1, as for an infinity
+        const float x = (float)v[u][e];
+        amax = fmaxf(amax, x == x ? fabsf(x) : INFINITY);
+      }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
@@ -1749,12 +1910,14 @@ __global__ __launch_bounds__(1024) void append_amax_kernel(const AppendArgs a) {
     float m = wmax[0];
 #pragma unroll
     for (int w = 1; w < NT / 64; ++w) m = fmaxf(m, wmax[w]);
-    const float sc = (m > 0.f && m <= 3.402823466e38f) ? m / 448.0f : 1.0f;
+    const float qmax = (!isv && a.k_int8) ? 127.0f : 448.0f;
+    const float sc = (m > 0.f && m <= 3.402823466e38f) ? m / qmax : 1.0f;
     (isv ? a.vsc : a.ksc)[(int64_t)bi * a.H + h] = sc;
   }
 }
 
-// The e4m3 append; blockIdx.y + kv0 selects K (0) or V (1).
+// The 8-bit append (e4m3, or int8 for the K of an INT8K_FP8V_BLOCK cache);
+// blockIdx.y + kv0 selects K (0) or V (1).
 template <int D>
 __global__ __launch_bounds__(256) void append_fp8_kernel(const AppendArgs a, int kv0) {
   constexpr int G = D / 8;
@@ -1777,7 +1940,7 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(const AppendArgs a, int
         2, y);
   unsigned char* dst = static_cast<unsigned char*>(isv ? a.vdst : a.kdst) +
                        (blk + (int64_t)h * a.head_stride_elems + (int64_t)r * D + g * 8);
-  *reinterpret_cast<uint2*>(dst) = e4m3x8(y, s);
+  *reinterpret_cast<uint2*>(dst) = (!isv && a.k_int8) ? int8x8(y, s) : e4m3x8(y, s);
 }
 
 // Rotary embedding of the current chunk's Q (blockIdx.y 0) and K (1) into
@@ -1868,6 +2031,7 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
         if (a.blk) {
           // the chunk's own per-head scales, as an append would take them
           q.dev_scales = 1;
+          q.k_int8 = a.i8k;
           q.host_blk = 0;
           q.ksc = const_cast<float*>(a.cur_sc);
           q.vsc = const_cast<float*>(a.cur_sc) + a.H;
@@ -1876,7 +2040,10 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
         const int64_t total = (int64_t)a.n * a.H * (D / 8);
         hipLaunchKernelGGL(append_fp8_kernel<D>, dim3((unsigned)((total + 255) / 256), 2),
                            dim3(256), 0, s, q, 0);
-        if (a.blk)
+        if (a.blk && a.i8k)
+          hipLaunchKernelGGL((attn_fp8_kernel<D, true, false, true>), dim3(p.wgs), dim3(512), 0,
+                             s, a);
+        else if (a.blk)
           hipLaunchKernelGGL((attn_fp8_kernel<D, true, false>), dim3(p.wgs), dim3(512), 0, s, a);
         else if (p.devt)
           hipLaunchKernelGGL((attn_fp8_kernel<D, false, true>), dim3(p.wgs), dim3(512), 0, s, a);
@@ -1959,7 +2126,7 @@ int launch_append(bca_dtype in, bca_dtype kv, int head_dim, const AppendArgs& a,
   const dim3 grid((unsigned)((total + 255) / 256), 2 - kv0);
   const dim3 rgrid((unsigned)(((int64_t)a.n * (head_dim / 8) + 127) / 128), 1,
                    (unsigned)((a.H + kRopeHeads - 1) / kRopeHeads));
-  if (kv == BCA_FP8_E4M3 || kv == BCA_FP8_E4M3_BLOCK) {
+  if (kv == BCA_FP8_E4M3 || kv == BCA_FP8_E4M3_BLOCK || kv == BCA_INT8K_FP8V_BLOCK) {
     if (head_dim != 128 || in != BCA_BF16) return -1;
     if (a.dev_scales)
       hipLaunchKernelGGL(append_amax_kernel<128>, dim3((unsigned)a.H, 2), dim3(1024), 0, s, a);

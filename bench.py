@@ -50,7 +50,9 @@ if ROOT not in sys.path:
 METRIC = "block-causal attention TFLOP/s & µs per chunk-layer; % of MFMA peak"
 # MI355X dense MFMA peak, published: bf16 for a bf16 cache; an fp8 cache
 # contracts on the fp8 matrix cores, priced against the fp8 dense peak.
-PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "fp8_block": 5033.2}
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "fp8_block": 5033.2,
+               # Q K^T on the int8 matrix cores (5.0 POP/s dense), P V on fp8 (5.0)
+               "int8k_block": 5033.2}
 PEAK_HBM_GBS = 8000.0
 
 CONFIGS = {
@@ -68,6 +70,8 @@ CONFIGS = {
             L=30, steps_per_chunk=1, kv="fp8_block"),
     7: dict(workload="wantofight_bf16_stream64_graph", H=12, d=128, n=1536, S=2, W=2, R=0, G=0,
             L=30, steps_per_chunk=4, kv="bf16", graph=True),
+    9: dict(workload="matrixgame4_int8k_fp8v_block_chunk", H=24, d=128, n=405, S=20, W=20, R=1,
+            G=4, L=30, steps_per_chunk=1, kv="int8k_block"),
     6: dict(workload="wantofight_bf16_sequence8", H=12, d=128, n=1536, C=8, W=2, P=0, G=0, L=30,
             kv="bf16", sequence=True),
 }
@@ -112,14 +116,19 @@ def cpu_baseline(cache, cfg, q0, k0, v0, t):
         hist = {c: (dec[K[:, s].cpu().numpy()] * scale, dec[V[:, s].cpu().numpy()] * scale)
                 for c, s in ((c, c % cfg["S"]) for c in hist)}
         ref = (dec[K[:, cfg["S"]].cpu().numpy()] * scale, dec[V[:, cfg["S"]].cpu().numpy()] * scale)
-    if cfg["kv"] == "fp8_block":
-        # codes with one scale per (block, head)
+    if cfg["kv"] in ("fp8_block", "int8k_block"):
+        # codes with one scale per (block, head); int8 K codes on "int8k_block"
         dec = oracle.e4m3_decode(np.arange(256, dtype=np.uint8))
         KS, VS = (x.cpu().numpy() for x in cache.block_scales(0))
         deq = lambda codes, sc: dec[codes.cpu().numpy()] * sc[:, None, None]  # noqa: E731
-        hist = {c: (deq(K[:, c % cfg["S"]], KS[c % cfg["S"]]),
+        if cfg["kv"] == "int8k_block":
+            deqk = lambda codes, sc: (codes.cpu().numpy().view(np.int8).astype(np.float64)  # noqa: E731
+                                      * sc[:, None, None])
+        else:
+            deqk = deq
+        hist = {c: (deqk(K[:, c % cfg["S"]], KS[c % cfg["S"]]),
                     deq(V[:, c % cfg["S"]], VS[c % cfg["S"]])) for c in hist}
-        ref = (deq(K[:, cfg["S"]], KS[cfg["S"]]), deq(V[:, cfg["S"]], VS[cfg["S"]]))
+        ref = (deqk(K[:, cfg["S"]], KS[cfg["S"]]), deq(V[:, cfg["S"]], VS[cfg["S"]]))
     qn, kn, vn = (x.float().cpu().numpy() for x in (q0, k0, v0))
     n_vis_blocks = 1 + sum(1 for c in hist if t - W <= c <= t - 1) + (1 if cfg["R"] else 0)
     nk = n_vis_blocks * n
@@ -560,7 +569,7 @@ def main():
     steps = args.steps if args.steps is not None else (64 if args.config == 3 else 5)
     H, d, n, S, W, R, G, L = (cfg[k] for k in ("H", "d", "n", "S", "W", "R", "G", "L"))
     spc = cfg["steps_per_chunk"]
-    fp8 = cfg["kv"] in ("fp8", "fp8_block")
+    fp8 = cfg["kv"] in ("fp8", "fp8_block", "int8k_block")
     rope_base = cfg.get("rope")
     rope = (lambda t: (rope_base, t * n)) if rope_base else (lambda t: None)
     torch.cuda.set_device(0)
@@ -662,7 +671,9 @@ def main():
         "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": ("bf16" if not fp8 else "bf16 q / fp8-e4m3 kv" if cfg["kv"] == "fp8"
-                  else "bf16 q / fp8-e4m3 kv, scales per block"), "data": "synthetic",
+                  else "bf16 q / fp8-e4m3 kv, scales per block" if cfg["kv"] == "fp8_block"
+                  else "bf16 q (int8 x2 in QK) / int8 k / fp8-e4m3 v, scales per block"),
+        "data": "synthetic",
         "config": {"workload": cfg["workload"], "heads": H, "head_dim": d, "chunk_tokens": n,
                    "visible_keys": nk, "ring_slots": S, "history": W, "reference": bool(R),
                    "segments": G if G else "auto", "layers": L,
@@ -678,6 +689,8 @@ def main():
             ("bca_attend_rope: rope_stage_kernel + " if rope_base else "bca_attend: ")
             + ("attn_fp8_kernel + append_fp8_kernel (chunk copy)" if cfg["kv"] == "fp8"
                else "attn_fp8_kernel (block scales) + append_amax_kernel + "
+                    "append_fp8_kernel (chunk copy)" if cfg["kv"] == "fp8_block"
+               else "attn_fp8_kernel (int8 K, block scales) + append_amax_kernel + "
                     "append_fp8_kernel (chunk copy)" if fp8
                else "attn_bf16_kernel")
             + (" + merge_kernel" if plan["merge"] else "")),

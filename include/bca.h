@@ -38,7 +38,8 @@
  *       cache memory             : [L][K|V][H][S+R][n][d] in kv_dtype, R = has_ref;
  *                                  the reference chunk is physical block S.
  *   - Supported (qkv dtype, kv dtype) pairs: (F32, F32), (BF16, BF16),
- *     (BF16, FP8_E4M3). head_dim must be 64 or 128 (FP8_E4M3: 128).
+ *     (BF16, FP8_E4M3), (BF16, FP8_E4M3_BLOCK), (BF16, INT8K_FP8V_BLOCK).
+ *     head_dim must be 64 or 128 (8-bit caches: 128, at most 64 heads).
  *   - Every argument is validated on the host before anything is enqueued. On
  *     an error nothing is enqueued and the cache state is unchanged; the return
  *     value says which class of error, bca_last_error() gives the text.
@@ -76,8 +77,23 @@ typedef enum {
  * 448), so an append re-quantises only the block it writes ("Matrix-Game 4.0"
  * summary, technical novelty: 8-bit K/V per interval, only the changed
  * interval re-quantised). The scales live in the cache memory after the
- * blocks. */
-typedef enum { BCA_F32 = 0, BCA_BF16 = 1, BCA_FP8_E4M3 = 2, BCA_FP8_E4M3_BLOCK = 3 } bca_dtype;
+ * blocks.
+ * BCA_INT8K_FP8V_BLOCK: the same per-block scheme with K held as INT8 and V as
+ * e4m3 (the same summary: each interval caches INT8 K and FP8 V). K codes are
+ * symmetric int8, round to nearest even of fp32(x / scale) clamped to
+ * [-127, 127] (NaN -> 0), with the block's K scale = its largest magnitude per
+ * head over 127; V as in FP8_E4M3_BLOCK (over 448). Layout and scale table as
+ * FP8_E4M3_BLOCK. Attention quantises each query row to two int8 terms
+ * (about 15 significant bits) and takes Q K^T on the int8 matrix cores with
+ * int32 accumulation, one int-to-float conversion per score; P V stays on the
+ * fp8 matrix cores. */
+typedef enum {
+  BCA_F32 = 0,
+  BCA_BF16 = 1,
+  BCA_FP8_E4M3 = 2,
+  BCA_FP8_E4M3_BLOCK = 3,
+  BCA_INT8K_FP8V_BLOCK = 4
+} bca_dtype;
 
 typedef struct bca_cache bca_cache; /* opaque host handle */
 
@@ -137,9 +153,9 @@ bca_status bca_cache_set_kv_scales(bca_cache* cache, int32_t layer, const float*
  * prerequisite "causal autoregression and KV cache"; WanToFight review, rolling
  * KV cache, updated after each chunk).
  * in_dtype: F32 for an F32 cache, BF16 for BF16 and FP8_E4M3 caches (quantised
- * on the fly with the layer's scales) and for FP8_E4M3_BLOCK caches (the
- * block's per-head scales are first taken from this chunk, then it is
- * quantised with them; no rotary form).
+ * on the fly with the layer's scales) and for FP8_E4M3_BLOCK and
+ * INT8K_FP8V_BLOCK caches (the block's per-head scales are first taken from
+ * this chunk, then it is quantised with them; no rotary form).
  * Ordering: per layer, ring chunk ids are non-decreasing; an id equal to the
  * last one re-writes that chunk in place; a smaller id returns
  * BCA_ERR_OUT_OF_ORDER. chunk_id >= 0. For is_ref the id is recorded only. */
@@ -175,7 +191,10 @@ size_t bca_attend_workspace_bytes(const bca_cache* cache, const bca_window_spec*
  * into the output normalisation. FP8_E4M3_BLOCK: the current chunk is
  * quantised with its own per-head scales, every visible block is padded to
  * whole 64-key tiles so that each tile has one block's scales, and the
- * workspace also holds the chunk's scales ([K|V][H] fp32).
+ * workspace also holds the chunk's scales ([K|V][H] fp32). INT8K_FP8V_BLOCK:
+ * as FP8_E4M3_BLOCK, with the chunk's K copy in int8 and Q K^T on the int8
+ * matrix cores (Q as two int8 terms per row: hi = rne(x / s), lo =
+ * rne(256 (x / s - hi)), s = the row's largest magnitude over 127).
  * Errors: BCA_ERR_OUT_OF_ORDER when a chunk of the window may already have been
  * overwritten (the layer's newest ring id >= t - W + S).
  * The visible set is resolved on the host from the slot table's chunk ids each
@@ -363,9 +382,9 @@ bca_status bca_cache_slot_chunk(const bca_cache* cache, int32_t layer, int32_t s
 /* Declares the content of a slot without touching device memory, for callers
  * that filled the cache memory themselves (restoring a saved cache). Slot S
  * (with has_ref) is the reference block. chunk_id -1 empties the slot. The
- * layer's newest id is recomputed from the table. For an FP8_E4M3_BLOCK cache
- * the block's scales (the table after the blocks) are part of what the
- * caller restores. */
+ * layer's newest id is recomputed from the table. For FP8_E4M3_BLOCK and
+ * INT8K_FP8V_BLOCK caches the block's scales (the table after the blocks) are
+ * part of what the caller restores. */
 bca_status bca_cache_set_slot_chunk(bca_cache* cache, int32_t layer, int32_t slot,
                                     int64_t chunk_id);
 

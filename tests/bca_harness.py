@@ -11,7 +11,10 @@ import numpy as np
 import oracle
 import synth
 
-TOL = {"fp32": 1e-5, "bf16": 1e-2, "fp8": 5e-2, "fp8_block": 5e-2}
+TOL = {"fp32": 1e-5, "bf16": 1e-2, "fp8": 5e-2, "fp8_block": 5e-2, "int8k_block": 5e-2}
+
+# caches fed bf16 inputs
+BF16_IN = ("bf16", "fp8", "fp8_block", "int8k_block")
 
 # An 8-bit cache against the oracle run on what the cache holds (the kernel's
 # own error): 1e-2 plus the bf16 rounding of the output, 2^-9 relative for O
@@ -29,7 +32,7 @@ def log(msg: str) -> None:
 def to_dev(x: np.ndarray, dtype: str):
     import torch
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
-    t = t.to(torch.bfloat16) if dtype in ("bf16", "fp8", "fp8_block") else t
+    t = t.to(torch.bfloat16) if dtype in BF16_IN else t
     return t.cuda()
 
 
@@ -56,6 +59,25 @@ def fp8_stored(x, scales):
     for h in range(x.shape[1]):
         out[:, h, :] = tab[oracle.quant_e4m3(x[:, h, :], scales[h])] * scales[h]
     return out
+
+
+def int8_stored(x, scales):
+    """What an int8 K block holds for x [n][H][d], dequantised: the oracle's
+    int8 code times s_h per head."""
+    out = np.empty(x.shape, dtype=np.float64)
+    for h in range(x.shape[1]):
+        out[:, h, :] = oracle.quant_int8(x[:, h, :], float(scales[h])).astype(np.float64) * \
+            float(scales[h])
+    return out
+
+
+def block_stored(kind, k, v):
+    """(K, V) as a per-block cache holds them: scales from the oracle's rule
+    (K over 127 for int8 K, else 448; V over 448)."""
+    if kind == "int8k_block":
+        return (int8_stored(k, oracle.block_scales(k, qmax=127.0)),
+                fp8_stored(v, oracle.block_scales(v)))
+    return fp8_stored(k, oracle.block_scales(k)), fp8_stored(v, oracle.block_scales(v))
 
 
 class Sequence:
@@ -85,8 +107,8 @@ class Sequence:
                          outlier_frac=self.outlier_frac)
 
     def stored(self, k, v):
-        if self.dtype == "fp8_block":
-            return (fp8_stored(k, oracle.block_scales(k)), fp8_stored(v, oracle.block_scales(v)))
+        if self.dtype in ("fp8_block", "int8k_block"):
+            return block_stored(self.dtype, k, v)
         if self.dtype == "fp8" and self.scales is not None:
             return fp8_stored(k, self.scales[0]), fp8_stored(v, self.scales[1])
         return k.astype(np.float64), v.astype(np.float64)

@@ -516,8 +516,8 @@ def test_descriptor_limits_of_32_bit_offsets():
     assert bca.bca_cache_bytes(bca.bca_cache_desc(1, 32, 128, 1 << 17, 1, 0, bca.BF16)) > 0
 
 
-def test_block_scaled_fp8_cache_on_the_host():
-    B = bca.FP8_E4M3_BLOCK
+@pytest.mark.parametrize("B", [bca.FP8_E4M3_BLOCK, bca.INT8K_FP8V_BLOCK])
+def test_block_scaled_fp8_cache_on_the_host(B):
     d = bca.bca_cache_desc(3, 4, 128, 405, 20, 1, B)
     table = ((3 * 2 * 21 * 4 * 4 + 255) // 256) * 256
     assert bca.bca_cache_bytes(d) == 3 * 2 * 4 * 21 * 405 * 128 + table
@@ -585,10 +585,11 @@ def test_attend_dev_validates_before_launch():
         bca.bca_attend_dev(h, 0, spec, P, P, P, P, bca.BF16, P, 0, P + 16, ws, 0)
     assert e.value.status == -3
     bca.bca_cache_destroy(h)
-    h8, _ = make(S=3, R=0, dt=bca.FP8_E4M3_BLOCK, d=128, H=2, n=16)
-    for sl in range(3):
-        bca.bca_cache_set_slot_chunk(h8, 0, sl, sl)
-    with pytest.raises(BcaError) as e:
-        bca.bca_attend_dev(h8, 0, spec, P, P, P, P, bca.BF16, P, 0, P, 1 << 30, 0)
-    assert e.value.status == -4
-    bca.bca_cache_destroy(h8)
+    for dt in (bca.FP8_E4M3_BLOCK, bca.INT8K_FP8V_BLOCK):
+        h8, _ = make(S=3, R=0, dt=dt, d=128, H=2, n=16)
+        for sl in range(3):
+            bca.bca_cache_set_slot_chunk(h8, 0, sl, sl)
+        with pytest.raises(BcaError) as e:
+            bca.bca_attend_dev(h8, 0, spec, P, P, P, P, bca.BF16, P, 0, P, 1 << 30, 0)
+        assert e.value.status == -4
+        bca.bca_cache_destroy(h8)

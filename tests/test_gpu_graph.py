@@ -17,8 +17,8 @@ import pytest
 
 import oracle
 import synth
-from bca_harness import (FP8_CACHE_ABS, FP8_CACHE_REL, TOL, assert_close, fp8_stored, log,
-                         max_err, to_dev, to_np)
+from bca_harness import (FP8_CACHE_ABS, FP8_CACHE_REL, TOL, assert_close, block_stored,
+                         fp8_stored, log, max_err, to_dev, to_np)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -48,14 +48,14 @@ def _oracle_check(kv, H, d, n, layer, t, W, R, o, lse, what):
     history, chunk t as the query chunk. On an 8-bit cache against what the
     cache holds, at the kernel's bar, and against the unquantised inputs within
     the quantisation's own error plus that bar."""
-    fp8 = kv in ("fp8", "fp8_block")
+    fp8 = kv in ("fp8", "fp8_block", "int8k_block")
 
     def stored(k, v):
         if kv == "fp8":
             s = [8.0 / 448.0] * H
             return fp8_stored(k, s), fp8_stored(v, s)
-        if kv == "fp8_block":
-            return fp8_stored(k, oracle.block_scales(k)), fp8_stored(v, oracle.block_scales(v))
+        if kv in ("fp8_block", "int8k_block"):
+            return block_stored(kv, k, v)
         return k.astype(np.float64), v.astype(np.float64)
 
     hist, hraw = {}, {}
@@ -90,13 +90,14 @@ CASES = [
     ("bf16", 2, 3, 64, 64, 3, True, 2),
     ("fp8", 2, 2, 128, 96, 2, True, 0),
     ("fp8_block", 2, 2, 128, 96, 2, True, 0),
+    ("int8k_block", 2, 2, 128, 96, 2, True, 0),
 ]
 
 
 @pytest.mark.parametrize("kv,L,H,d,n,S,R,G", CASES)
 def test_replayed_chunk_step_equals_eager(kv, L, H, d, n, S, R, G):
     import attention_bca_attend_amd as bca
-    fp8 = kv in ("fp8", "fp8_block")
+    fp8 = kv in ("fp8", "fp8_block", "int8k_block")
     log(f"graph replay {kv} L {L} H {H} d {d} n {n} S {S} R {R} G {G}")
     A = bca.Cache(L, H, d, n, S, has_ref=R, kv_dtype=kv)
     B = bca.Cache(L, H, d, n, S, has_ref=R, kv_dtype=kv)

@@ -58,7 +58,7 @@ def test_fp32_full_ring():
         assert_close(o, lse, eo, el, TOL["fp32"], f"fp32 62-slot ring, window 40, G={G}")
 
 
-@pytest.mark.parametrize("dtype", ["fp8", "fp8_block"])
+@pytest.mark.parametrize("dtype", ["fp8", "fp8_block", "int8k_block"])
 def test_fp8_with_64_heads(dtype):
     H, d, n, S, W = 64, 128, 40, 2, 2
     cache = new_cache(1, H, d, n, S, dtype=dtype)
