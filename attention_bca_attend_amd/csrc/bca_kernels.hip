@@ -1600,55 +1600,76 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(const AttnArgs a) {
 // Log-sum-exp merge of the segments of every split unit:
 //   M = max_g LSE_g, w_g = exp(LSE_g - M) (0 for LSE_g = -inf),
 //   O = sum_g w_g O_g / sum_g w_g, LSE = M + ln sum_g w_g.
-// One work group covers 256 / (D/4) rows of one unit; each thread four dims.
+// One work group covers 256 / (D/8) rows of one unit; each thread eight dims
+// (one 16-byte load per bf16 piece). The unit's first piece and piece count
+// come from the range arithmetic once per work group (thread 0, through LDS).
 // Pieces whose loads the merge issues all at once.
 constexpr int kMergeBatch = 4;
 
-// Four partial-output values: fp32 (fp32 path, e4m3 cache) or bf16 (bf16 path).
-__device__ __forceinline__ f32x4_t load_part4(const float* p) {
-  return *reinterpret_cast<const f32x4_t*>(p);
+// Eight partial-output values: fp32 (fp32 path, e4m3 cache) or bf16 (bf16 path).
+__device__ __forceinline__ void load_part8(const float* p, float (&x)[8]) {
+  const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
+  const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = a[i];
+    x[4 + i] = b[i];
+  }
 }
-__device__ __forceinline__ f32x4_t load_part4(const __bf16* p) {
-  return __builtin_convertvector(*reinterpret_cast<const bf16x4_t*>(p), f32x4_t);
+__device__ __forceinline__ void load_part8(const __bf16* p, float (&x)[8]) {
+  const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = (float)v[i];
 }
 
 template <int D, typename OutT, typename PartT>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
-  constexpr int TPR = D / 4, RPB = 256 / TPR;
+  constexpr int TPR = D / 8, RPB = 256 / TPR;
   const int blocks_per_unit = (a.bm + RPB - 1) / RPB;
   const int u = blockIdx.x / blocks_per_unit;
   const int rb = blockIdx.x - u * blocks_per_unit;
-  // pieces of unit u: the work groups w0 .. w0 + pieces - 1 whose ranges meet it
-  const int64_t I = (int64_t)a.units * a.T;
-  const int64_t w0 = first_wg_of((int64_t)u * a.T, I, a.P);
-  const int pieces = (int)(first_wg_of((int64_t)(u + 1) * a.T - 1, I, a.P) - w0 + 1);
+  // pieces of unit u: the work groups w0 .. w0 + pieces - 1 whose ranges meet
+  // it; piece j >= 1 has the slot of its own (its range starts inside unit u),
+  // piece 0 part_slot's choice
+  __shared__ int64_t s_w0, s_slot0;
+  __shared__ int s_pieces;
+  if (threadIdx.x == 0) {
+    const int64_t I = (int64_t)a.units * a.T;
+    const int64_t w0 = first_wg_of((int64_t)u * a.T, I, a.P);
+    s_w0 = w0;
+    s_pieces = (int)(first_wg_of((int64_t)(u + 1) * a.T - 1, I, a.P) - w0 + 1);
+    s_slot0 = part_slot(w0, u, I, a.T, a.P, a.spw);
+  }
+  __syncthreads();
+  const int pieces = s_pieces;
   if (pieces <= 1) return;  // written whole by the attention kernel
   const int rloc = rb * RPB + threadIdx.x / TPR;
-  const int c4 = (threadIdx.x % TPR) * 4;
+  const int c8 = (threadIdx.x % TPR) * 8;
   if (rloc >= a.bm) return;
   const int ci = u / a.upc, ul = u - ci * a.upc;  // chunk of a batched launch
   const int h = ul / a.QT, qt = ul - h * a.QT;
   const int row = qt * a.bm + rloc;
   if (row >= a.n) return;
-  // piece j is work group w0 + j's part: a slot of its own for j >= 1 (that
-  // range starts inside unit u), part_slot's choice for j = 0
-  const int64_t prow0 = part_slot(w0, u, I, a.T, a.P, a.spw) * a.bm + rloc;
+  const int64_t w0 = s_w0;
+  const int64_t prow0 = s_slot0 * a.bm + rloc;
   auto prow_of = [&](int j) -> int64_t {
     return j == 0 ? prow0 : ((w0 + j) * a.spw) * a.bm + rloc;
   };
-  float M = -INFINITY;
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  float wsum = 0.f;
+  const PartT* part = reinterpret_cast<const PartT*>(a.part_o);
+  float M = -INFINITY, wsum = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   if (pieces <= kMergeBatch) {
     // every load of the row first, then the combination (one memory latency)
     float lj[kMergeBatch];
-    f32x4_t oj[kMergeBatch];
+    float oj[kMergeBatch][8];
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
       if (j < pieces) {
         const int64_t prow = prow_of(j);
         lj[j] = a.part_lse[prow];
-        oj[j] = load_part4(reinterpret_cast<const PartT*>(a.part_o) + prow * D + c4);
+        load_part8(part + prow * D + c8, oj[j]);
       }
     }
 #pragma unroll
@@ -1660,7 +1681,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
         if (j < pieces) {
           const float wj = (lj[j] == -INFINITY) ? 0.f : expf(lj[j] - M);
           wsum += wj;
-          acc += wj * oj[j];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] += wj * oj[j][i];
         }
       }
     }
@@ -1672,20 +1694,27 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
         const float lj = a.part_lse[prow];
         const float wj = (lj == -INFINITY) ? 0.f : expf(lj - M);
         wsum += wj;
-        const f32x4_t oj = load_part4(reinterpret_cast<const PartT*>(a.part_o) + prow * D + c4);
-        acc += wj * oj;
+        float oj[8];
+        load_part8(part + prow * D + c8, oj);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += wj * oj[i];
       }
     }
   }
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-  acc *= inv;
-  OutT* op = static_cast<OutT*>(a.o) + ci * a.chunk_elems + ((int64_t)row * a.H + h) * D + c4;
+  OutT* op = static_cast<OutT*>(a.o) + ci * a.chunk_elems + ((int64_t)row * a.H + h) * D + c8;
   if constexpr (sizeof(OutT) == 2) {
-    *reinterpret_cast<bf16x4_t*>(op) = __builtin_convertvector(acc, bf16x4_t);
+    bf16x8_t v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (__bf16)(acc[i] * inv);
+    *reinterpret_cast<bf16x8_t*>(op) = v;
   } else {
-    *reinterpret_cast<f32x4_t*>(op) = acc;
+    f32x4_t v0 = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    f32x4_t v1 = {acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+    *reinterpret_cast<f32x4_t*>(op) = v0;
+    *reinterpret_cast<f32x4_t*>(op + 4) = v1;
   }
-  if (c4 == 0 && a.lse)
+  if (c8 == 0 && a.lse)
     a.lse[ci * a.chunk_lse + (int64_t)h * a.n + row] = (M == -INFINITY) ? M : M + logf(wsum);
 }
 
@@ -2078,7 +2107,7 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
     m.upc = a.upc;
     m.chunk_elems = a.chunk_elems;
     m.chunk_lse = a.chunk_lse;
-    constexpr int RPB = 256 / (D / 4);
+    constexpr int RPB = 256 / (D / 8);
     const int blocks = a.units * ((p.bm + RPB - 1) / RPB);
     if (p.kern == Kern::F32)
       hipLaunchKernelGGL((merge_kernel<D, float, float>), dim3(blocks), dim3(256), 0, s, m);
