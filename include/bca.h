@@ -119,7 +119,11 @@ typedef struct {
 } bca_window_spec;
 
 /* Bytes of device memory a cache with this descriptor needs (K/V blocks of all
- * layers). Returns 0 for an invalid descriptor, including one whose blocks of
+ * layers): per layer S ring slots plus the pinned reference block, the
+ * fixed-size rolling cache of the Matrix-Game 4.0 summary (prerequisite
+ * "causal autoregression and KV cache": a ring buffer of the recent window
+ * and a reference frame) and of the WanToFight review (rolling KV cache of
+ * the previous chunks). Returns 0 for an invalid descriptor, including one whose blocks of
  * one head ((S+R)*n*d elements) or whose chunk rows (n*H*d elements of q, k,
  * v or o) would reach 2 GiB: the kernels address those with 32-bit byte
  * offsets. */
@@ -127,12 +131,14 @@ size_t bca_cache_bytes(const bca_cache_desc* desc);
 
 /* Creates the host handle over caller memory dev_mem (at least
  * bca_cache_bytes(desc) bytes, 256-byte aligned). All slots start empty
- * (chunk id -1) and no reference chunk is present. Device memory is not
- * touched. *out receives the handle. */
+ * (chunk id -1) and no reference chunk is present, as at the start of a
+ * rollout before the first chunk is committed (same passages as
+ * bca_cache_bytes). Device memory is not touched. *out receives the handle. */
 bca_status bca_cache_create(const bca_cache_desc* desc, void* dev_mem, size_t bytes,
                             bca_cache** out);
 
-/* Frees the host handle only; the device memory stays the caller's. NULL is a no-op. */
+/* Frees the host handle only; the device memory stays the caller's. NULL is a
+ * no-op. (Library housekeeping; the pages describe no counterpart.) */
 bca_status bca_cache_destroy(bca_cache* cache);
 
 /* FP8_E4M3 caches only. Sets the per-head dequantisation scales of one layer:
@@ -162,8 +168,12 @@ bca_status bca_cache_set_kv_scales(bca_cache* cache, int32_t layer, const float*
 bca_status bca_append_chunk(bca_cache* cache, int32_t layer, int64_t chunk_id, int32_t is_ref,
                             const void* k, const void* v, int32_t in_dtype, bca_stream_t stream);
 
-/* Workspace bytes bca_attend needs for this spec (0 when it needs none). The
- * figure covers any ring occupancy, so one buffer sized once serves every call
+/* Workspace bytes bca_attend needs for this spec (0 when it needs none): the
+ * partial outputs of the window's segments before their log-sum-exp merge
+ * (Matrix-Game 4.0 summary, technical novelty: the window is cut into
+ * intervals computed in parallel and merged by log-sum-exp), and on 8-bit
+ * caches the quantised copy of the current chunk. The figure covers any ring
+ * occupancy, so one buffer sized once serves every call
  * with the same spec fields. Returns 0 as well for an invalid spec; check
  * bca_attend's status. */
 size_t bca_attend_workspace_bytes(const bca_cache* cache, const bca_window_spec* spec);
@@ -375,7 +385,9 @@ bca_status bca_attend_dev(const bca_cache* cache, int32_t layer, const bca_windo
 
 /* Host-side slot table query: chunk id held by ring slot `slot` (0 <= slot < S)
  * of `layer`, -1 if empty. slot == S (with has_ref) reports the reference block
- * (its recorded id, or -1). */
+ * (its recorded id, or -1). The table is the ring's bookkeeping of which
+ * chunk overwrote which slot (Matrix-Game 4.0 summary, prerequisite "causal
+ * autoregression and KV cache": the oldest slot is overwritten in place). */
 bca_status bca_cache_slot_chunk(const bca_cache* cache, int32_t layer, int32_t slot,
                                 int64_t* chunk_id);
 
@@ -408,7 +420,8 @@ typedef struct {
 bca_status bca_attend_plan(const bca_cache* cache, int32_t layer, const bca_window_spec* spec,
                            bca_plan_info* out);
 
-/* Static text for a status code. */
+/* Static text for a status code. (Library housekeeping; the pages describe no
+ * counterpart.) */
 const char* bca_status_string(bca_status status);
 
 /* Text of the last error on the calling thread ("" if none). */
