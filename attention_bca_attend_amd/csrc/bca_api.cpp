@@ -89,8 +89,8 @@ bool desc_ok(const bca_cache_desc* d, std::string* why) {
   if (d->has_ref != 0 && d->has_ref != 1) return bad("has_ref must be 0 or 1");
   if (elem_size(d->kv_dtype) == 0) return bad("kv_dtype is not a bca_dtype");
   if (is_fp8(d->kv_dtype)) {
-    if (d->num_heads > kMaxHeadsFp8) return bad("FP8_E4M3 caches support at most 64 heads");
-    if (d->head_dim != 128) return bad("FP8_E4M3 caches need head_dim 128");
+    if (d->num_heads > kMaxHeadsFp8) return bad("8-bit caches support at most 64 heads");
+    if (d->head_dim != 128) return bad("8-bit caches need head_dim 128");
   }
   // keys per head (all blocks plus the current chunk) must fit int32 with room
   const int64_t blocks = (int64_t)d->ring_slots + d->has_ref + 1;
