@@ -173,6 +173,45 @@ def test_deterministic():
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+def test_split_merge_ignores_workspace_contents():
+    """Whatever the workspace holds before a call (zeros, all ones, random
+    bytes, or a previous call's partial outputs) the output and LSE of a
+    split window are the same, bit for bit, and match the oracle; so do
+    repeated calls on one workspace."""
+    H, d, n, S, W = 12, 128, 300, 2, 2
+    cache = new_cache(1, H, d, n, S)
+    seq = Sequence(cache, H, d, n, "bf16", seed_layer=6)
+    for t in range(2):
+        _, k, v = seq.chunk(t)
+        seq.append(0, t, k, v)
+    q, k, v = seq.chunk(2)
+    eo, el = seq.expected(2, q, k, v, W)
+    qd, kd, vd = (to_dev(x, "bf16") for x in (q, k, v))
+    for G in (3, 0):
+        spec = cache.spec(2, W, num_segments=G)
+        plan = cache.plan(0, spec)
+        assert plan["merge"] == 1, plan
+        ws = torch.empty(plan["workspace_bytes"], dtype=torch.uint8, device="cuda")
+        g = torch.Generator(device="cuda").manual_seed(7)
+        ref = None
+        for fill in ("zero", "ones", "random", "reuse", "reuse"):
+            if fill == "zero":
+                ws.zero_()
+            elif fill == "ones":
+                ws.fill_(255)
+            elif fill == "random":
+                ws.copy_(torch.randint(0, 256, ws.shape, generator=g, device="cuda",
+                                       dtype=torch.int32).to(torch.uint8))
+            o, lse = cache.attend(0, qd, kd, vd, spec, workspace=ws)
+            torch.cuda.synchronize()
+            got = (to_np(o), to_np(lse))
+            if ref is None:
+                ref = got
+                assert_close(got[0], got[1], eo, el, TOL["bf16"], f"split G={G}, fresh workspace")
+            assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]), (G, fill)
+        log(f"split G={G}: same result over zeroed, 0xff, random and reused workspaces")
+
+
 def test_stream_k_ranges_cross_units():
     """More units than work groups: ranges of tile iterations cross unit
     boundaries, so one work group finishes the end of one unit and starts the
