@@ -616,10 +616,13 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
 
     // Q^T fragments (B operand): lane holds query q0+l32, dims 16kk+8hi .. +7;
     // rows past the chunk read as zeros (out-of-range buffer offsets).
+    // Each wave group loads its Q in its own branch below (group 1 needs it a
+    // phase later and waits for it then), so that the compiler, which sees
+    // only these loads, places its one wait for them at a point of the
+    // group's own code where no tile request it cannot see is in flight.
     const __bf16* qc = static_cast<const __bf16*>(a.q) + cel;
     const HeadSrc qsrc = head_src(qc, qc, a, h, D, 2, 2);
-    bf16x8_t qf[D / 16];
-    {
+    auto load_q = [&](bf16x8_t (&qf)[D / 16]) {
       const int row = q0 + l32;
       const int qoff = row < a.n ? (row * a.H * D + 8 * hi) * 2 : kOob;
 #pragma unroll
@@ -627,12 +630,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
         const uint4 x = buf16(qsrc.cur, qsrc.cur_bytes, qoff + (row < a.n ? 32 * kk : 0));
         qf[kk] = __builtin_bit_cast(bf16x8_t, x);
       }
-    }
-    // Wait for everything in flight (the first tiles and Q) with a wait the
-    // compiler sees: it then knows the Q registers are loaded and inserts no
-    // vector-memory waits in the loop, where the only loads in flight are the
-    // tile requests this kernel waits for itself.
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    };
 
     PPState<D> st;
 #pragma unroll
@@ -664,9 +662,15 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
     };
     auto stage = [&](int r) -> const unsigned char* { return smem + (r & 3) * C::STAGE; };
 
-    wg_barrier();
-
     if (grp == 0) {
+      // Q and this wave's shares of the first two tiles, with a wait the
+      // compiler sees: it then knows Q is loaded and inserts no vector-memory
+      // waits in the loop, where the only loads in flight are the tile
+      // requests this kernel waits for itself.
+      bf16x8_t qf[D / 16];
+      load_q(qf);
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      wg_barrier();
       // k = 2r: PV(r-1) + QK(r); k = 2r+1: softmax(r)
       begin_phase(0);
       if (wave_rows) {
@@ -700,6 +704,16 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
       begin_phase(2 * nt + 1);
       end_phase(2 * nt + 1);
     } else {
+      // Q after this wave's tile requests: the tiles' shares are waited for
+      // before the first barrier (everything but the D/16 Q loads, which
+      // complete in order after them), Q itself during phase 0, where this
+      // group has nothing to compute, with a wait the compiler sees, before
+      // the tile-2 requests are issued.
+      bf16x8_t qf[D / 16];
+      load_q(qf);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(D / 16) : "memory");
+      wg_barrier();
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
       // one phase later: k = 2r+1: PV(r-1) + QK(r); k = 2r+2: softmax(r)
       begin_phase(0);
       end_phase(0);
