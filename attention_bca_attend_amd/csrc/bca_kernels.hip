@@ -173,6 +173,17 @@ __device__ __forceinline__ float xhalf_max(float x) {
                                                   false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// The softmax's maxima propagate NaN (IEEE maximum, v_maximum3_f32): unlike
+// fmaxf they need no quieting of the MFMA results first, and a NaN score makes
+// its row NaN either way.
+__device__ __forceinline__ float max3n(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+__device__ __forceinline__ float xhalf_maxn(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 __device__ __forceinline__ float xhalf_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
@@ -516,13 +527,13 @@ __device__ __forceinline__ void pp_softmax(PPState<D>& st, int lim, int hi, floa
   const f32x16_t v0 = st.s[0], v1 = st.s[1];
   float m[11];
 #pragma unroll
-  for (int e = 0; e < 5; ++e) m[e] = fmaxf(fmaxf(v0[3 * e], v0[3 * e + 1]), v0[3 * e + 2]);
+  for (int e = 0; e < 5; ++e) m[e] = max3n(v0[3 * e], v0[3 * e + 1], v0[3 * e + 2]);
 #pragma unroll
-  for (int e = 0; e < 5; ++e) m[5 + e] = fmaxf(fmaxf(v1[3 * e], v1[3 * e + 1]), v1[3 * e + 2]);
-  m[10] = fmaxf(v0[15], v1[15]);
-  const float n0 = fmaxf(fmaxf(m[0], m[1]), m[2]), n1 = fmaxf(fmaxf(m[3], m[4]), m[5]);
-  const float n2 = fmaxf(fmaxf(m[6], m[7]), m[8]), n3 = fmaxf(m[9], m[10]);
-  const float mx = xhalf_max(fmaxf(fmaxf(n0, n1), fmaxf(n2, n3)));
+  for (int e = 0; e < 5; ++e) m[5 + e] = max3n(v1[3 * e], v1[3 * e + 1], v1[3 * e + 2]);
+  m[10] = __builtin_elementwise_maximum(v0[15], v1[15]);
+  const float n0 = max3n(m[0], m[1], m[2]), n1 = max3n(m[3], m[4], m[5]);
+  const float n2 = max3n(m[6], m[7], m[8]), n3 = __builtin_elementwise_maximum(m[9], m[10]);
+  const float mx = xhalf_maxn(max3n(n0, n1, __builtin_elementwise_maximum(n2, n3)));
   const float mxs = mx * c;
   const bool need = !(mxs <= st.m_run + 8.0f);
   if (__any(need)) {
@@ -1122,14 +1133,14 @@ __device__ __forceinline__ void f8_softmax(F8State<D>& st, int lim, int hi, floa
   const f32x16_t v0 = st.s[0], v1 = st.s[1];
   float m[11];
 #pragma unroll
-  for (int e = 0; e < 5; ++e) m[e] = fmaxf(fmaxf(v0[3 * e], v0[3 * e + 1]), v0[3 * e + 2]);
+  for (int e = 0; e < 5; ++e) m[e] = max3n(v0[3 * e], v0[3 * e + 1], v0[3 * e + 2]);
 #pragma unroll
-  for (int e = 0; e < 5; ++e) m[5 + e] = fmaxf(fmaxf(v1[3 * e], v1[3 * e + 1]), v1[3 * e + 2]);
-  m[10] = fmaxf(v0[15], v1[15]);
-  const float n0 = fmaxf(fmaxf(m[0], m[1]), m[2]), n1 = fmaxf(fmaxf(m[3], m[4]), m[5]);
-  const float n2 = fmaxf(fmaxf(m[6], m[7]), m[8]), n3 = fmaxf(m[9], m[10]);
+  for (int e = 0; e < 5; ++e) m[5 + e] = max3n(v1[3 * e], v1[3 * e + 1], v1[3 * e + 2]);
+  m[10] = __builtin_elementwise_maximum(v0[15], v1[15]);
+  const float n0 = max3n(m[0], m[1], m[2]), n1 = max3n(m[3], m[4], m[5]);
+  const float n2 = max3n(m[6], m[7], m[8]), n3 = __builtin_elementwise_maximum(m[9], m[10]);
   // c > 0, so the maximum of the scaled scores is c times the maximum score
-  const float mxs = xhalf_max(fmaxf(fmaxf(n0, n1), fmaxf(n2, n3)) * c);
+  const float mxs = xhalf_maxn(max3n(n0, n1, __builtin_elementwise_maximum(n2, n3)) * c);
   if (__any(!(mxs <= st.m_run + 4.0f))) {
     const float m_new = fmaxf(st.m_run, mxs);
     const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
