@@ -541,6 +541,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only the copy of known size that calibrates the traffic counters")
+    ap.add_argument("--segments", type=int, default=None,
+                    help="override the workload's segment count (0: the planner's own split)")
     ap.add_argument("--layers", type=int, default=None,
                     help="profiling runs only: fewer layers (each layer's launches are alike; "
                          "counter collection serialises every dispatch)")
@@ -560,6 +562,8 @@ def main():
     cfg = dict(CONFIGS[args.config])
     if args.layers:
         cfg["L"] = args.layers
+    if args.segments is not None:
+        cfg["G"] = args.segments
     if cfg.get("sequence"):
         main_sequence(args, cfg)
         return
