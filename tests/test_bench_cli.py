@@ -23,5 +23,5 @@ def test_more_than_one_gpu_is_refused_with_a_message():
 def test_help_lists_the_workloads():
     r = run_bench("--help")
     assert r.returncode == 0
-    for flag in ("--gpus", "--steps", "--warmup", "--config"):
+    for flag in ("--gpus", "--steps", "--warmup", "--config", "--segments"):
         assert flag in r.stdout
