@@ -1625,11 +1625,12 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(const AttnArgs a) {
 // Log-sum-exp merge of the segments of every split unit:
 //   M = max_g LSE_g, w_g = exp(LSE_g - M) (0 for LSE_g = -inf),
 //   O = sum_g w_g O_g / sum_g w_g, LSE = M + ln sum_g w_g.
-// One work group covers 256 / (D/8) rows of one unit; each thread eight dims
-// (one 16-byte load per bf16 piece). The unit's first piece and piece count
+// One work group covers 256 / (D/16) rows of one unit; each thread sixteen
+// dims (two 16-byte loads per bf16 piece). The unit's first piece and piece count
 // come from the range arithmetic once per work group (thread 0, through LDS).
 // Pieces whose loads the merge issues all at once.
 constexpr int kMergeBatch = 4;
+constexpr int kMergeEpt = 16;  // dims per thread
 
 // Eight partial-output values: fp32 (fp32 path, e4m3 cache) or bf16 (bf16 path).
 __device__ __forceinline__ void load_part8(const float* p, float (&x)[8]) {
@@ -1649,7 +1650,7 @@ __device__ __forceinline__ void load_part8(const __bf16* p, float (&x)[8]) {
 
 template <int D, typename OutT, typename PartT>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
-  constexpr int TPR = D / 8, RPB = 256 / TPR;
+  constexpr int NG = kMergeEpt / 8, TPR = D / kMergeEpt, RPB = 256 / TPR;
   const int blocks_per_unit = (a.bm + RPB - 1) / RPB;
   const int u = blockIdx.x / blocks_per_unit;
   const int rb = blockIdx.x - u * blocks_per_unit;
@@ -1669,7 +1670,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   const int pieces = s_pieces;
   if (pieces <= 1) return;  // written whole by the attention kernel
   const int rloc = rb * RPB + threadIdx.x / TPR;
-  const int c8 = (threadIdx.x % TPR) * 8;
+  const int c8 = (threadIdx.x % TPR) * kMergeEpt;
   if (rloc >= a.bm) return;
   const int ci = u / a.upc, ul = u - ci * a.upc;  // chunk of a batched launch
   const int h = ul / a.QT, qt = ul - h * a.QT;
@@ -1682,19 +1683,21 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   };
   const PartT* part = reinterpret_cast<const PartT*>(a.part_o);
   float M = -INFINITY, wsum = 0.f;
-  float acc[8];
+  float acc[8 * NG];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int i = 0; i < 8 * NG; ++i) acc[i] = 0.f;
   if (pieces <= kMergeBatch) {
     // every load of the row first, then the combination (one memory latency)
     float lj[kMergeBatch];
-    float oj[kMergeBatch][8];
+    float oj[kMergeBatch][8 * NG];
 #pragma unroll
     for (int j = 0; j < kMergeBatch; ++j) {
       if (j < pieces) {
         const int64_t prow = prow_of(j);
         lj[j] = a.part_lse[prow];
-        load_part8(part + prow * D + c8, oj[j]);
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+          load_part8(part + prow * D + c8 + 8 * g, *reinterpret_cast<float(*)[8]>(&oj[j][8 * g]));
       }
     }
 #pragma unroll
@@ -1707,7 +1710,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
           const float wj = (lj[j] == -INFINITY) ? 0.f : expf(lj[j] - M);
           wsum += wj;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[i] += wj * oj[j][i];
+          for (int i = 0; i < 8 * NG; ++i) acc[i] += wj * oj[j][i];
         }
       }
     }
@@ -1719,25 +1722,32 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
         const float lj = a.part_lse[prow];
         const float wj = (lj == -INFINITY) ? 0.f : expf(lj - M);
         wsum += wj;
-        float oj[8];
-        load_part8(part + prow * D + c8, oj);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += wj * oj[i];
+        for (int g = 0; g < NG; ++g) {
+          float oj[8];
+          load_part8(part + prow * D + c8 + 8 * g, oj);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[8 * g + i] += wj * oj[i];
+        }
       }
     }
   }
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
   OutT* op = static_cast<OutT*>(a.o) + ci * a.chunk_elems + ((int64_t)row * a.H + h) * D + c8;
-  if constexpr (sizeof(OutT) == 2) {
-    bf16x8_t v;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = (__bf16)(acc[i] * inv);
-    *reinterpret_cast<bf16x8_t*>(op) = v;
-  } else {
-    f32x4_t v0 = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-    f32x4_t v1 = {acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
-    *reinterpret_cast<f32x4_t*>(op) = v0;
-    *reinterpret_cast<f32x4_t*>(op + 4) = v1;
+  for (int g = 0; g < NG; ++g) {
+    const float* ag = acc + 8 * g;
+    if constexpr (sizeof(OutT) == 2) {
+      bf16x8_t v;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (__bf16)(ag[i] * inv);
+      *reinterpret_cast<bf16x8_t*>(op + 8 * g) = v;
+    } else {
+      f32x4_t v0 = {ag[0] * inv, ag[1] * inv, ag[2] * inv, ag[3] * inv};
+      f32x4_t v1 = {ag[4] * inv, ag[5] * inv, ag[6] * inv, ag[7] * inv};
+      *reinterpret_cast<f32x4_t*>(op + 8 * g) = v0;
+      *reinterpret_cast<f32x4_t*>(op + 8 * g + 4) = v1;
+    }
   }
   if (c8 == 0 && a.lse)
     a.lse[ci * a.chunk_lse + (int64_t)h * a.n + row] = (M == -INFINITY) ? M : M + logf(wsum);
@@ -2132,7 +2142,7 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
     m.upc = a.upc;
     m.chunk_elems = a.chunk_elems;
     m.chunk_lse = a.chunk_lse;
-    constexpr int RPB = 256 / (D / 8);
+    constexpr int RPB = 256 / (D / kMergeEpt);
     const int blocks = a.units * ((p.bm + RPB - 1) / RPB);
     if (p.kern == Kern::F32)
       hipLaunchKernelGGL((merge_kernel<D, float, float>), dim3(blocks), dim3(256), 0, s, m);
