@@ -165,7 +165,7 @@ def assert_fp8(seq, o, lse, t, q, k, v, W, use_ref=False, raw_tol=None, what="",
     """An 8-bit cache result against the oracle twice: on what the cache holds
     (the kernel's own error, FP8_CACHE_ABS + FP8_CACHE_REL |O|, LSE 1e-2), and
     on the unquantised seeded inputs. The second bar is raw_tol when given
-    (the benchmark spec's 5e-2); otherwise it is the quantisation's own error (the
+    (5e-2, the bar for 8-bit K/V); otherwise it is the quantisation's own error (the
     oracle on the cache contents against the oracle on the raw inputs) plus the
     kernel's bar, i.e. what the first check already implies: e4m3 keeps 3
     mantissa bits, and on a few hundred keys a row dominated by one key

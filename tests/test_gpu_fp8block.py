@@ -6,7 +6,7 @@ the oracle's rule (oracle.block_scales: fp32 max |x| / 448) and e4m3
 quantiser; attention is held to the oracle run on exactly what the cache
 holds (the current chunk quantised by the same rule with its own scales),
 and to the oracle on the unquantised seeded inputs: at the Matrix-Game size
-at the benchmark spec's 5e-2, on small shapes at the quantisation's own error
+at 5e-2 (the bar for 8-bit K/V), on small shapes at the quantisation's own error
 plus the kernel's bar (bca_harness.assert_fp8).
 """
 import math

@@ -8,7 +8,7 @@ the oracle's rule (oracle.block_scales: fp32 max |x| / 127 for K, / 448 for
 V) and its int8 and e4m3 quantisers; attention is held to the oracle run on
 exactly what the cache holds (the current chunk quantised by the same rule
 with its own scales), and to the oracle on the unquantised seeded inputs: at
-the Matrix-Game size at the benchmark spec's 5e-2, on small shapes at the
+the Matrix-Game size at 5e-2 (the bar for 8-bit K/V), on small shapes at the
 quantisation's own error plus the kernel's bar (bca_harness.assert_fp8).
 """
 import math
@@ -109,7 +109,7 @@ def test_int8k_full_size_matrix_game_shape(seed):
     """24 heads x 405 tokens, reference + 20 ring chunks + current, 4 segments
     and the automatic split, 1% outliers of 8 sigma: the seeded inputs of the
     e4m3 workload (seed 4) and of the block-scaled e4m3 test (seed 44), held
-    to the benchmark spec's 5e-2 against the unquantised inputs."""
+    to 5e-2 (the bar for 8-bit K/V) against the unquantised inputs."""
     H, d, n, S, W = 24, 128, 405, 20, 20
     cache = new_cache(1, H, d, n, S, R=True)
     seq = Sequence(cache, H, d, n, KIND, seed_layer=seed, outlier_frac=0.01)
