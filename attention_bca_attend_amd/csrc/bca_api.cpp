@@ -644,12 +644,11 @@ bca_status attend_impl(const bca_cache* c, int32_t layer, const bca_window_spec*
   bca_status st = make_plan(c, layer, s, qkv_dtype, p);
   if (st != BCA_OK) return st;
   if (dev_t) {
-    // the chunk id comes from the device: only the bf16 ring path, with a ring
-    // that holds the S chunks before spec->q_chunk_id (then every later chunk
-    // of a consecutive stream sees W blocks, in slots the kernel derives)
-    if (c->d.kv_dtype != BCA_BF16 && c->d.kv_dtype != BCA_FP8_E4M3)
-      return fail(BCA_ERR_UNSUPPORTED,
-                  "device-side chunk ids need a BF16 or FP8_E4M3 (per-head scales) cache");
+    // the chunk id comes from the device: the bf16 and 8-bit ring paths, with
+    // a ring that holds the S chunks before spec->q_chunk_id (then every later
+    // chunk of a consecutive stream sees W blocks, in slots the kernel derives)
+    if (c->d.kv_dtype == BCA_F32)
+      return fail(BCA_ERR_UNSUPPORTED, "device-side chunk ids need a 16- or 8-bit cache");
     if (!aligned(dev_t, 8))
       return fail(BCA_ERR_INVALID_ARG, "d_q_chunk_id must be 8-byte aligned");
     const int S = c->d.ring_slots;

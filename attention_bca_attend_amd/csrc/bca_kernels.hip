@@ -292,8 +292,11 @@ struct FetchRun {
 };
 
 // Runs of a launch whose visible slots the kernel derives itself
-// (bca_attend_dev): built once per work group in LDS.
-__shared__ Run dev_runs[4];
+// (bca_attend_dev): built once per work group in LDS. A per-block cache has
+// one run per visible block; dev_vis keeps that block's index (ring slot, or
+// S for the reference) for its scales.
+__shared__ Run dev_runs[kMaxBlocks];
+__shared__ int dev_vis[kMaxBlocks];
 __shared__ int dev_nruns;
 
 template <bool DEVT>
@@ -309,16 +312,22 @@ __device__ __forceinline__ int nruns_of(const AttnArgs& a) {
 
 // The visible ring slots of query chunk t = *a.dev_t when the ring holds
 // consecutive ids: chunks t-W .. t-1 sit in slots (t-W) mod S .. (t-1) mod S.
-// The runs are built as the host builds them (ascending physical blocks,
-// adjacent blocks merged, the reference block S last), so the launch
-// computes exactly what a host-planned call for the same chunk computes.
+// The runs are built as the host builds them (ascending physical blocks, the
+// reference block S last; adjacent blocks merged, or with BLK one run per
+// block, each padded to a.tpb whole key tiles), so the launch computes
+// exactly what a host-planned call for the same chunk computes.
+template <bool BLK>
 __device__ __forceinline__ void build_dev_runs(const AttnArgs& a) {
   const int64_t t = *a.dev_t;
   const int S = a.dev_S, W = a.dev_W, n = a.n;
   const int s0 = (int)((((t - W) % S) + S) % S);
   int nr = 0, nb = 0;
   auto add = [&](int b) {
-    if (nr > 0 && dev_runs[nr - 1].phys + dev_runs[nr - 1].len == b * n) {
+    if (BLK) {
+      dev_runs[nr] = Run{nb * a.tpb * 64, n, b * n, 0};
+      dev_vis[nr] = b;
+      ++nr;
+    } else if (nr > 0 && dev_runs[nr - 1].phys + dev_runs[nr - 1].len == b * n) {
       dev_runs[nr - 1].len += n;
     } else {
       dev_runs[nr] = Run{nb * n, n, b * n, 0};
@@ -601,7 +610,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
   }
   const FetchLane<D> fl = fetch_lane<D>(wave, lane, SEQ ? a.cache_row_elems * 2 : C::ROWB);
   if constexpr (DEVT) {
-    if (tid == 0) build_dev_runs(a);
+    if (tid == 0) build_dev_runs<false>(a);
     __syncthreads();
   }
 
@@ -1181,7 +1190,7 @@ __device__ __forceinline__ void f8_softmax(F8State<D>& st, int lim, int hi, floa
 // corrected per tile and s_ref applied at normalisation.
 template <int D, bool BLK, bool DEVT, bool I8K = false>
 __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
-  static_assert(!I8K || (BLK && !DEVT), "int8 K comes with per-block scales");
+  static_assert(!I8K || BLK, "int8 K comes with per-block scales");
   using C = F8Cfg<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::NSTAGE * C::STAGE];
   // BLK: the unit's K scale per block, and per block the exponent offset
@@ -1217,7 +1226,7 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
   }
 
   if constexpr (DEVT) {
-    if (tid == 0) build_dev_runs(a);
+    if (tid == 0) build_dev_runs<BLK>(a);
     __syncthreads();
   }
   while (it < it_end) {
@@ -1316,7 +1325,7 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
       float svj = 0.f;
       if (tid <= a.nvis_cache) {
         const bool cur = tid == a.nvis_cache;
-        const int64_t e = cur ? h : (int64_t)a.vis_blk[tid] * a.H + h;
+        const int64_t e = cur ? h : (int64_t)(DEVT ? dev_vis[tid] : a.vis_blk[tid]) * a.H + h;
         sc_k[tid] = cur ? a.cur_sc[e] : a.ksc[e];
         svj = cur ? a.cur_sc[a.H + e] : a.vsc[e];
         sc_fac[tid] = svj;
@@ -2104,9 +2113,14 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
         const int64_t total = (int64_t)a.n * a.H * (D / 8);
         hipLaunchKernelGGL(append_fp8_kernel<D>, dim3((unsigned)((total + 255) / 256), 2),
                            dim3(256), 0, s, q, 0);
-        if (a.blk && a.i8k)
+        if (a.blk && a.i8k && p.devt)
+          hipLaunchKernelGGL((attn_fp8_kernel<D, true, true, true>), dim3(p.wgs), dim3(512), 0,
+                             s, a);
+        else if (a.blk && a.i8k)
           hipLaunchKernelGGL((attn_fp8_kernel<D, true, false, true>), dim3(p.wgs), dim3(512), 0,
                              s, a);
+        else if (a.blk && p.devt)
+          hipLaunchKernelGGL((attn_fp8_kernel<D, true, true>), dim3(p.wgs), dim3(512), 0, s, a);
         else if (a.blk)
           hipLaunchKernelGGL((attn_fp8_kernel<D, true, false>), dim3(p.wgs), dim3(512), 0, s, a);
         else if (p.devt)

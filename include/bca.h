@@ -374,8 +374,10 @@ bca_status bca_attend_replayable(const bca_cache* cache, int32_t layer,
  * in order keeps it (bca_append_chunk_dev with the same counter, advanced
  * after the appends). spec->q_chunk_id is the chunk the call is made (or
  * captured) for: the host plans with it and requires every ring slot to hold
- * one of the S chunks before it (no slot empty, hence t >= S). BF16 and FP8_E4M3 caches
- * (BCA_ERR_UNSUPPORTED for the others); other arguments and errors as for bca_attend, plus
+ * one of the S chunks before it (no slot empty, hence t >= S). BF16 and 8-bit
+ * caches, per-block scales included (each visible block's scales are looked
+ * up from the slot it derives); BCA_ERR_UNSUPPORTED for an F32 cache. Other
+ * arguments and errors as for bca_attend, plus
  * BCA_ERR_INVALID_ARG for a NULL or misaligned d_q_chunk_id or a ring that
  * does not hold the S chunks before spec->q_chunk_id. */
 bca_status bca_attend_dev(const bca_cache* cache, int32_t layer, const bca_window_spec* spec,

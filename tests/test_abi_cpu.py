@@ -585,11 +585,20 @@ def test_attend_dev_validates_before_launch():
         bca.bca_attend_dev(h, 0, spec, P, P, P, P, bca.BF16, P, 0, P + 16, ws, 0)
     assert e.value.status == -3
     bca.bca_cache_destroy(h)
-    for dt in (bca.FP8_E4M3_BLOCK, bca.INT8K_FP8V_BLOCK):
+    # an fp32 cache is refused; the 8-bit caches (per-head and per-block
+    # scales) pass the dtype check and stop at the next one (a misaligned id)
+    hf, _ = make(S=3, R=0, dt=bca.F32, d=64, H=2, n=16)
+    for sl in range(3):
+        bca.bca_cache_set_slot_chunk(hf, 0, sl, sl)
+    with pytest.raises(BcaError) as e:
+        bca.bca_attend_dev(hf, 0, spec, P, P, P, P, bca.F32, P, 0, P, 1 << 30, 0)
+    assert e.value.status == -4
+    bca.bca_cache_destroy(hf)
+    for dt in (bca.FP8_E4M3, bca.FP8_E4M3_BLOCK, bca.INT8K_FP8V_BLOCK):
         h8, _ = make(S=3, R=0, dt=dt, d=128, H=2, n=16)
         for sl in range(3):
             bca.bca_cache_set_slot_chunk(h8, 0, sl, sl)
         with pytest.raises(BcaError) as e:
-            bca.bca_attend_dev(h8, 0, spec, P, P, P, P, bca.BF16, P, 0, P, 1 << 30, 0)
-        assert e.value.status == -4
+            bca.bca_attend_dev(h8, 0, spec, P + 4, P, P, P, bca.BF16, P, 0, P, 1 << 30, 0)
+        assert e.value.status == -1, dt
         bca.bca_cache_destroy(h8)

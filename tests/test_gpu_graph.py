@@ -204,22 +204,27 @@ def test_device_chunk_id_negative_writes_nothing():
 @pytest.mark.parametrize("kv,L,H,d,n,S,W,R,G", [("bf16", 2, 2, 128, 100, 3, 2, False, 0),
                                                 ("bf16", 2, 3, 64, 64, 4, 1, True, 2),
                                                 ("bf16", 1, 2, 128, 405, 20, 19, True, 4),
-                                                ("fp8", 2, 2, 128, 96, 3, 2, True, 0)])
+                                                ("fp8", 2, 2, 128, 96, 3, 2, True, 0),
+                                                ("fp8_block", 2, 2, 128, 96, 3, 2, True, 0),
+                                                ("fp8_block", 1, 2, 128, 130, 5, 3, False, 2),
+                                                ("int8k_block", 2, 2, 128, 96, 3, 2, True, 0),
+                                                ("int8k_block", 1, 3, 128, 64, 4, 1, True, 0)])
 def test_replayed_step_with_window_smaller_than_ring(kv, L, H, d, n, S, W, R, G):
     """Windows smaller than the ring see different slots from chunk to chunk:
     the captured attends read the chunk id from the device counter and take
-    the visible slots from it (bca_attend_dev). Every replay must equal a
-    host-planned bca_attend of the same chunk on a twin cache, bit for bit."""
+    the visible slots from it (bca_attend_dev; on a block-scaled cache also
+    each visible block's scales). Every replay must equal a host-planned
+    bca_attend of the same chunk on a twin cache, bit for bit."""
     import attention_bca_attend_amd as bca
     log(f"graph replay, window {W} < ring {S}: {kv} L {L} H {H} d {d} n {n} R {R} G {G}")
-    fp8 = kv == "fp8"
+    fp8 = kv in ("fp8", "fp8_block", "int8k_block")
     A = bca.Cache(L, H, d, n, S, has_ref=R, kv_dtype=kv)
     B = bca.Cache(L, H, d, n, S, has_ref=R, kv_dtype=kv)
     A.mem.zero_()
     B.mem.zero_()
     for c in (A, B):
         for l in range(L):
-            if fp8:
+            if kv == "fp8":
                 c.set_kv_scales(l, [8.0 / 448.0] * H, [8.0 / 448.0] * H)
             if R:
                 _, k, v = _chunk(n, H, d, l, 1000, fp8)
@@ -239,7 +244,7 @@ def test_replayed_step_with_window_smaller_than_ring(kv, L, H, d, n, S, W, R, G)
     d_chunk = torch.full((1,), t0, dtype=torch.int64, device="cuda")
     # code objects load on first launch: one eager run on a scratch cache first
     scratch = bca.Cache(1, H, d, n, S, has_ref=R, kv_dtype=kv)
-    if fp8:
+    if kv == "fp8":
         scratch.set_kv_scales(0, [8.0 / 448.0] * H, [8.0 / 448.0] * H)
     for t in range(S):
         _, k, v = _chunk(n, H, d, 0, t, False)

@@ -138,14 +138,3 @@ def test_int8k_refused_calls():
     with pytest.raises(bca.BcaError) as e:
         cache.append_chunk(0, 0, to_dev(k, "bf16"), to_dev(v, "bf16"), rope=(1e4, 0))
     assert e.value.status == -4
-    cache.append_chunk(0, 0, to_dev(k, "bf16"), to_dev(v, "bf16"))
-    cache.append_chunk(0, 1, to_dev(k, "bf16"), to_dev(v, "bf16"))
-    spec = cache.spec(2, 1)
-    q = to_dev(k, "bf16")
-    o = torch.empty_like(q)
-    lse = torch.empty((2, 32), dtype=torch.float32, device="cuda")
-    ws = cache.workspace(spec)
-    d_t = torch.full((1,), 2, dtype=torch.int64, device="cuda")
-    with pytest.raises(bca.BcaError) as e:  # windows from a device-side id: not this cache
-        cache.attend_dev(0, d_t, q, q, to_dev(v, "bf16"), spec, o, lse, ws)
-    assert e.value.status == -4
