@@ -99,12 +99,13 @@ typedef struct bca_cache bca_cache; /* opaque host handle */
 
 typedef struct {
   int32_t num_layers;   /* L >= 1                                               */
-  int32_t num_heads;    /* H >= 1 (FP8_E4M3: H <= 64)                           */
+  int32_t num_heads;    /* H >= 1 (8-bit caches: H <= 64)                       */
   int32_t head_dim;     /* d in {64, 128}                                       */
   int32_t chunk_tokens; /* n >= 1: tokens per chunk (query chunk = cached chunk) */
   int32_t ring_slots;   /* S in [1, 62]                                         */
   int32_t has_ref;      /* R in {0, 1}: reserve one pinned reference block       */
-  int32_t kv_dtype;     /* bca_dtype of the cache: F32, BF16 or FP8_E4M3         */
+  int32_t kv_dtype;     /* bca_dtype of the cache: F32, BF16, FP8_E4M3,
+                           FP8_E4M3_BLOCK or INT8K_FP8V_BLOCK                     */
 } bca_cache_desc;
 
 typedef struct {
