@@ -467,8 +467,7 @@ bca_status append_impl(bca_cache* c, int32_t layer, int64_t chunk_id, int32_t is
       a.v_scale[h] = c->v_scale[(size_t)layer * d.num_heads + h];
     }
   if (is_blk(kv)) {
-    if (rope)
-      return fail(BCA_ERR_UNSUPPORTED, "no rotary append into a per-block 8-bit cache");
+    // with rotation, the block's K scale is taken over the rotated rows
     a.dev_scales = 1;
     a.k_int8 = kv == BCA_INT8K_FP8V_BLOCK ? 1 : 0;
     a.host_blk = blk;
@@ -681,8 +680,6 @@ bca_status attend_impl(const bca_cache* c, int32_t layer, const bca_window_spec*
       return fail(BCA_ERR_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes,
                   need);
   }
-  if (rope && is_blk(d.kv_dtype))
-    return fail(BCA_ERR_UNSUPPORTED, "no rotary attention over a per-block 8-bit cache");
   if (rope) {
     RopeStageArgs r;
     std::memset(&r, 0, sizeof r);

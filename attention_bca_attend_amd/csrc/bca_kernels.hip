@@ -1944,14 +1944,18 @@ __device__ __forceinline__ int append_scale_block(const AppendArgs& a) {
 // head, scale = (largest |x| of the chunk's rows of that head) / 448 (/ 127
 // for int8 K), 1 when that maximum is 0 or not finite (any NaN or infinity). One work group of 1024 threads per
 // (head, K|V), each thread with up to 8 row loads in flight; blockIdx.y
-// selects K (0) or V (1).
-template <int D>
+// selects K (0) or V (1). ROPE (a rotary append): K's maximum is taken over
+// the rotated rows, which are what the append stores.
+template <int D, bool ROPE>
 __global__ __launch_bounds__(1024) void append_amax_kernel(const AppendArgs a) {
-  constexpr int G = D / 8, NT = 1024, U = 8;
+  // fewer row loads in flight with rotation (its angles take registers)
+  constexpr int G = D / 8, NT = 1024, U = ROPE ? 2 : 8;
   const int h = blockIdx.x;
   const bool isv = blockIdx.y == 1;
   const int bi = append_scale_block(a);
   if (bi < 0) return;
+  __shared__ double inv_freq[ROPE ? D / 2 : 1];
+  if constexpr (ROPE) rope_inv_freq<D>(inv_freq, a.rope_log2_base);
   const __bf16* src = static_cast<const __bf16*>(isv ? a.v : a.k);
   const int64_t total = (int64_t)a.n * G;
   float amax = 0.f;
@@ -1965,14 +1969,21 @@ __global__ __launch_bounds__(1024) void append_amax_kernel(const AppendArgs a) {
                        : bf16x8_t{};
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < 8; ++e) x[e] = (float)v[u][e];
+      if (ROPE && !isv) {
+        const int64_t i = i0 + (int64_t)u * NT;
+        const int64_t r = i / G, g = i % G;
+        rope8<D>(x, rope_angles<D>((int)g, a.rope_pos0 + r, inv_freq));
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
         // a NaN counts as an infinite magnitude: the maximum is then not
         // finite and the scale 1, as for an infinity
-        const float x = (float)v[u][e];
-        amax = fmaxf(amax, x == x ? fabsf(x) : INFINITY);
-      }
+        amax = fmaxf(amax, x[e] == x[e] ? fabsf(x[e]) : INFINITY);
+    }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
@@ -2046,8 +2057,10 @@ __global__ __launch_bounds__(128) void rope_stage_kernel(const RopeStageArgs a, 
 
 // The rotated K of an append: like rope_stage_kernel (one thread per token,
 // 8-dim group and kRopeHeads heads), writing the block's [H][n][d] rows in the cache
-// dtype: bf16 or fp32 (es 2 or 4) when FP8 is false, e4m3 with the head's
-// scale (rotated first, in fp32, then quantised) when it is true.
+// dtype: bf16 or fp32 (es 2 or 4) when FP8 is false; when it is true, 8-bit
+// codes with the head's scale (rotated first, in fp32, then quantised): e4m3,
+// or int8 for the K of an INT8K_FP8V_BLOCK cache, with the per-head scale of
+// the cache or the block's scale from the table append_amax_kernel fills.
 template <int D, bool FP8>
 __global__ __launch_bounds__(128) void append_rope_k_kernel(const AppendArgs a, int es) {
   constexpr int G = D / 8;
@@ -2067,10 +2080,14 @@ __global__ __launch_bounds__(128) void append_rope_k_kernel(const AppendArgs a, 
     load8(src + (((int64_t)r * a.H + h) * D + 8 * g) * ies, ies, x);
     rope8<D>(x, ang);
     const int64_t e = (int64_t)h * a.head_stride_elems + (int64_t)r * D + 8 * g;
-    if constexpr (FP8)
-      *reinterpret_cast<uint2*>(static_cast<unsigned char*>(a.kdst) + e) = e4m3x8(x, a.k_scale[h]);
-    else
+    if constexpr (FP8) {
+      const float sc =
+          a.dev_scales ? a.ksc[(int64_t)append_scale_block(a) * a.H + h] : a.k_scale[h];
+      *reinterpret_cast<uint2*>(static_cast<unsigned char*>(a.kdst) + e) =
+          a.k_int8 ? int8x8(x, sc) : e4m3x8(x, sc);
+    } else {
       store8(static_cast<char*>(a.kdst) + e * es, es, x);
+    }
   }
 }
 
@@ -2108,7 +2125,7 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
           q.host_blk = 0;
           q.ksc = const_cast<float*>(a.cur_sc);
           q.vsc = const_cast<float*>(a.cur_sc) + a.H;
-          hipLaunchKernelGGL(append_amax_kernel<D>, dim3((unsigned)a.H, 2), dim3(1024), 0, s, q);
+          hipLaunchKernelGGL((append_amax_kernel<D, false>), dim3((unsigned)a.H, 2), dim3(1024), 0, s, q);
         }
         const int64_t total = (int64_t)a.n * a.H * (D / 8);
         hipLaunchKernelGGL(append_fp8_kernel<D>, dim3((unsigned)((total + 255) / 256), 2),
@@ -2206,8 +2223,12 @@ int launch_append(bca_dtype in, bca_dtype kv, int head_dim, const AppendArgs& a,
                    (unsigned)((a.H + kRopeHeads - 1) / kRopeHeads));
   if (kv == BCA_FP8_E4M3 || kv == BCA_FP8_E4M3_BLOCK || kv == BCA_INT8K_FP8V_BLOCK) {
     if (head_dim != 128 || in != BCA_BF16) return -1;
-    if (a.dev_scales)
-      hipLaunchKernelGGL(append_amax_kernel<128>, dim3((unsigned)a.H, 2), dim3(1024), 0, s, a);
+    if (a.dev_scales && a.rope)
+      hipLaunchKernelGGL((append_amax_kernel<128, true>), dim3((unsigned)a.H, 2), dim3(1024), 0, s,
+                         a);
+    else if (a.dev_scales)
+      hipLaunchKernelGGL((append_amax_kernel<128, false>), dim3((unsigned)a.H, 2), dim3(1024), 0,
+                         s, a);
     hipLaunchKernelGGL(append_fp8_kernel<128>, grid, dim3(256), 0, s, a, kv0);
     if (a.rope) hipLaunchKernelGGL((append_rope_k_kernel<128, true>), rgrid, dim3(128), 0, s, a, 1);
   } else {

@@ -162,7 +162,7 @@ bca_status bca_cache_set_kv_scales(bca_cache* cache, int32_t layer, const float*
  * in_dtype: F32 for an F32 cache, BF16 for BF16 and FP8_E4M3 caches (quantised
  * on the fly with the layer's scales) and for FP8_E4M3_BLOCK and
  * INT8K_FP8V_BLOCK caches (the block's per-head scales are first taken from
- * this chunk, then it is quantised with them; no rotary form).
+ * this chunk, then it is quantised with them).
  * Ordering: per layer, ring chunk ids are non-decreasing; an id equal to the
  * last one re-writes that chunk in place; a smaller id returns
  * BCA_ERR_OUT_OF_ORDER. chunk_id >= 0. For is_ref the id is recorded only. */
@@ -248,7 +248,8 @@ bca_status bca_attend_noalloc(const bca_cache* cache, int32_t layer, const bca_w
  * the same for every head. Angles are formed and reduced modulo pi/2 in double
  * precision, their cosines and sines taken in fp32 from the reduced angle, the
  * rotation done in fp32, and the result rounded to the destination
- * dtype (FP8_E4M3 caches: rotated, then quantised). rope_base must be finite
+ * dtype (8-bit caches: rotated, then quantised; on a per-block cache the
+ * block's K scale is taken over the rotated rows). rope_base must be finite
  * and > 0 (10000 is usual); positions must be >= 0. Token r of a chunk sits at
  * position pos0 + r; with pos0 = chunk id * n for every chunk, queries and keys
  * share one position axis and q.k depends only on the distance between tokens.

@@ -526,9 +526,11 @@ def test_block_scaled_fp8_cache_on_the_host(B):
     with pytest.raises(BcaError) as e:
         bca.bca_cache_set_kv_scales(h, 0, [1.0] * 4, [1.0] * 4)
     assert e.value.status == -4
+    # rotary appends and attends are accepted on these caches (the GPU tests
+    # run them); here only checks that fail before any launch
     with pytest.raises(BcaError) as e:
-        bca.bca_append_chunk_rope(h, 0, 0, 0, FAKE, FAKE, bca.BF16, 1e4, 0, 0)
-    assert e.value.status == -4
+        bca.bca_append_chunk_rope(h, 0, 0, 0, FAKE, FAKE, bca.BF16, float("nan"), 0, 0)
+    assert e.value.status == -1
     for sl in range(20):
         bca.bca_cache_set_slot_chunk(h, 0, sl, sl)
     bca.bca_cache_set_slot_chunk(h, 0, 20, 0)
@@ -538,10 +540,12 @@ def test_block_scaled_fp8_cache_on_the_host(B):
     assert plan["kv_tiles"] == 22 * 7 and plan["visible_keys"] == 22 * 405, plan
     need = bca.bca_attend_workspace_bytes(h, spec)
     assert need == plan["workspace_bytes"] and need >= 2 * 4 * 405 * 128 + 2 * 4 * 4
+    rneed = bca.bca_attend_rope_workspace_bytes(h, spec)
+    assert rneed >= need + 2 * 405 * 4 * 128 * 2  # the rotated Q and K copies on top
     with pytest.raises(BcaError) as e:
         bca.bca_attend_rope(h, 0, spec, FAKE, FAKE, FAKE, bca.BF16, 1e4, 0, FAKE, 0, FAKE,
-                            bca.bca_attend_rope_workspace_bytes(h, spec), 0)
-    assert e.value.status == -4
+                            rneed - 1, 0)
+    assert e.value.status == -3
     bca.bca_cache_destroy(h)
 
 

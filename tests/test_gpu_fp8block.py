@@ -129,6 +129,7 @@ def test_block_refused_calls():
         cache.set_kv_scales(0, [1.0, 1.0], [1.0, 1.0])
     assert e.value.status == -4
     _, k, v = Sequence(cache, 2, 128, 32, "fp8_block").chunk(0)
-    with pytest.raises(bca.BcaError) as e:
-        cache.append_chunk(0, 0, to_dev(k, "bf16"), to_dev(v, "bf16"), rope=(1e4, 0))
+    kf, vf = to_dev(k, "fp32"), to_dev(v, "fp32")
+    with pytest.raises(bca.BcaError) as e:  # only bf16 inputs are quantised into it
+        bca.bca_append_chunk(cache.handle, 0, 0, 0, kf.data_ptr(), vf.data_ptr(), bca.F32, 0)
     assert e.value.status == -4

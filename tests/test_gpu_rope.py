@@ -3,7 +3,10 @@ bca_attend_rope) against the CPU oracle's rotation (oracle.rope, fp64).
 
 Bars: the stored K equals the oracle's rotation rounded to the cache dtype,
 bf16 within one unit in the last place (plus 2e-6 where a pair's components
-cancel), fp32 within 4e-6, e4m3 codes equal or adjacent; attention as for bca_attend (1e-5 fp32, 1e-2 bf16, 5e-2 fp8).
+cancel), fp32 within 4e-6, 8-bit codes equal or adjacent (on a per-block
+cache with the block's K scale taken over the rotated rows, as the oracle's
+rule gives it to within the fp32 rotation's rounding); attention as for
+bca_attend (1e-5 fp32, 1e-2 bf16, the 8-bit bars of bca_harness.assert_fp8).
 """
 import math
 
@@ -12,8 +15,8 @@ import pytest
 
 import oracle
 import synth
-from bca_harness import (FP8_CACHE_ABS, FP8_CACHE_REL, TOL, assert_close, fp8_stored, log,
-                         max_err, to_dev, to_np)
+from bca_harness import (FP8_CACHE_ABS, FP8_CACHE_REL, TOL, assert_close, block_stored,
+                         fp8_stored, log, max_err, to_dev, to_np)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -96,13 +99,60 @@ def test_append_rope_fp8_codes():
         assert same / kc.size >= 0.99
 
 
+@pytest.mark.parametrize("kind", ["fp8_block", "int8k_block"])
+def test_append_rope_block_scales_and_codes(kind):
+    """A rotary append into a per-block cache: the block's K scales are the
+    oracle's rule (fp32 max |x| / 448, / 127 for int8 K) over the oracle's
+    rotation, to within the fp32 rotation's own rounding (the kernel rotates
+    in fp32, the oracle in fp64); the K codes, taken with the stored scale,
+    equal the oracle's or differ by one step where the two rotations fall on
+    either side of a rounding boundary; V is stored as given, bit for bit."""
+    H, d, n, S = 4, 128, 40, 2
+    cache = new_cache(1, H, d, n, S, dtype=kind)
+    int8 = kind == "int8k_block"
+    for t in (0, 3, 777):
+        _, k, v = synth.qkv(n, H, d, 6, t, 0, dtype="bf16", outlier_frac=0.01)
+        pos0 = t * n
+        cache.append_chunk(0, t, to_dev(k, "bf16"), to_dev(v, "bf16"), rope=(BASE, pos0))
+        torch.cuda.synchronize()
+        K, V = cache.blocks(0)
+        KS, VS = cache.block_scales(0)
+        blk = t % S
+        rot = oracle.rope(k.astype(np.float64), pos0, BASE).astype(np.float32)
+        want_ks = oracle.block_scales(rot, qmax=127.0 if int8 else 448.0)
+        gks = KS[blk].cpu().numpy()
+        assert np.allclose(gks, want_ks, rtol=2.0 ** -20, atol=0.0), (t, gks, want_ks)
+        assert np.array_equal(VS[blk].cpu().numpy(), oracle.block_scales(v)), t
+        kc = K[:, blk].cpu().numpy()
+        vc = V[:, blk].cpu().numpy()
+        same = 0
+        for h in range(H):
+            if int8:
+                got = kc[h].view(np.int8).astype(int)
+                want = oracle.quant_int8(rot[:, h, :], float(gks[h])).astype(int)
+                assert np.all(np.abs(got - want) <= 1), (t, h)
+                same += int(np.sum(got == want))
+            else:
+                want = oracle.quant_e4m3(rot[:, h, :], float(gks[h]))
+                dmag = np.abs((kc[h] & 0x7F).astype(int) - (want & 0x7F).astype(int))
+                sign_ok = ((kc[h] ^ want) & 0x80) == 0
+                assert np.all((dmag == 0) | ((dmag == 1) & sign_ok)), (t, h)
+                same += int(np.sum(kc[h] == want))
+            assert np.array_equal(vc[h], oracle.quant_e4m3(v[:, h, :], float(VS[blk][h]))), (t, h)
+        log(f"append rope {kind} t {t}: {same / kc.size:.4%} of K codes equal to the oracle's")
+        assert same / kc.size >= 0.99
+
+
 CASES = [
     # dtype, H, d, n, S, W, R, G, chunks
     ("bf16", 2, 128, 100, 2, 2, False, 0, 5),
     ("bf16", 3, 64, 130, 3, 2, True, 3, 5),
     ("fp32", 2, 64, 16, 2, 2, False, 2, 6),
     ("fp8", 4, 128, 405 // 5, 4, 3, True, 2, 6),
+    ("fp8_block", 4, 128, 405 // 5, 4, 3, True, 2, 6),
+    ("int8k_block", 3, 128, 100, 3, 2, True, 0, 5),
 ]
+EIGHT_BIT = ("fp8", "fp8_block", "int8k_block")
 
 
 @pytest.mark.parametrize("dtype,H,d,n,S,W,R,G,chunks", CASES)
@@ -120,6 +170,8 @@ def test_attend_rope_sequence(dtype, H, d, n, S, W, R, G, chunks):
     def stored(k, v):
         if dtype == "fp8":
             return fp8_stored(k, scales[0]), fp8_stored(v, scales[1])
+        if dtype in ("fp8_block", "int8k_block"):
+            return block_stored(dtype, k, v)
         return k.astype(np.float64), v.astype(np.float64)
 
     history, history_raw, ref, ref_raw = {}, {}, None, None
@@ -139,26 +191,26 @@ def test_attend_rope_sequence(dtype, H, d, n, S, W, R, G, chunks):
                               rope=(BASE, pos0))
         qr = oracle.rope(q.astype(np.float64), pos0, BASE)
         kr = oracle.rope(k.astype(np.float64), pos0, BASE)
-        if dtype == "fp8":
+        if dtype in EIGHT_BIT:
             # the staging pass writes the rotated K in the qkv dtype (bf16)
-            # before the e4m3 copy of the chunk is made from it
+            # before the 8-bit copy of the chunk is made from it
             ks, vs = stored(synth.round_bf16(kr).astype(np.float64), v)
         else:
             ks, vs = stored(kr, v)
         eo, el = oracle.attend(qr, ks, vs, history, t=t, W=W, scale=scale, ref=ref, use_ref=R)
-        if dtype == "fp8":
+        if dtype in EIGHT_BIT:
             # against the cache contents (the kernel's own error), then against
             # the unquantised rotated inputs: within the quantisation's own
             # error plus the kernel's bar (a few hundred keys; see assert_fp8)
             go, gl = to_np(o), to_np(lse)
-            log(f"rope fp8 t={t}: vs stored max|dO| {max_err(go, eo):.3e}, "
+            log(f"rope {dtype} t={t}: vs stored max|dO| {max_err(go, eo):.3e}, "
                 f"max|dLSE| {max_err(gl, el):.3e}")
             assert np.all(np.abs(go - eo) <= FP8_CACHE_ABS + FP8_CACHE_REL * np.abs(eo)), t
             assert max_err(gl, el) <= FP8_CACHE_ABS, t
             ro, rl = oracle.attend(qr, kr, v.astype(np.float64), history_raw, t=t, W=W,
                                    scale=scale, ref=ref_raw, use_ref=R)
             quant = max_err(eo, ro)
-            log(f"rope fp8 t={t}: vs raw max|dO| {max_err(go, ro):.3e}, quantisation alone "
+            log(f"rope {dtype} t={t}: vs raw max|dO| {max_err(go, ro):.3e}, quantisation alone "
                 f"{quant:.3e}")
             assert max_err(go, ro) <= quant + FP8_CACHE_ABS + FP8_CACHE_REL * np.abs(eo).max()
             assert max_err(gl, rl) <= max_err(el, rl) + FP8_CACHE_ABS
