@@ -1,17 +1,20 @@
 // bca_kernels.hip — gfx950 kernels of block-causal ring-KV chunk attention.
 //
 //   attn_bf16_kernel   bf16 flash attention on MFMA (v_mfma_f32_32x32x16_bf16)
-//   attn_fp8_kernel    e4m3-cache flash attention on the fp8 MFMA
-//                      (v_mfma_f32_32x32x64_f8f6f4)
+//   attn_fp8_kernel    8-bit-cache flash attention: e4m3 K and V on the fp8
+//                      MFMA (v_mfma_f32_32x32x64_f8f6f4), or int8 K on the
+//                      int8 MFMA (v_mfma_i32_32x32x32_i8) with e4m3 V
 //   attn_f32_kernel    fp32 flash attention on the vector ALUs
 //   merge_kernel       log-sum-exp merge of segment partials
 //   append_copy_kernel fused K/V write of one chunk into its ring slot
-//   append_fp8_kernel  the same with e4m3 quantisation (also the e4m3 copy of
-//                      the current chunk that the fp8 kernel reads)
+//   append_amax_kernel per-head scales of a per-block 8-bit append
+//   append_fp8_kernel  the same with 8-bit quantisation (also the 8-bit copy of
+//                      the current chunk that the 8-bit kernels read)
 //   rope_stage_kernel  rotary embedding of the current chunk's Q and K into
 //                      staging copies
-//   append_rope_k_kernel  the rotated K of an append (copy or e4m3)
+//   append_rope_k_kernel  the rotated K of an append (copy or 8-bit codes)
 //   counter_advance_kernel  the device-side chunk counter of a replayed step
+//   mfma_peak_kernel, mfma_peak_fp8_kernel  matrix-core rate probes
 //
 // What is computed follows "WanToFight" (xllm-io review), section 3 model
 // components table (block-causal attention: bidirectional in the chunk, causal
