@@ -211,9 +211,14 @@ float* block_scales(const bca_cache* c, int32_t layer, int kv) {
 int32_t slots_per_wg(int64_t units, int64_t P) { return (P >= units && P % units == 0) ? 1 : 2; }
 
 // Bytes of part_o [P][spw][bm][d] (sized for fp32), then part_lse [P][spw][bm]
-// fp32, each region 256-byte aligned.
+// fp32, each region 256-byte aligned. The bf16 path's fp16 partials fill the
+// first half of part_o; their row exponents [P][spw][bm] (int32) follow them
+// in the second half (part_exp_offset).
 size_t part_o_bytes(int64_t P, int32_t spw, int bm, int d) {
   return ((size_t)P * spw * bm * d * 4 + 255) & ~(size_t)255;
+}
+size_t part_exp_offset(int64_t P, int32_t spw, int bm, int d) {
+  return (size_t)P * spw * bm * d * 2;
 }
 size_t partial_bytes(int64_t P, int32_t spw, int bm, int d) {
   const size_t pl = (size_t)P * spw * bm * 4;
@@ -719,6 +724,8 @@ bca_status attend_impl(const bca_cache* c, int32_t layer, const bca_window_spec*
     a.part_o = static_cast<float*>(workspace);
     a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                           part_o_bytes(p.wgs, p.spw, p.bm, d.head_dim));
+    a.part_exp = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                            part_exp_offset(p.wgs, p.spw, p.bm, d.head_dim));
   }
   a.cache_head_elems = (int64_t)(d.ring_slots + d.has_ref) * d.chunk_tokens * d.head_dim;
   a.cache_span_elems = a.cache_head_elems;
@@ -909,6 +916,8 @@ bca_status attend_sequence_impl(const bca_sequence_spec* s, const void* q, const
       a.part_o = static_cast<float*>(workspace);
       a.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                             part_o_bytes(p.wgs, p.spw, p.bm, (int)D));
+      a.part_exp = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                              part_exp_offset(p.wgs, p.spw, p.bm, (int)D));
     }
     // the "cache" is the token-major K/V itself: heads d apart, rows H*d apart
     a.cache_head_elems = D;

@@ -85,8 +85,9 @@ struct AttnArgs {
   const void* vc;     // this layer's V blocks
   void* o;            // [n][H][d]
   float* lse;         // [H][n] or null
-  float* part_o;      // [P][spw][bm][d] (fp32, bf16 on the bf16 path)
+  float* part_o;      // [P][spw][bm][d]: fp32, or fp16 scaled per row on the bf16 path
   float* part_lse;    // [P][spw][bm]
+  int32_t* part_exp;  // [P][spw][bm]: the bf16 path's row exponents (see merge_kernel)
   int64_t cache_head_elems;  // elements between heads' first cache rows: (S+R)*n*d for the
                              // ring, d for a token-major sequence [rows][H][d]
   int64_t cache_span_elems;  // elements one head's cache rows span (buffer resource size)
@@ -126,6 +127,7 @@ struct AttnArgs {
 struct MergeArgs {
   const float* part_o;
   const float* part_lse;
+  const int32_t* part_exp;  // fp16 partials only
   void* o;
   float* lse;
   int32_t n, H, T, QT, units, P, spw, bm;

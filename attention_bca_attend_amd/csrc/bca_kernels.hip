@@ -49,6 +49,8 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -796,19 +798,36 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
         } else {
           const int64_t prow =
               part_slot(w, u, I, a.T, a.P, a.spw) * C::BM + (wave & 7) * 32 + l32;
-          // bf16 partial outputs (normalised, so |O| stays within the values' range)
-          __bf16* pp = reinterpret_cast<__bf16*>(a.part_o) + prow * D;
+          // fp16 partial outputs with a power-of-two scale per row: the row's
+          // largest |O| (over the lane pair that holds the row) is brought into
+          // [0.5, 1), so a value is rounded to within 2^-12 of that maximum
+          // (bf16 would give 2^-9) in the same two bytes; the exponent goes to
+          // part_exp and the merge multiplies it back exactly. A row with a
+          // NaN or an infinity keeps exponent 0 and carries them through.
+          float mx = 0.f;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(st.o[db][e]));
+          mx = xhalf_max(mx) * inv;
+          int ex = 0;
+          if (mx > 0.f && mx <= 3.402823466e38f) (void)frexpf(mx, &ex);
+          const float sc = __builtin_amdgcn_ldexpf(inv, -ex);
+          _Float16* pp = reinterpret_cast<_Float16*>(a.part_o) + prow * D;
 #pragma unroll
           for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               f32x4_t v4 = {st.o[db][4 * g], st.o[db][4 * g + 1], st.o[db][4 * g + 2],
                             st.o[db][4 * g + 3]};
-              v4 *= inv;
-              *reinterpret_cast<bf16x4_t*>(pp + 32 * db + 8 * g + 4 * hi) =
-                  __builtin_convertvector(v4, bf16x4_t);
+              v4 *= sc;
+              *reinterpret_cast<f16x4_t*>(pp + 32 * db + 8 * g + 4 * hi) =
+                  __builtin_convertvector(v4, f16x4_t);
             }
-          if (hi == 0) a.part_lse[prow] = lse_val;
+          if (hi == 0) {
+            a.part_lse[prow] = lse_val;
+            a.part_exp[prow] = ex;
+          }
         }
       }
     }
@@ -1644,7 +1663,8 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(const AttnArgs a) {
 constexpr int kMergeBatch = 4;
 constexpr int kMergeEpt = 16;  // dims per thread
 
-// Eight partial-output values: fp32 (fp32 path, e4m3 cache) or bf16 (bf16 path).
+// Eight partial-output values: fp32 (fp32 path, 8-bit caches) or fp16 scaled
+// by 2^-e per row (bf16 path; e in part_exp).
 __device__ __forceinline__ void load_part8(const float* p, float (&x)[8]) {
   const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
   const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
@@ -1654,8 +1674,8 @@ __device__ __forceinline__ void load_part8(const float* p, float (&x)[8]) {
     x[4 + i] = b[i];
   }
 }
-__device__ __forceinline__ void load_part8(const __bf16* p, float (&x)[8]) {
-  const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(p);
+__device__ __forceinline__ void load_part8(const _Float16* p, float (&x)[8]) {
+  const f16x8_t v = *reinterpret_cast<const f16x8_t*>(p);
 #pragma unroll
   for (int i = 0; i < 8; ++i) x[i] = (float)v[i];
 }
@@ -1694,6 +1714,11 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
     return j == 0 ? prow0 : ((w0 + j) * a.spw) * a.bm + rloc;
   };
   const PartT* part = reinterpret_cast<const PartT*>(a.part_o);
+  constexpr bool SCALED = sizeof(PartT) == 2;  // fp16 partials with row exponents
+  // piece j's weight on its stored values: w_j, times 2^e_j for fp16 partials
+  auto scaled = [&](float wj, int64_t prow) {
+    return SCALED ? __builtin_amdgcn_ldexpf(wj, a.part_exp[prow]) : wj;
+  };
   float M = -INFINITY, wsum = 0.f;
   float acc[8 * NG];
 #pragma unroll
@@ -1721,8 +1746,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
         if (j < pieces) {
           const float wj = (lj[j] == -INFINITY) ? 0.f : expf(lj[j] - M);
           wsum += wj;
+          const float ws = scaled(wj, prow_of(j));
 #pragma unroll
-          for (int i = 0; i < 8 * NG; ++i) acc[i] += wj * oj[j][i];
+          for (int i = 0; i < 8 * NG; ++i) acc[i] += ws * oj[j][i];
         }
       }
     }
@@ -1734,12 +1760,13 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
         const float lj = a.part_lse[prow];
         const float wj = (lj == -INFINITY) ? 0.f : expf(lj - M);
         wsum += wj;
+        const float ws = scaled(wj, prow);
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
           float oj[8];
           load_part8(part + prow * D + c8 + 8 * g, oj);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[8 * g + i] += wj * oj[i];
+          for (int i = 0; i < 8; ++i) acc[8 * g + i] += ws * oj[i];
         }
       }
     }
@@ -2163,6 +2190,7 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
     MergeArgs m{};
     m.part_o = a.part_o;
     m.part_lse = a.part_lse;
+    m.part_exp = a.part_exp;
     m.o = a.o;
     m.lse = a.lse;
     m.n = a.n;
@@ -2183,7 +2211,7 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
     else if (p.kern == Kern::FP8)
       hipLaunchKernelGGL((merge_kernel<D, __bf16, float>), dim3(blocks), dim3(256), 0, s, m);
     else
-      hipLaunchKernelGGL((merge_kernel<D, __bf16, __bf16>), dim3(blocks), dim3(256), 0, s, m);
+      hipLaunchKernelGGL((merge_kernel<D, __bf16, _Float16>), dim3(blocks), dim3(256), 0, s, m);
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
   }
