@@ -804,6 +804,10 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
           // (bf16 would give 2^-9) in the same two bytes; the exponent goes to
           // part_exp and the merge multiplies it back exactly. A row with a
           // NaN or an infinity keeps exponent 0 and carries them through.
+          // The wave's 32 rows are stored as the lanes hold them (chunk
+          // 2 db + hf of lane l at 16 bytes x (64 (2 db + hf) + l) from the
+          // wave's first row), so that each store writes 1 KB of consecutive
+          // bytes; merge_lanes_kernel reads that layout.
           float mx = 0.f;
 #pragma unroll
           for (int db = 0; db < D / 32; ++db)
@@ -813,16 +817,16 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
           int ex = 0;
           if (mx > 0.f && mx <= 3.402823466e38f) (void)frexpf(mx, &ex);
           const float sc = __builtin_amdgcn_ldexpf(inv, -ex);
-          _Float16* pp = reinterpret_cast<_Float16*>(a.part_o) + prow * D;
+          _Float16* pp = reinterpret_cast<_Float16*>(a.part_o) + (prow - l32) * D + lane * 8;
 #pragma unroll
           for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              f32x4_t v4 = {st.o[db][4 * g], st.o[db][4 * g + 1], st.o[db][4 * g + 2],
-                            st.o[db][4 * g + 3]};
-              v4 *= sc;
-              *reinterpret_cast<f16x4_t*>(pp + 32 * db + 8 * g + 4 * hi) =
-                  __builtin_convertvector(v4, f16x4_t);
+            for (int hf = 0; hf < 2; ++hf) {
+              f32x8_t v8;
+#pragma unroll
+              for (int j = 0; j < 8; ++j) v8[j] = st.o[db][8 * hf + j] * sc;
+              *reinterpret_cast<f16x8_t*>(pp + (2 * db + hf) * 512) =
+                  __builtin_convertvector(v8, f16x8_t);
             }
           if (hi == 0) {
             a.part_lse[prow] = lse_val;
@@ -1656,15 +1660,15 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(const AttnArgs a) {
 // Log-sum-exp merge of the segments of every split unit:
 //   M = max_g LSE_g, w_g = exp(LSE_g - M) (0 for LSE_g = -inf),
 //   O = sum_g w_g O_g / sum_g w_g, LSE = M + ln sum_g w_g.
-// One work group covers 256 / (D/16) rows of one unit; each thread sixteen
-// dims (two 16-byte loads per bf16 piece). The unit's first piece and piece count
-// come from the range arithmetic once per work group (thread 0, through LDS).
+// merge_kernel reads fp32 partials stored row by row (fp32 path, 8-bit
+// caches): one work group covers 256 / (D/16) rows of one unit, each thread
+// sixteen dims. The unit's first piece and piece count come from the range
+// arithmetic once per work group (thread 0, through LDS).
 // Pieces whose loads the merge issues all at once.
 constexpr int kMergeBatch = 4;
 constexpr int kMergeEpt = 16;  // dims per thread
 
-// Eight partial-output values: fp32 (fp32 path, 8-bit caches) or fp16 scaled
-// by 2^-e per row (bf16 path; e in part_exp).
+// Eight fp32 partial-output values (fp32 path, 8-bit caches).
 __device__ __forceinline__ void load_part8(const float* p, float (&x)[8]) {
   const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
   const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
@@ -1674,13 +1678,7 @@ __device__ __forceinline__ void load_part8(const float* p, float (&x)[8]) {
     x[4 + i] = b[i];
   }
 }
-__device__ __forceinline__ void load_part8(const _Float16* p, float (&x)[8]) {
-  const f16x8_t v = *reinterpret_cast<const f16x8_t*>(p);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) x[i] = (float)v[i];
-}
-
-template <int D, typename OutT, typename PartT>
+template <int D, typename OutT>
 __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   constexpr int NG = kMergeEpt / 8, TPR = D / kMergeEpt, RPB = 256 / TPR;
   const int blocks_per_unit = (a.bm + RPB - 1) / RPB;
@@ -1713,12 +1711,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   auto prow_of = [&](int j) -> int64_t {
     return j == 0 ? prow0 : ((w0 + j) * a.spw) * a.bm + rloc;
   };
-  const PartT* part = reinterpret_cast<const PartT*>(a.part_o);
-  constexpr bool SCALED = sizeof(PartT) == 2;  // fp16 partials with row exponents
-  // piece j's weight on its stored values: w_j, times 2^e_j for fp16 partials
-  auto scaled = [&](float wj, int64_t prow) {
-    return SCALED ? __builtin_amdgcn_ldexpf(wj, a.part_exp[prow]) : wj;
-  };
+  const float* part = a.part_o;
   float M = -INFINITY, wsum = 0.f;
   float acc[8 * NG];
 #pragma unroll
@@ -1746,9 +1739,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
         if (j < pieces) {
           const float wj = (lj[j] == -INFINITY) ? 0.f : expf(lj[j] - M);
           wsum += wj;
-          const float ws = scaled(wj, prow_of(j));
 #pragma unroll
-          for (int i = 0; i < 8 * NG; ++i) acc[i] += ws * oj[j][i];
+          for (int i = 0; i < 8 * NG; ++i) acc[i] += wj * oj[j][i];
         }
       }
     }
@@ -1760,13 +1752,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
         const float lj = a.part_lse[prow];
         const float wj = (lj == -INFINITY) ? 0.f : expf(lj - M);
         wsum += wj;
-        const float ws = scaled(wj, prow);
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
           float oj[8];
           load_part8(part + prow * D + c8 + 8 * g, oj);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[8 * g + i] += ws * oj[i];
+          for (int i = 0; i < 8; ++i) acc[8 * g + i] += wj * oj[i];
         }
       }
     }
@@ -1790,6 +1781,112 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
   }
   if (c8 == 0 && a.lse)
     a.lse[ci * a.chunk_lse + (int64_t)h * a.n + row] = (M == -INFINITY) ? M : M + logf(wsum);
+}
+
+// merge_lanes_kernel reads the bf16 path's fp16 partials, stored per wave as
+// the attention kernel's lanes hold them: for the wave's 32 rows, 16-byte
+// chunk c = 2 db + hf of lane l (values o[db][8 hf .. 8 hf + 7], i.e. dims
+// 32 db + 16 hf + 4 (l / 32) + {0..3, 8..11} of row l % 32) at 16 (64 c + l)
+// bytes from the wave's start, each row's values scaled by 2^-part_exp.
+// One work group merges one 32-row slice of a unit: its threads read the
+// chunks of every piece in order (consecutive threads, consecutive 16
+// bytes; all of a thread's chunks belong to one row), combine them, and
+// write the result out through LDS as whole rows.
+template <int D>
+__global__ __launch_bounds__(256) void merge_lanes_kernel(const MergeArgs a) {
+  constexpr int NCH = 4 * D / 256;  // chunks per thread: a slice holds 4 D of them
+  constexpr int RS = D + 8;         // LDS row stride (elements), off the bank period
+  __shared__ __bf16 tile[32 * RS];
+  const int slices = a.bm / 32;
+  const int u = blockIdx.x / slices;
+  const int sl = blockIdx.x - u * slices;
+  const int64_t I = (int64_t)a.units * a.T;
+  const int64_t w0 = first_wg_of((int64_t)u * a.T, I, a.P);
+  const int pieces = (int)(first_wg_of((int64_t)(u + 1) * a.T - 1, I, a.P) - w0 + 1);
+  if (pieces <= 1) return;  // written whole by the attention kernel
+  const int ci = u / a.upc, ul = u - ci * a.upc;  // chunk of a batched launch
+  const int h = ul / a.QT, qt = ul - h * a.QT;
+  const int row0 = qt * a.bm + sl * 32;  // the slice's first query row
+  if (row0 >= a.n) return;
+  const int t = threadIdx.x;
+  const int lane = t & 63, r = lane & 31, hi = lane >> 5;
+  const bool live = row0 + r < a.n;
+  const int64_t slot0 = part_slot(w0, u, I, a.T, a.P, a.spw);
+  // piece j >= 1 has the slot of its own (its range starts inside unit u)
+  auto slot_of = [&](int j) -> int64_t { return j == 0 ? slot0 : (w0 + j) * a.spw; };
+  const _Float16* part = reinterpret_cast<const _Float16*>(a.part_o);
+  float M = -INFINITY, wsum = 0.f;
+  float acc[8 * NCH];
+#pragma unroll
+  for (int i = 0; i < 8 * NCH; ++i) acc[i] = 0.f;
+  if (live) {
+    for (int j0 = 0; j0 < pieces; j0 += kMergeBatch) {
+      // every load of a batch of pieces first, then the combination
+      float lj[kMergeBatch];
+      int ej[kMergeBatch];
+      f16x8_t vj[kMergeBatch][NCH];
+#pragma unroll
+      for (int b = 0; b < kMergeBatch; ++b) {
+        if (j0 + b < pieces) {
+          const int64_t base = (slot_of(j0 + b) * a.bm + sl * 32);
+          lj[b] = a.part_lse[base + r];
+          ej[b] = a.part_exp[base + r];
+#pragma unroll
+          for (int k = 0; k < NCH; ++k)
+            vj[b][k] = *reinterpret_cast<const f16x8_t*>(part + base * D + (t + 256 * k) * 8);
+        }
+      }
+      float Mb = M;
+#pragma unroll
+      for (int b = 0; b < kMergeBatch; ++b)
+        if (j0 + b < pieces) Mb = fmaxf(Mb, lj[b]);
+      if (Mb == -INFINITY) continue;
+      // rescale what earlier batches summed to the new maximum
+      const float rs = (M == -INFINITY) ? 0.f : expf(M - Mb);
+      wsum *= rs;
+#pragma unroll
+      for (int i = 0; i < 8 * NCH; ++i) acc[i] *= rs;
+      M = Mb;
+#pragma unroll
+      for (int b = 0; b < kMergeBatch; ++b) {
+        if (j0 + b < pieces) {
+          const float wj = (lj[b] == -INFINITY) ? 0.f : expf(lj[b] - M);
+          wsum += wj;
+          const float ws = __builtin_amdgcn_ldexpf(wj, ej[b]);
+#pragma unroll
+          for (int k = 0; k < NCH; ++k)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[8 * k + i] += ws * (float)vj[b][k][i];
+        }
+      }
+    }
+  }
+  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  // the thread's values into the slice's rows in LDS (two runs of 4 dims per chunk)
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) {
+    const int c = (t >> 6) + 4 * k, db = c >> 1, hf = c & 1;
+    const int d0 = 32 * db + 16 * hf + 4 * hi;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      f32x4_t v4 = {acc[8 * k + 4 * g], acc[8 * k + 4 * g + 1], acc[8 * k + 4 * g + 2],
+                    acc[8 * k + 4 * g + 3]};
+      v4 *= inv;
+      *reinterpret_cast<bf16x4_t*>(&tile[r * RS + d0 + 8 * g]) = __builtin_convertvector(v4, bf16x4_t);
+    }
+  }
+  if (t < 32 && live && a.lse)
+    a.lse[ci * a.chunk_lse + (int64_t)h * a.n + row0 + r] = (M == -INFINITY) ? M : M + logf(wsum);
+  __syncthreads();
+  // whole rows out: 16 bytes per thread, D / 8 threads per row
+  __bf16* ob = static_cast<__bf16*>(a.o) + ci * a.chunk_elems;
+#pragma unroll
+  for (int k = 0; k < NCH; ++k) {
+    const int q = t + 256 * k, rr = q / (D / 8), c8 = q - rr * (D / 8);
+    if (row0 + rr < a.n)
+      *reinterpret_cast<bf16x8_t*>(ob + ((int64_t)(row0 + rr) * a.H + h) * D + 8 * c8) =
+          *reinterpret_cast<const bf16x8_t*>(&tile[rr * RS + 8 * c8]);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -2207,11 +2304,11 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
     constexpr int RPB = 256 / (D / kMergeEpt);
     const int blocks = a.units * ((p.bm + RPB - 1) / RPB);
     if (p.kern == Kern::F32)
-      hipLaunchKernelGGL((merge_kernel<D, float, float>), dim3(blocks), dim3(256), 0, s, m);
+      hipLaunchKernelGGL((merge_kernel<D, float>), dim3(blocks), dim3(256), 0, s, m);
     else if (p.kern == Kern::FP8)
-      hipLaunchKernelGGL((merge_kernel<D, __bf16, float>), dim3(blocks), dim3(256), 0, s, m);
+      hipLaunchKernelGGL((merge_kernel<D, __bf16>), dim3(blocks), dim3(256), 0, s, m);
     else
-      hipLaunchKernelGGL((merge_kernel<D, __bf16, _Float16>), dim3(blocks), dim3(256), 0, s, m);
+      hipLaunchKernelGGL(merge_lanes_kernel<D>, dim3(a.units * (p.bm / 32)), dim3(256), 0, s, m);
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
   }
