@@ -1506,19 +1506,34 @@ __global__ __launch_bounds__(512) void attn_fp8_kernel(const AttnArgs a) {
             }
           if (hi == 0 && a.lse) a.lse[(int64_t)h * a.n + row] = lse_val;
         } else {
+          // fp16 partials scaled per row, stored as the lanes hold them: the
+          // bf16 kernel's format, merged by merge_lanes_kernel
           const int64_t prow =
               part_slot(w, u, I, a.T, a.P, a.spw) * C::BM + (wave & 7) * 32 + l32;
-          float* pp = a.part_o + prow * D;
+          float mx = 0.f;
 #pragma unroll
           for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              f32x4_t v4 = {st.o[db][4 * g], st.o[db][4 * g + 1], st.o[db][4 * g + 2],
-                            st.o[db][4 * g + 3]};
-              v4 *= inv;
-              *reinterpret_cast<f32x4_t*>(pp + 32 * db + 8 * g + 4 * hi) = v4;
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(st.o[db][e]));
+          mx = xhalf_max(mx) * inv;
+          int ex = 0;
+          if (mx > 0.f && mx <= 3.402823466e38f) (void)frexpf(mx, &ex);
+          const float sc = __builtin_amdgcn_ldexpf(inv, -ex);
+          _Float16* pp = reinterpret_cast<_Float16*>(a.part_o) + (prow - l32) * D + lane * 8;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+              f32x8_t v8;
+#pragma unroll
+              for (int j = 0; j < 8; ++j) v8[j] = st.o[db][8 * hf + j] * sc;
+              *reinterpret_cast<f16x8_t*>(pp + (2 * db + hf) * 512) =
+                  __builtin_convertvector(v8, f16x8_t);
             }
-          if (hi == 0) a.part_lse[prow] = lse_val;
+          if (hi == 0) {
+            a.part_lse[prow] = lse_val;
+            a.part_exp[prow] = ex;
+          }
         }
       }
     }
@@ -2305,8 +2320,6 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
     const int blocks = a.units * ((p.bm + RPB - 1) / RPB);
     if (p.kern == Kern::F32)
       hipLaunchKernelGGL((merge_kernel<D, float>), dim3(blocks), dim3(256), 0, s, m);
-    else if (p.kern == Kern::FP8)
-      hipLaunchKernelGGL((merge_kernel<D, __bf16>), dim3(blocks), dim3(256), 0, s, m);
     else
       hipLaunchKernelGGL(merge_lanes_kernel<D>, dim3(a.units * (p.bm / 32)), dim3(256), 0, s, m);
     e = hipGetLastError();

@@ -485,7 +485,7 @@ def main_sequence(args, cfg):
         "step_ms_min_max": [round(min(step_ms), 4), round(max(step_ms), 4)],
         "roofline": roofline_mfma(tflops, "bf16", measured_traffic(cfg["workload"]),
                                   f"bca_attend_sequence: {C} x (attn_bf16_kernel + "
-                                  f"merge_kernel where split)"),
+                                  f"merge_lanes_kernel where split)"),
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
@@ -697,7 +697,7 @@ def main():
                else "attn_fp8_kernel (int8 K, block scales) + append_amax_kernel + "
                     "append_fp8_kernel (chunk copy)" if fp8
                else "attn_bf16_kernel")
-            + (" + merge_kernel" if plan["merge"] else "")),
+            + (" + merge_lanes_kernel" if plan["merge"] else "")),
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
