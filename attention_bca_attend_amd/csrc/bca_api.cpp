@@ -837,28 +837,114 @@ void seq_plan(const bca_sequence_spec* s, int32_t qkv_dtype, int cus, int64_t c,
   p.ws_bytes = p.merge ? partial_bytes(p.wgs, p.spw, p.bm, s->head_dim) : 0;
 }
 
-// The launches of a sequence: (first chunk, chunk count). Chunks before the
-// steady window go one by one; from chunk W (W + 1 with a prefix, where chunk
-// W's window still touches the prefix) on every chunk sees the same number of
-// keys, and the bf16 kernel takes them all in one launch. The fp32 kernel
-// runs chunk by chunk.
-std::vector<std::pair<int64_t, int64_t>> seq_launches(const bca_sequence_spec* s,
-                                                      int32_t qkv_dtype) {
-  std::vector<std::pair<int64_t, int64_t>> out;
+// The launches of a sequence. Chunks before the steady window go one by one;
+// from chunk W (W + 1 with a prefix, where chunk W's window still touches
+// the prefix) on every chunk sees the same number of keys, and the bf16
+// kernel takes them all in one launch. The fp32 kernel runs chunk by chunk.
+// With the automatic split on the bf16 path, when the chunks fill the device
+// with units, the last kMaxGroups of those launches become one launch of
+// groups (UnitGroup): that launch is cut stream-K style anyway, and the
+// chunks before the window is full no longer pay a launch, a split and a
+// merge each.
+struct SeqLaunch {
+  int64_t c, count;            // chunks c .. c + count - 1
+  int32_t ng;                  // > 0: a launch of ng groups
+  int64_t gc[kMaxGroups];      // first chunk of each group
+  int64_t gn[kMaxGroups];      // chunks of each group
+};
+
+std::vector<SeqLaunch> seq_launches(const bca_sequence_spec* s, int32_t qkv_dtype, int cus) {
   const int64_t C = s->num_chunks;
   const int64_t steady = (int64_t)s->history + (s->prefix_tokens > 0 ? 1 : 0);
   const int64_t single = qkv_dtype == BCA_BF16 ? std::min(C, steady) : C;
-  for (int64_t c = 0; c < single; ++c) out.push_back({c, 1});
-  if (single < C) out.push_back({single, C - single});
+  std::vector<std::pair<int64_t, int64_t>> plain;
+  for (int64_t c = 0; c < single; ++c) plain.push_back({c, 1});
+  if (single < C) plain.push_back({single, C - single});
+  const size_t first = plain.size() > (size_t)kMaxGroups ? plain.size() - kMaxGroups : 0;
+  const int64_t bm = tile_shape(Kern::BF16).bm;
+  const int64_t units = (C - plain[first].first) * s->num_heads * ((s->chunk_tokens + bm - 1) / bm);
+  const bool group = qkv_dtype == BCA_BF16 && s->num_segments == 0 && plain.size() - first >= 2 &&
+                     units >= (int64_t)cus * wgs_per_cu(Kern::BF16);
+  std::vector<SeqLaunch> out;
+  const size_t ungrouped = group ? first : plain.size();
+  for (size_t i = 0; i < ungrouped; ++i) {
+    SeqLaunch L{};
+    L.c = plain[i].first;
+    L.count = plain[i].second;
+    out.push_back(L);
+  }
+  if (group) {
+    SeqLaunch L{};
+    L.c = plain[first].first;
+    L.count = C - L.c;
+    L.ng = (int32_t)(plain.size() - first);
+    for (int g = 0; g < L.ng; ++g) {
+      L.gc[g] = plain[first + g].first;
+      L.gn[g] = plain[first + g].second;
+    }
+    out.push_back(L);
+  }
   return out;
+}
+
+// Plan of one launch of a sequence: seq_plan's, or for a launch of groups
+// each group's own (its chunks' runs, keys and tiles), the units numbered
+// group after group, and one range of tile iterations per resident work
+// group over all of them.
+void seq_launch_plan(const bca_sequence_spec* s, int32_t qkv_dtype, int cus, const SeqLaunch& L,
+                     Plan& p) {
+  if (L.ng == 0) {
+    seq_plan(s, qkv_dtype, cus, L.c, L.count, p);
+    return;
+  }
+  Plan gp;
+  seq_plan(s, qkv_dtype, cus, L.gc[L.ng - 1], L.gn[L.ng - 1], gp);
+  p = gp;  // the last group's fields stand as the launch's own
+  int64_t units = 0, iters = 0;
+  int nruns = 0;
+  for (int g = 0; g < L.ng; ++g) {
+    seq_plan(s, qkv_dtype, cus, L.gc[g], L.gn[g], gp);
+    UnitGroup& G = p.grp[g];
+    G = UnitGroup{};
+    G.iter0 = iters;
+    G.units0 = (int32_t)units;
+    G.T = gp.kv_tiles;
+    G.cache_tiles = gp.cache_tiles;
+    G.nk_cache = gp.nk_cache;
+    G.run0 = nruns;
+    G.nruns = gp.nruns;
+    G.chunk0 = (int32_t)(L.gc[g] - L.c);
+    for (int i = 0; i < gp.nruns; ++i) p.runs[nruns++] = gp.runs[i];
+    units += gp.units;
+    iters += (int64_t)gp.units * gp.kv_tiles;
+  }
+  p.ngroups = L.ng;
+  p.iters = iters;
+  p.nruns = nruns;
+  p.units = (int32_t)units;
+  p.wgs = (int32_t)std::max<int64_t>(1, std::min<int64_t>(iters, (int64_t)cus * wgs_per_cu(p.kern)));
+  int32_t worst = 1;
+  for (int g = 0; g < L.ng; ++g) {
+    const UnitGroup& G = p.grp[g];
+    const int64_t gu = (g + 1 < L.ng ? p.grp[g + 1].units0 : units) - G.units0;
+    for (int64_t u = 0; u < gu; ++u) {
+      const int64_t x = G.iter0 + u * G.T;
+      const int64_t pieces = first_wg(x + G.T - 1, iters, p.wgs) - first_wg(x, iters, p.wgs) + 1;
+      worst = std::max<int32_t>(worst, (int32_t)pieces);
+    }
+  }
+  p.jmax = worst;
+  p.merge = worst > 1 ? 1 : 0;
+  p.spw = 2;  // ranges end one unit and start the next
+  p.ws_bytes = p.merge ? partial_bytes(p.wgs, p.spw, p.bm, s->head_dim) : 0;
 }
 
 // The workspace is the largest any launch of the sequence needs.
 size_t seq_workspace(const bca_sequence_spec* s, int32_t qkv_dtype, int cus) {
   size_t ws = 0;
-  for (const auto& l : seq_launches(s, qkv_dtype)) {
+  for (const auto& l : seq_launches(s, qkv_dtype, cus)) {
     Plan p;
-    seq_plan(s, qkv_dtype, cus, l.first, l.second, p);
+    seq_launch_plan(s, qkv_dtype, cus, l, p);
     ws = std::max(ws, p.ws_bytes);
   }
   return ws;
@@ -897,10 +983,10 @@ bca_status attend_sequence_impl(const bca_sequence_spec* s, const void* q, const
   const int64_t n = s->chunk_tokens, H = s->num_heads, D = s->head_dim, P = s->prefix_tokens;
   const size_t es = elem_size(qkv_dtype);
   const int64_t rows = P + (int64_t)s->num_chunks * n;
-  for (const auto& l : seq_launches(s, qkv_dtype)) {
-    const int64_t c = l.first;
+  for (const auto& l : seq_launches(s, qkv_dtype, cus)) {
+    const int64_t c = l.c;
     Plan p;
-    seq_plan(s, qkv_dtype, cus, c, l.second, p);
+    seq_launch_plan(s, qkv_dtype, cus, l, p);
     AttnArgs a;
     std::memset(&a, 0, sizeof a);
     const size_t chunk_off = (size_t)(c * n * H * D) * es;      // chunk c's rows of q and o
@@ -942,6 +1028,9 @@ bca_status attend_sequence_impl(const bca_sequence_spec* s, const void* q, const
     a.chunk_lse = H * n;
     a.nruns = p.nruns;
     for (int i = 0; i < p.nruns; ++i) a.runs[i] = p.runs[i];
+    a.ngroups = p.ngroups;
+    a.iters = p.iters;
+    for (int g = 0; g < p.ngroups; ++g) a.grp[g] = p.grp[g];
     const int err = launch_attention(p, a, (int)D, (void*)stream);
     if (err != 0)
       return fail(BCA_ERR_HIP, "attention launch for chunk %lld failed (hip error %d)",

@@ -12,6 +12,7 @@ namespace bca {
 constexpr int kMaxBlocks = 64;  // ring slots + reference + current chunk
 constexpr int kMaxHeadsFp8 = 64;
 constexpr int kMaxSegments = 64;
+constexpr int kMaxGroups = 8;
 
 // A maximal range of consecutive visible cache keys that sits at one base
 // address. Visible cache keys are numbered 0 .. nk_cache-1 in "key order":
@@ -29,6 +30,22 @@ struct Run {
   int32_t moves;   // 1: in a launch over several chunks of a sequence, the run
                    // moves down by chunk_rows rows per chunk (the window);
                    // 0: it stays (a memory prefix)
+};
+
+// Consecutive chunks of a bca_attend_sequence launch that share a plan: the
+// same keys per unit (T tiles) and the same runs, whose moving runs shift by
+// chunk_rows rows per chunk of the group. A launch with groups (ngroups > 0)
+// holds chunks whose windows differ in length (the chunks before the window
+// is full); its units are numbered chunk by chunk, group after group.
+struct UnitGroup {
+  int64_t iter0;        // first tile iteration of the group
+  int32_t units0;       // first unit of the group
+  int32_t T;            // key tiles per unit
+  int32_t cache_tiles;  // key tiles over the cache keys
+  int32_t nk_cache;     // visible cache keys
+  int32_t run0, nruns;  // the group's runs: runs[run0 .. run0 + nruns)
+  int32_t chunk0;       // the group's first chunk, counted from the launch's first
+  int32_t pad;
 };
 
 // Kernel families; each has fixed tile sizes.
@@ -70,6 +87,9 @@ struct Plan {
   int32_t jmax;                     // most work groups any unit is split over
   int32_t spw;                      // partial-output slots per work group (1 or 2)
   int32_t merge;                    // 1: some unit is split over work groups
+  int32_t ngroups;                  // > 0: units of different lengths (see UnitGroup)
+  int64_t iters;                    // tile iterations of the launch
+  UnitGroup grp[kMaxGroups];
   size_t stage_off;                 // fp8 cache: offset of the current-chunk staging copy
   size_t ws_bytes;                  // workspace this call needs
 };
@@ -118,6 +138,12 @@ struct AttnArgs {
   // current chunk's scales [K|V][H]; vis_blk the physical block of each of the
   // nvis_cache visible cache blocks.
   int32_t blk, i8k, tpb, nvis_cache;
+  // Grouped sequence launches: ngroups > 0 groups of units (UnitGroup), iters
+  // tile iterations in all; otherwise every unit has T tiles and the runs,
+  // nk_cache and cache_tiles above.
+  int32_t ngroups;
+  int64_t iters;
+  UnitGroup grp[kMaxGroups];
   const float* ksc;
   const float* vsc;
   const float* cur_sc;
@@ -134,6 +160,9 @@ struct MergeArgs {
   int32_t upc;          // units per chunk (see AttnArgs)
   int64_t chunk_elems;  // o elements per chunk
   int64_t chunk_lse;    // lse floats per chunk
+  int32_t ngroups;      // grouped launch (see AttnArgs)
+  int64_t iters;
+  UnitGroup grp[kMaxGroups];
 };
 
 struct AppendArgs {

@@ -73,6 +73,46 @@ __device__ __forceinline__ int64_t part_slot(int64_t w, int64_t u, int64_t I, in
   return (int64_t)spw * w + (u != range_begin(w, I, P) / T ? 1 : 0);
 }
 
+// Launches whose units differ in length (ngroups > 0, see UnitGroup): the
+// group holding unit u or iteration it, the launch's iterations, the first
+// iteration of unit u, the unit holding iteration it. With ngroups = 0 every
+// unit has T tiles.
+template <typename Args>
+__device__ __forceinline__ int group_of_unit(const Args& a, int64_t u) {
+  int g = 0;
+  for (int i = 1; i < a.ngroups; ++i)
+    if (u >= a.grp[i].units0) g = i;
+  return g;
+}
+template <typename Args>
+__device__ __forceinline__ int group_of_iter(const Args& a, int64_t it) {
+  int g = 0;
+  for (int i = 1; i < a.ngroups; ++i)
+    if (it >= a.grp[i].iter0) g = i;
+  return g;
+}
+template <typename Args>
+__device__ __forceinline__ int64_t total_iters(const Args& a) {
+  return a.ngroups > 0 ? a.iters : (int64_t)a.units * a.T;
+}
+template <typename Args>
+__device__ __forceinline__ int64_t unit_first_iter(const Args& a, int64_t u) {
+  if (a.ngroups <= 0) return u * a.T;
+  const UnitGroup& G = a.grp[group_of_unit(a, u)];
+  return G.iter0 + (u - G.units0) * G.T;
+}
+template <typename Args>
+__device__ __forceinline__ int64_t unit_of_iter(const Args& a, int64_t it) {
+  if (a.ngroups <= 0) return it / a.T;
+  const UnitGroup& G = a.grp[group_of_iter(a, it)];
+  return G.units0 + (it - G.iter0) / G.T;
+}
+// part_slot for units of any length.
+template <typename Args>
+__device__ __forceinline__ int64_t part_slot_of(const Args& a, int64_t w, int64_t u, int64_t I) {
+  return (int64_t)a.spw * w + (u != unit_of_iter(a, range_begin(w, I, a.P)) ? 1 : 0);
+}
+
 // Work-group ids are handed to the 8 XCDs round robin (id % 8). Remapping so
 // that XCD x gets the contiguous range [x P/8, (x+1) P/8) keeps the work
 // groups that read the same head's K/V on one XCD and its L2.
@@ -296,6 +336,12 @@ struct FetchRun {
   int shift;  // rows a moving run is displaced by (the unit's chunk in a batched launch)
 };
 
+// A unit's own runs and cache tiles on the sequence path (those of its group
+// in a launch of groups): runs[rb .. rb + rn), ct key tiles over cache keys.
+struct UnitRuns {
+  int rb, rn, ct;
+};
+
 // Runs of a launch whose visible slots the kernel derives itself
 // (bca_attend_dev): built once per work group in LDS. A per-block cache has
 // one run per visible block; dev_vis keeps that block's index (ring slot, or
@@ -358,6 +404,17 @@ __device__ __forceinline__ FetchRun fetch_run_at(const AttnArgs& a, int ri, int 
   f.phys = R.phys + (R.moves ? shift : 0);
   return f;
 }
+// Run ri of a unit whose runs start at runs[rb].
+__device__ __forceinline__ FetchRun fetch_run_in(const AttnArgs& a, int rb, int ri, int shift) {
+  const Run R = a.runs[rb + ri];
+  FetchRun f;
+  f.ri = ri;
+  f.shift = shift;
+  f.vstart = R.vstart;
+  f.vend = f.vstart + R.len;
+  f.phys = R.phys + (R.moves ? shift : 0);
+  return f;
+}
 
 // Per-lane constants of the request pattern: the tile row each of the lane's
 // IPW loads covers and its swizzled byte column for K and for V.
@@ -394,14 +451,18 @@ template <int D, bool SEQ, bool DEVT>
 __device__ __forceinline__ void bf16_fetch_tile(const AttnArgs& a, const HeadSrc& ks,
                                                 const HeadSrc& vs, int tile, FetchRun& fr,
                                                 const FetchLane<D>& fl, unsigned char* stage,
-                                                int wave) {
+                                                int wave, const UnitRuns& ur) {
   using C = Bf16Cfg<D>;
   unsigned char* kdst = stage + wave * C::IPW * 1024;
   unsigned char* vdst = kdst + C::TILE_BYTES;
-  if (tile < a.cache_tiles) {
+  // the unit's runs and cache tiles: its own on the sequence path
+  const int ct = SEQ ? ur.ct : a.cache_tiles;
+  const int rn = SEQ ? ur.rn : nruns_of<DEVT>(a);
+  const int rb = SEQ ? ur.rb : 0;
+  if (tile < ct) {
     const int j0 = tile * C::BN;
-    while (j0 >= fr.vend && fr.ri + 1 < nruns_of<DEVT>(a))
-      fr = fetch_run_at<DEVT>(a, fr.ri + 1, fr.shift);
+    while (j0 >= fr.vend && fr.ri + 1 < rn)
+      fr = SEQ ? fetch_run_in(a, rb, fr.ri + 1, fr.shift) : fetch_run_at<DEVT>(a, fr.ri + 1, fr.shift);
     const int rowb = SEQ ? a.cache_row_elems * 2 : C::ROWB;
     if (j0 + C::BN <= fr.vend) {
       // the whole tile lies in one run
@@ -418,8 +479,8 @@ __device__ __forceinline__ void bf16_fetch_tile(const AttnArgs& a, const HeadSrc
       for (int q = 0; q < C::IPW; ++q) {
         const int j = j0 + fl.r[q];
         int phys = -1;
-        for (int rr = fr.ri; rr < nruns_of<DEVT>(a); ++rr) {
-          const Run R = run_of<DEVT>(a, rr);
+        for (int rr = fr.ri; rr < rn; ++rr) {
+          const Run R = run_of<DEVT>(a, rb + rr);
           if (R.vstart >= j0 + C::BN) break;
           if (j >= R.vstart && j < R.vstart + R.len)
             phys = R.phys + (SEQ && R.moves ? fr.shift : 0) + j - R.vstart;
@@ -431,7 +492,7 @@ __device__ __forceinline__ void bf16_fetch_tile(const AttnArgs& a, const HeadSrc
       }
     }
   } else {
-    const int r0 = (tile - a.cache_tiles) * C::BN;
+    const int r0 = (tile - ct) * C::BN;
 #pragma unroll
     for (int q = 0; q < C::IPW; ++q) {
       const int row = r0 + fl.r[q];
@@ -444,10 +505,15 @@ __device__ __forceinline__ void bf16_fetch_tile(const AttnArgs& a, const HeadSrc
   }
 }
 
-// Keys of `tile` that are real (the rest of the tile is padding).
+// Keys of `tile` that are real (the rest of the tile is padding), for a
+// unit with cache_tiles tiles over nk_cache cache keys and n keys of its own.
+__device__ __forceinline__ int tile_valid_of(int cache_tiles, int nk_cache, int n, int tile,
+                                             int bn) {
+  if (tile < cache_tiles) return min(bn, nk_cache - tile * bn);
+  return min(bn, n - (tile - cache_tiles) * bn);
+}
 __device__ __forceinline__ int tile_valid(const AttnArgs& a, int tile, int bn) {
-  if (tile < a.cache_tiles) return min(bn, a.nk_cache - tile * bn);
-  return min(bn, a.n - (tile - a.cache_tiles) * bn);
+  return tile_valid_of(a.cache_tiles, a.nk_cache, a.n, tile, bn);
 }
 
 // Work-group barrier without the memory fences __syncthreads() adds (those
@@ -591,7 +657,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
   const int grp = wave >> 2;
   const int lane = tid & 63, l32 = lane & 31, hi = lane >> 5;
   const int w = logical_wg(a);
-  const int64_t I = (int64_t)a.units * a.T;
+  const int64_t I = SEQ ? total_iters(a) : (int64_t)a.units * a.T;
   int64_t it = range_begin(w, I, a.P);
   const int64_t it_end = range_begin(w + 1, I, a.P);
 
@@ -620,9 +686,35 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
   }
 
   while (it < it_end) {
-    const int u = (int)(it / a.T);
-    const int t0 = (int)(it - (int64_t)u * a.T);
-    const int t1 = (int)((it_end - it) < (int64_t)(a.T - t0) ? t0 + (it_end - it) : a.T);
+    // the unit holding iteration it: its length, first iteration and runs
+    // (on the sequence path those of its group in a launch of groups)
+    int u, t0, T;
+    UnitRuns ur{0, 0, 0};
+    int nkc = 0, shift = 0;
+    if constexpr (SEQ) {
+      T = a.T;
+      ur = UnitRuns{0, a.nruns, a.cache_tiles};
+      nkc = a.nk_cache;
+      int64_t gi0 = 0;
+      int gu0 = 0, gc0 = 0;
+      if (a.ngroups > 0) {
+        const UnitGroup& G = a.grp[group_of_iter(a, it)];
+        T = G.T;
+        ur = UnitRuns{G.run0, G.nruns, G.cache_tiles};
+        nkc = G.nk_cache;
+        gc0 = G.chunk0;
+        gi0 = G.iter0;
+        gu0 = G.units0;
+      }
+      u = gu0 + (int)((it - gi0) / T);
+      t0 = (int)(it - gi0 - (int64_t)(u - gu0) * T);
+      shift = (u / a.upc - gc0) * a.chunk_rows;
+    } else {
+      u = (int)(it / a.T);
+      t0 = (int)(it - (int64_t)u * a.T);
+      T = a.T;
+    }
+    const int t1 = (int)((it_end - it) < (int64_t)(T - t0) ? t0 + (it_end - it) : T);
     const int nt = t1 - t0;
     const int ci = SEQ ? __builtin_amdgcn_readfirstlane(u / a.upc) : 0;  // chunk of the launch
     const int ul = u - ci * a.upc;
@@ -635,9 +727,13 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
     const HeadSrc vsrc = head_src(a.vc, static_cast<const __bf16*>(a.vcur) + cel, a, h, D, 2, 2);
     const float c = a.scale_log2;  // base-2 softmax scale
 
-    FetchRun fr = fetch_run_at<DEVT>(a, 0, SEQ ? ci * a.chunk_rows : 0);
-    bf16_fetch_tile<D, SEQ, DEVT>(a, ksrc, vsrc, t0, fr, fl, smem, wave);
-    if (nt > 1) bf16_fetch_tile<D, SEQ, DEVT>(a, ksrc, vsrc, t0 + 1, fr, fl, smem + C::STAGE, wave);
+    FetchRun fr = SEQ ? fetch_run_in(a, ur.rb, 0, shift) : fetch_run_at<DEVT>(a, 0);
+    // real keys of a tile of this unit
+    auto valid = [&](int tile) {
+      return SEQ ? tile_valid_of(ur.ct, nkc, a.n, tile, C::BN) : tile_valid(a, tile, C::BN);
+    };
+    bf16_fetch_tile<D, SEQ, DEVT>(a, ksrc, vsrc, t0, fr, fl, smem, wave, ur);
+    if (nt > 1) bf16_fetch_tile<D, SEQ, DEVT>(a, ksrc, vsrc, t0 + 1, fr, fl, smem + C::STAGE, wave, ur);
 
     // Q^T fragments (B operand): lane holds query q0+l32, dims 16kk+8hi .. +7;
     // rows past the chunk read as zeros (out-of-range buffer offsets).
@@ -673,7 +769,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
       const int r = k >> 1;
       if ((k & 1) == 0 && r + 2 < nt)
         bf16_fetch_tile<D, SEQ, DEVT>(a, ksrc, vsrc, t0 + r + 2, fr, fl, smem + ((r + 2) & 3) * C::STAGE,
-                           wave);
+                           wave, ur);
     };
     auto end_phase = [&](int k) {
       const int q = (k + 1) >> 1;
@@ -705,7 +801,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
       }
       end_phase(0);
       begin_phase(1);
-      if (wave_rows) pp_softmax<D>(st, tile_valid(a, t0, C::BN), hi, c);
+      if (wave_rows) pp_softmax<D>(st, valid(t0), hi, c);
       end_phase(1);
       for (int r = 1; r < nt; ++r) {
         begin_phase(2 * r);
@@ -716,7 +812,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
         }
         end_phase(2 * r);
         begin_phase(2 * r + 1);
-        if (wave_rows) pp_softmax<D>(st, tile_valid(a, t0 + r, C::BN), hi, c);
+        if (wave_rows) pp_softmax<D>(st, valid(t0 + r), hi, c);
         end_phase(2 * r + 1);
       }
       begin_phase(2 * nt);
@@ -751,7 +847,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
       end_phase(1);
       for (int r = 1; r < nt; ++r) {
         begin_phase(2 * r);
-        if (wave_rows) pp_softmax<D>(st, tile_valid(a, t0 + r - 1, C::BN), hi, c);
+        if (wave_rows) pp_softmax<D>(st, valid(t0 + r - 1), hi, c);
         end_phase(2 * r);
         begin_phase(2 * r + 1);
         if (wave_rows) {
@@ -762,7 +858,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
         end_phase(2 * r + 1);
       }
       begin_phase(2 * nt);
-      if (wave_rows) pp_softmax<D>(st, tile_valid(a, t0 + nt - 1, C::BN), hi, c);
+      if (wave_rows) pp_softmax<D>(st, valid(t0 + nt - 1), hi, c);
       end_phase(2 * nt);
       begin_phase(2 * nt + 1);
       if (wave_rows) {
@@ -779,7 +875,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
       const float inv = 1.0f / l_tot;
       const float lse_val = (st.m_run + log2f(l_tot)) * kLn2;
       const int row = q0 + l32;
-      const bool whole = (t0 == 0) && (t1 == a.T);
+      const bool whole = (t0 == 0) && (t1 == T);
       if (row < a.n) {
         if (whole) {
           __bf16* op = static_cast<__bf16*>(a.o) + cel + ((int64_t)row * a.H + h) * D;
@@ -796,8 +892,8 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
           if (hi == 0 && a.lse)
             a.lse[(SEQ ? ci * a.chunk_lse : 0) + (int64_t)h * a.n + row] = lse_val;
         } else {
-          const int64_t prow =
-              part_slot(w, u, I, a.T, a.P, a.spw) * C::BM + (wave & 7) * 32 + l32;
+          const int64_t slot = SEQ ? part_slot_of(a, w, u, I) : part_slot(w, u, I, a.T, a.P, a.spw);
+          const int64_t prow = slot * C::BM + (wave & 7) * 32 + l32;
           // fp16 partial outputs with a power-of-two scale per row: the row's
           // largest |O| (over the lane pair that holds the row) is brought into
           // [0.5, 1), so a value is rounded to within 2^-12 of that maximum
@@ -1807,7 +1903,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const MergeArgs a) {
 // chunks of every piece in order (consecutive threads, consecutive 16
 // bytes; all of a thread's chunks belong to one row), combine them, and
 // write the result out through LDS as whole rows.
-template <int D>
+// GROUPED: the units of a launch of groups (see UnitGroup).
+template <int D, bool GROUPED>
 __global__ __launch_bounds__(256) void merge_lanes_kernel(const MergeArgs a) {
   constexpr int NCH = 4 * D / 256;  // chunks per thread: a slice holds 4 D of them
   constexpr int RS = D + 8;         // LDS row stride (elements), off the bank period
@@ -1815,9 +1912,11 @@ __global__ __launch_bounds__(256) void merge_lanes_kernel(const MergeArgs a) {
   const int slices = a.bm / 32;
   const int u = blockIdx.x / slices;
   const int sl = blockIdx.x - u * slices;
-  const int64_t I = (int64_t)a.units * a.T;
-  const int64_t w0 = first_wg_of((int64_t)u * a.T, I, a.P);
-  const int pieces = (int)(first_wg_of((int64_t)(u + 1) * a.T - 1, I, a.P) - w0 + 1);
+  const int64_t I = GROUPED ? a.iters : (int64_t)a.units * a.T;
+  const int64_t w0 = first_wg_of(GROUPED ? unit_first_iter(a, u) : (int64_t)u * a.T, I, a.P);
+  const int pieces = (int)(first_wg_of((GROUPED ? unit_first_iter(a, u + 1) : (int64_t)(u + 1) * a.T) - 1,
+                                       I, a.P) -
+                           w0 + 1);
   if (pieces <= 1) return;  // written whole by the attention kernel
   const int ci = u / a.upc, ul = u - ci * a.upc;  // chunk of a batched launch
   const int h = ul / a.QT, qt = ul - h * a.QT;
@@ -1826,7 +1925,8 @@ __global__ __launch_bounds__(256) void merge_lanes_kernel(const MergeArgs a) {
   const int t = threadIdx.x;
   const int lane = t & 63, r = lane & 31, hi = lane >> 5;
   const bool live = row0 + r < a.n;
-  const int64_t slot0 = part_slot(w0, u, I, a.T, a.P, a.spw);
+  const int64_t slot0 =
+      GROUPED ? part_slot_of(a, w0, u, I) : part_slot(w0, u, I, a.T, a.P, a.spw);
   // piece j >= 1 has the slot of its own (its range starts inside unit u)
   auto slot_of = [&](int j) -> int64_t { return j == 0 ? slot0 : (w0 + j) * a.spw; };
   const _Float16* part = reinterpret_cast<const _Float16*>(a.part_o);
@@ -2316,12 +2416,19 @@ int launch_attention_d(const Plan& p, const AttnArgs& a, hipStream_t s) {
     m.upc = a.upc;
     m.chunk_elems = a.chunk_elems;
     m.chunk_lse = a.chunk_lse;
+    m.ngroups = a.ngroups;
+    m.iters = a.iters;
+    for (int g = 0; g < a.ngroups; ++g) m.grp[g] = a.grp[g];
     constexpr int RPB = 256 / (D / kMergeEpt);
     const int blocks = a.units * ((p.bm + RPB - 1) / RPB);
     if (p.kern == Kern::F32)
       hipLaunchKernelGGL((merge_kernel<D, float>), dim3(blocks), dim3(256), 0, s, m);
+    else if (a.ngroups > 0)
+      hipLaunchKernelGGL((merge_lanes_kernel<D, true>), dim3(a.units * (p.bm / 32)), dim3(256), 0,
+                         s, m);
     else
-      hipLaunchKernelGGL(merge_lanes_kernel<D>, dim3(a.units * (p.bm / 32)), dim3(256), 0, s, m);
+      hipLaunchKernelGGL((merge_lanes_kernel<D, false>), dim3(a.units * (p.bm / 32)), dim3(256), 0,
+                         s, m);
     e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
   }

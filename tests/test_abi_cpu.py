@@ -402,6 +402,75 @@ def test_partial_slots_fit_and_do_not_collide():
         assert read == written, (units, T, P)
 
 
+
+def test_grouped_partial_slots_fit_and_do_not_collide():
+    """The same indexing for a launch whose units differ in length (a
+    bca_attend_sequence launch of groups: the chunks before the window is full
+    and the steady block, units numbered group after group, one range of
+    iterations per work group over all of them, two slots per work group).
+    The unit of an iteration and the first iteration of a unit come from the
+    group table as the kernels compute them; every slot written is below
+    2 P, no two parts share one, and the merge reads exactly those."""
+    def rb(w, I, P):
+        return w * I // P
+
+    def first_wg(x, I, P):
+        return ((x + 1) * P + I - 1) // I - 1
+
+    def table(groups):  # [(units, T)] -> [(iter0, units0, T)]
+        out, it, u = [], 0, 0
+        for units, T in groups:
+            out.append((it, u, T))
+            it += units * T
+            u += units
+        return out, it, u
+
+    def unit_of_iter(tab, it):
+        g = max(i for i, (i0, _, _) in enumerate(tab) if it >= i0)
+        i0, u0, T = tab[g]
+        return u0 + (it - i0) // T
+
+    def unit_first_iter(tab, u):
+        g = max(i for i, (_, u0, _) in enumerate(tab) if u >= u0)
+        i0, u0, T = tab[g]
+        return i0 + (u - u0) * T
+
+    cases = [([(72, 24), (72, 48), (432, 72)], 256), ([(12, 3), (12, 5), (60, 7)], 256),
+             ([(6, 1), (6, 2), (6, 3), (30, 4)], 17), ([(5, 9), (3, 2)], 7),
+             ([(48, 8), (48, 15), (48, 22), (96, 29)], 192)]
+    for groups, P in cases:
+        tab, I, units = table(groups)
+        P = min(P, I)
+        spw = 2
+        written = {}
+        for w in range(P):
+            a, b = rb(w, I, P), rb(w + 1, I, P)
+            u_first = unit_of_iter(tab, a)
+            it = a
+            while it < b:
+                g = max(i for i, (i0, _, _) in enumerate(tab) if it >= i0)
+                i0, u0, T = tab[g]
+                u = u0 + (it - i0) // T
+                t0 = it - i0 - (u - u0) * T
+                t1 = min(T, t0 + (b - it))
+                if not (t0 == 0 and t1 == T):
+                    slot = spw * w + (1 if u != u_first else 0)
+                    assert slot < spw * P, (groups, P, w, u)
+                    assert slot not in written, (groups, P, w, u)
+                    written[slot] = (w, u)
+                it += t1 - t0
+        read = {}
+        for u in range(units):
+            w0 = first_wg(unit_first_iter(tab, u), I, P)
+            pieces = first_wg(unit_first_iter(tab, u + 1) - 1, I, P) - w0 + 1
+            if pieces <= 1:
+                continue
+            for j in range(pieces):
+                slot = (spw * w0 + (1 if u != unit_of_iter(tab, rb(w0, I, P)) else 0)) if j == 0 \
+                    else spw * (w0 + j)
+                read[slot] = (w0 + j, u)
+        assert read == written, (groups, P)
+
 def test_sequence_entry_point_validates_before_launch():
     P = FAKE
     S = bca.bca_sequence_spec

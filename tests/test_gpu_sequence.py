@@ -71,6 +71,26 @@ def test_sequence_matches_oracle(dtype, H, d, n, C, P, W, G):
     assert_close(o, lse, eo, el, TOL[dtype], f"sequence {dtype} n {n} C {C} P {P} W {W} G {G}")
 
 
+GROUPED = [
+    # H, d, n, C, P, W with the automatic split and at least as many units as
+    # the device has CUs: the chunks before the window is full and the steady
+    # block run as one launch of groups of different lengths
+    (32, 64, 256, 9, 100, 3),  # 5 groups (4 single chunks and the steady block), a prefix
+    (16, 64, 128, 16, 0, 9),   # 10 launches' worth: the first 2 chunks alone, 8 groups in one
+    (8, 64, 260, 16, 0, 1),    # ragged query tiles (260 = 256 + 4 rows)
+]
+
+
+@pytest.mark.parametrize("H,d,n,C,P,W", GROUPED)
+def test_sequence_grouped_launch(H, d, n, C, P, W):
+    """Launches of groups against the oracle, every head and row."""
+    log(f"grouped sequence H {H} d {d} n {n} C {C} P {P} W {W}")
+    q, k, v = seq_inputs(C, n, H, d, P, "bf16", 70 + C + W)
+    o, lse = run(q, k, v, n, W, P, 0, "bf16")
+    eo, el = oracle.attend_sequence(q, k, v, n, W, P, 1.0 / math.sqrt(d))
+    assert_close(o, lse, eo, el, TOL["bf16"], f"grouped sequence n {n} C {C} P {P} W {W}")
+
+
 def test_sequence_invisible_rows_do_not_leak():
     # NaN in chunk 0's keys and values: chunks c > W never see chunk 0, so their
     # outputs must equal those of an unpoisoned run bit for bit
