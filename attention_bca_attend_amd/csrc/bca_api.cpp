@@ -174,12 +174,37 @@ int32_t pieces_bound(int64_t units, int64_t T, int64_t P) {
 // a unit boundary, and each unit has the fewest partial outputs to merge);
 // otherwise one range of tile iterations per resident work group
 // ("stream-K").
+// Work groups for a stream-K cut of I iterations over units whose first
+// iterations unit_first(u) (u = 0 .. units, unit_first(units) = I) are given:
+// among the counts from target down to 97 % of it, the one that leaves the
+// fewest units split across work groups (each split unit costs partial
+// outputs and their merge; 3 % fewer work groups cost at most 3 % more
+// tiles per group). A cut whose ranges all end on unit boundaries needs no
+// merge at all.
+template <typename First>
+int64_t fewest_split_wgs(int64_t I, int64_t units, int64_t target, First unit_first) {
+  const int64_t hi = std::max<int64_t>(1, std::min(I, target));
+  const int64_t lo = std::max<int64_t>(1, hi - hi * 3 / 100);
+  int64_t best = hi, best_split = -1;
+  for (int64_t P = hi; P >= lo; --P) {
+    int64_t split = 0;
+    for (int64_t u = 0; u < units; ++u)
+      split += first_wg(unit_first(u + 1) - 1, I, P) != first_wg(unit_first(u), I, P);
+    if (best_split < 0 || split < best_split) {
+      best = P;
+      best_split = split;
+    }
+    if (split == 0) break;
+  }
+  return best;
+}
+
 int64_t choose_wgs_on(int cus, Kern k, int64_t units, int64_t T, int32_t G) {
   const int64_t I = units * T;
   if (G >= 1) return units * std::min<int64_t>(G, T);
   const int64_t target = (int64_t)cus * wgs_per_cu(k);
   if (units <= target) return units * std::min<int64_t>(T, target / units);
-  return std::max<int64_t>(1, std::min(I, target));
+  return fewest_split_wgs(I, units, target, [T](int64_t u) { return u * T; });
 }
 
 int64_t choose_wgs(const bca_cache* c, Kern k, int64_t units, int64_t T, int32_t G) {
@@ -922,7 +947,13 @@ void seq_launch_plan(const bca_sequence_spec* s, int32_t qkv_dtype, int cus, con
   p.iters = iters;
   p.nruns = nruns;
   p.units = (int32_t)units;
-  p.wgs = (int32_t)std::max<int64_t>(1, std::min<int64_t>(iters, (int64_t)cus * wgs_per_cu(p.kern)));
+  p.wgs = (int32_t)fewest_split_wgs(iters, units, (int64_t)cus * wgs_per_cu(p.kern),
+                                     [&p, &L, units](int64_t u) -> int64_t {
+                                       int g = 0;
+                                       for (int i = 1; i < L.ng; ++i)
+                                         if (u >= p.grp[i].units0) g = i;
+                                       return p.grp[g].iter0 + (u - p.grp[g].units0) * p.grp[g].T;
+                                     });
   int32_t worst = 1;
   for (int g = 0; g < L.ng; ++g) {
     const UnitGroup& G = p.grp[g];

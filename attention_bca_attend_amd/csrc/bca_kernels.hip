@@ -876,58 +876,73 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(const AttnArgs a) {
       const float lse_val = (st.m_run + log2f(l_tot)) * kLn2;
       const int row = q0 + l32;
       const bool whole = (t0 == 0) && (t1 == T);
-      if (row < a.n) {
-        if (whole) {
-          __bf16* op = static_cast<__bf16*>(a.o) + cel + ((int64_t)row * a.H + h) * D;
+      if (whole) {
+        // the wave's 32 rows through its own 32 rows of LDS stages 2-3 (free
+        // here: the next unit requests tile 2 only after its first barrier),
+        // so that every store writes whole rows (RPW rows of D bf16)
+        constexpr int CPR = D / 8, RPW = 64 / CPR;
+        // lane-derived offsets computed here, not kept through the tile loop
+        int le = lane;
+        asm volatile("" : "+v"(le));
+        const int r32 = le & 31, h2 = le >> 5;
+        unsigned char* ws = smem + 2 * C::STAGE + (wave & 7) * 32 * C::ROWB;
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              f32x4_t v4 = {st.o[db][4 * g], st.o[db][4 * g + 1], st.o[db][4 * g + 2],
-                            st.o[db][4 * g + 3]};
-              v4 *= inv;
-              *reinterpret_cast<bf16x4_t*>(op + 32 * db + 8 * g + 4 * hi) =
-                  __builtin_convertvector(v4, bf16x4_t);
-            }
-          if (hi == 0 && a.lse)
-            a.lse[(SEQ ? ci * a.chunk_lse : 0) + (int64_t)h * a.n + row] = lse_val;
-        } else {
-          const int64_t slot = SEQ ? part_slot_of(a, w, u, I) : part_slot(w, u, I, a.T, a.P, a.spw);
-          const int64_t prow = slot * C::BM + (wave & 7) * 32 + l32;
-          // fp16 partial outputs with a power-of-two scale per row: the row's
-          // largest |O| (over the lane pair that holds the row) is brought into
-          // [0.5, 1), so a value is rounded to within 2^-12 of that maximum
-          // (bf16 would give 2^-9) in the same two bytes; the exponent goes to
-          // part_exp and the merge multiplies it back exactly. A row with a
-          // NaN or an infinity keeps exponent 0 and carries them through.
-          // The wave's 32 rows are stored as the lanes hold them (chunk
-          // 2 db + hf of lane l at 16 bytes x (64 (2 db + hf) + l) from the
-          // wave's first row), so that each store writes 1 KB of consecutive
-          // bytes; merge_lanes_kernel reads that layout.
-          float mx = 0.f;
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(st.o[db][e]));
-          mx = xhalf_max(mx) * inv;
-          int ex = 0;
-          if (mx > 0.f && mx <= 3.402823466e38f) (void)frexpf(mx, &ex);
-          const float sc = __builtin_amdgcn_ldexpf(inv, -ex);
-          _Float16* pp = reinterpret_cast<_Float16*>(a.part_o) + (prow - l32) * D + lane * 8;
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-              f32x8_t v8;
-#pragma unroll
-              for (int j = 0; j < 8; ++j) v8[j] = st.o[db][8 * hf + j] * sc;
-              *reinterpret_cast<f16x8_t*>(pp + (2 * db + hf) * 512) =
-                  __builtin_convertvector(v8, f16x8_t);
-            }
-          if (hi == 0) {
-            a.part_lse[prow] = lse_val;
-            a.part_exp[prow] = ex;
+          for (int g = 0; g < 4; ++g) {
+            f32x4_t v4 = {st.o[db][4 * g], st.o[db][4 * g + 1], st.o[db][4 * g + 2],
+                          st.o[db][4 * g + 3]};
+            v4 *= inv;
+            *reinterpret_cast<bf16x4_t*>(ws + r32 * C::ROWB + (((4 * db + g) ^ (r32 % CPR)) << 4) +
+                                         8 * h2) = __builtin_convertvector(v4, bf16x4_t);
           }
+        const int rq = le / CPR, cq = le % CPR;
+#pragma unroll
+        for (int i = 0; i < 32 / RPW; ++i) {
+          const int rr = i * RPW + rq;
+          const uint4 x = *reinterpret_cast<const uint4*>(ws + rr * C::ROWB + ((cq ^ (rr % CPR)) << 4));
+          if (q0 + rr < a.n)
+            *reinterpret_cast<uint4*>(static_cast<__bf16*>(a.o) + cel +
+                                      ((int64_t)(q0 + rr) * a.H + h) * D + 8 * cq) = x;
+        }
+        if (hi == 0 && a.lse && row < a.n)
+          a.lse[(SEQ ? ci * a.chunk_lse : 0) + (int64_t)h * a.n + row] = lse_val;
+      } else if (row < a.n) {
+        const int64_t slot = SEQ ? part_slot_of(a, w, u, I) : part_slot(w, u, I, a.T, a.P, a.spw);
+        const int64_t prow = slot * C::BM + (wave & 7) * 32 + l32;
+        // fp16 partial outputs with a power-of-two scale per row: the row's
+        // largest |O| (over the lane pair that holds the row) is brought into
+        // [0.5, 1), so a value is rounded to within 2^-12 of that maximum
+        // (bf16 would give 2^-9) in the same two bytes; the exponent goes to
+        // part_exp and the merge multiplies it back exactly. A row with a
+        // NaN or an infinity keeps exponent 0 and carries them through.
+        // The wave's 32 rows are stored as the lanes hold them (chunk
+        // 2 db + hf of lane l at 16 bytes x (64 (2 db + hf) + l) from the
+        // wave's first row), so that each store writes 1 KB of consecutive
+        // bytes; merge_lanes_kernel reads that layout.
+        float mx = 0.f;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(st.o[db][e]));
+        mx = xhalf_max(mx) * inv;
+        int ex = 0;
+        if (mx > 0.f && mx <= 3.402823466e38f) (void)frexpf(mx, &ex);
+        const float sc = __builtin_amdgcn_ldexpf(inv, -ex);
+        _Float16* pp = reinterpret_cast<_Float16*>(a.part_o) + (prow - l32) * D + lane * 8;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            f32x8_t v8;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v8[j] = st.o[db][8 * hf + j] * sc;
+            *reinterpret_cast<f16x8_t*>(pp + (2 * db + hf) * 512) =
+                __builtin_convertvector(v8, f16x8_t);
+          }
+        if (hi == 0) {
+          a.part_lse[prow] = lse_val;
+          a.part_exp[prow] = ex;
         }
       }
     }

@@ -346,14 +346,20 @@ def test_rope_entry_points_validate_before_launch():
 
 def test_sequence_workspace_bounded_by_work_groups():
     """Partial outputs are indexed by work group (at most two per group), so a
-    whole clip's workspace does not grow with its number of chunks: 64
-    Wan-shaped chunks need what 8 need, below 200 MB."""
+    whole clip's workspace does not grow with its number of chunks: 64 chunks
+    of 12 x 1200 tokens need what 8 need, below 200 MB. The Wan-shaped clips
+    (12 x 1536) need none: their launch of groups is cut into ranges that all
+    end on unit boundaries (252 work groups of 144 tiles for 8 chunks), so no
+    unit is split and nothing is merged."""
     S = bca.bca_sequence_spec
-    need = {C: bca.bca_attend_sequence_workspace_bytes(S(12, 128, 1536, C, 0, 2, 0, 0.088),
+    need = {C: bca.bca_attend_sequence_workspace_bytes(S(12, 128, 1200, C, 0, 2, 0, 0.088),
                                                       bca.BF16) for C in (8, 64)}
     assert 0 < need[64] == need[8] < 200e6, need
     # 256 work groups x 2 slots x 256 rows x (128 + 1) fp32
     assert need[64] <= 256 * 2 * 256 * 129 * 4 + 512
+    for C in (8, 64):
+        assert bca.bca_attend_sequence_workspace_bytes(S(12, 128, 1536, C, 0, 2, 0, 0.088),
+                                                       bca.BF16) == 0, C
 
 
 def test_partial_slots_fit_and_do_not_collide():
