@@ -236,9 +236,10 @@ float* block_scales(const bca_cache* c, int32_t layer, int kv) {
 int32_t slots_per_wg(int64_t units, int64_t P) { return (P >= units && P % units == 0) ? 1 : 2; }
 
 // Bytes of part_o [P][spw][bm][d] (sized for fp32), then part_lse [P][spw][bm]
-// fp32, each region 256-byte aligned. The bf16 path's fp16 partials fill the
-// first half of part_o; their row exponents [P][spw][bm] (int32) follow them
-// in the second half (part_exp_offset).
+// fp32, each region 256-byte aligned. The fp16 partials of the bf16 and 8-bit
+// paths fill the first half of part_o; their row exponents [P][spw][bm]
+// (int32) follow them in the second half (part_exp_offset). The fp32 path
+// fills part_o with fp32.
 size_t part_o_bytes(int64_t P, int32_t spw, int bm, int d) {
   return ((size_t)P * spw * bm * d * 4 + 255) & ~(size_t)255;
 }

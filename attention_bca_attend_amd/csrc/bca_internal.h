@@ -105,9 +105,10 @@ struct AttnArgs {
   const void* vc;     // this layer's V blocks
   void* o;            // [n][H][d]
   float* lse;         // [H][n] or null
-  float* part_o;      // [P][spw][bm][d]: fp32, or fp16 scaled per row on the bf16 path
+  float* part_o;      // [P][spw][bm][d]: fp32 (fp32 path), or fp16 scaled per row
+                      // and stored as the lanes hold them (bf16, 8-bit paths)
   float* part_lse;    // [P][spw][bm]
-  int32_t* part_exp;  // [P][spw][bm]: the bf16 path's row exponents (see merge_kernel)
+  int32_t* part_exp;  // [P][spw][bm]: the fp16 partials' row exponents (merge_lanes_kernel)
   int64_t cache_head_elems;  // elements between heads' first cache rows: (S+R)*n*d for the
                              // ring, d for a token-major sequence [rows][H][d]
   int64_t cache_span_elems;  // elements one head's cache rows span (buffer resource size)

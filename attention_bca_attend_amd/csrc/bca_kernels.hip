@@ -5,7 +5,8 @@
 //                      MFMA (v_mfma_f32_32x32x64_f8f6f4), or int8 K on the
 //                      int8 MFMA (v_mfma_i32_32x32x32_i8) with e4m3 V
 //   attn_f32_kernel    fp32 flash attention on the vector ALUs
-//   merge_kernel       log-sum-exp merge of segment partials
+//   merge_lanes_kernel log-sum-exp merge of segment partials (bf16, 8-bit paths)
+//   merge_kernel       the same for the fp32 path's partials
 //   append_copy_kernel fused K/V write of one chunk into its ring slot
 //   append_amax_kernel per-head scales of a per-block 8-bit append
 //   append_fp8_kernel  the same with 8-bit quantisation (also the 8-bit copy of
@@ -30,10 +31,12 @@
 // (head, query tile) unit has the same number T of key tiles. The units*T tile
 // iterations are cut into P consecutive, equal ranges, one per work group; a
 // unit whose tiles span several ranges is computed as several segments, each
-// written as a normalised partial output plus its LSE, and merge_kernel
+// written as a normalised partial output plus its LSE, and the merge kernel
 // combines them. A unit computed whole writes the final output. (With P a
 // multiple of the unit count every unit gets the same number of equal
-// segments; otherwise ranges cross unit boundaries, "stream-K" style.)
+// segments; otherwise ranges cross unit boundaries, "stream-K" style.) A
+// sequence launch may hold groups of units of different lengths (UnitGroup),
+// numbered group after group.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -1786,15 +1789,14 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(const AttnArgs a) {
 // Log-sum-exp merge of the segments of every split unit:
 //   M = max_g LSE_g, w_g = exp(LSE_g - M) (0 for LSE_g = -inf),
 //   O = sum_g w_g O_g / sum_g w_g, LSE = M + ln sum_g w_g.
-// merge_kernel reads fp32 partials stored row by row (fp32 path, 8-bit
-// caches): one work group covers 256 / (D/16) rows of one unit, each thread
-// sixteen dims. The unit's first piece and piece count come from the range
+// merge_kernel reads the fp32 path's partials, stored row by row: one work
+// group covers 256 / (D/16) rows of one unit, each thread sixteen dims. The unit's first piece and piece count come from the range
 // arithmetic once per work group (thread 0, through LDS).
 // Pieces whose loads the merge issues all at once.
 constexpr int kMergeBatch = 4;
 constexpr int kMergeEpt = 16;  // dims per thread
 
-// Eight fp32 partial-output values (fp32 path, 8-bit caches).
+// Eight fp32 partial-output values (fp32 path).
 __device__ __forceinline__ void load_part8(const float* p, float (&x)[8]) {
   const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
   const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);

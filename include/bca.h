@@ -303,7 +303,11 @@ bca_status bca_attend_rope(const bca_cache* cache, int32_t layer, const bca_wind
  * merge launch when its windows are split: with BCA_BF16 one launch per chunk
  * before the window reaches its full length (chunks 0 .. W-1, and chunk W too
  * with a prefix) and one launch for all the remaining chunks, which see the
- * same number of keys; with BCA_F32 one launch per chunk.
+ * same number of keys; with BCA_F32 one launch per chunk. With BCA_BF16 and
+ * num_segments 0, when the clip has at least as many (head, 256-row query
+ * tile) units as the device has compute units, the last eight of those
+ * launches become one launch, cut where possible on unit boundaries (then
+ * nothing is merged and the workspace may be 0 bytes).
  * Errors: BCA_ERR_INVALID_ARG for a NULL or bad spec (non-positive sizes,
  * history < 0, prefix_tokens < 0, num_segments outside [0, 64], non-finite
  * scale), NULL or misaligned buffers (16 bytes; lse 4), or K/V larger than
