@@ -142,6 +142,23 @@ def test_sequence_full_size_wan_shape():
         assert_close(o[:, hs], lse[:, hs], eo, el, TOL["bf16"], f"Wan-shaped sequence head {h}")
 
 
+def test_sequence_unsplit_launch_of_groups():
+    """4 Wan-shaped chunks (12 heads x 1536 tokens) with a window of 1: chunk 0
+    and chunks 1-3 run as one launch of groups cut on unit boundaries (no unit
+    split, no merge, every output row stored whole by the attention kernel);
+    the workspace is 0 bytes. The oracle on heads 0 and 11, every row."""
+    import attention_bca_attend_amd as bca
+    H, d, n, C, W = 12, 128, 1536, 4, 1
+    spec = bca.bca_sequence_spec(H, d, n, C, 0, W, 0, 1.0 / math.sqrt(d))
+    assert bca.bca_attend_sequence_workspace_bytes(spec, bca.BF16) == 0
+    q, k, v = seq_inputs(C, n, H, d, 0, "bf16", 65)
+    o, lse = run(q, k, v, n, W, 0, 0, "bf16")
+    for h in (0, 11):
+        hs = slice(h, h + 1)
+        eo, el = oracle.attend_sequence(q[:, hs], k[:, hs], v[:, hs], n, W, 0, 1.0 / math.sqrt(d))
+        assert_close(o[:, hs], lse[:, hs], eo, el, TOL["bf16"], f"unsplit launch of groups head {h}")
+
+
 def test_sequence_64_chunk_wan_clip():
     """A 64-chunk Wan-shaped clip (12 heads x 1536 tokens, window 2) in one
     call: its workspace is bounded by the launches' work groups (below 200 MB;
