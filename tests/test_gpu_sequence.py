@@ -159,6 +159,23 @@ def test_sequence_unsplit_launch_of_groups():
         assert_close(o[:, hs], lse[:, hs], eo, el, TOL["bf16"], f"unsplit launch of groups head {h}")
 
 
+def test_sequence_wan_clip_of_8_as_benchmarked():
+    """The training-form workload in the launch configuration the benchmark
+    times: 8 Wan-shaped chunks (12 heads x 1536 tokens), window 2, automatic
+    split: one launch of groups over 252 work groups of 144 tiles, no unit
+    split, no merge. The oracle on heads 0, 5 and 11, every row."""
+    import attention_bca_attend_amd as bca
+    H, d, n, C, W = 12, 128, 1536, 8, 2
+    spec = bca.bca_sequence_spec(H, d, n, C, 0, W, 0, 1.0 / math.sqrt(d))
+    assert bca.bca_attend_sequence_workspace_bytes(spec, bca.BF16) == 0
+    q, k, v = seq_inputs(C, n, H, d, 0, "bf16", 66)
+    o, lse = run(q, k, v, n, W, 0, 0, "bf16")
+    for h in (0, 5, 11):
+        hs = slice(h, h + 1)
+        eo, el = oracle.attend_sequence(q[:, hs], k[:, hs], v[:, hs], n, W, 0, 1.0 / math.sqrt(d))
+        assert_close(o[:, hs], lse[:, hs], eo, el, TOL["bf16"], f"benchmarked 8-chunk clip head {h}")
+
+
 def test_sequence_64_chunk_wan_clip():
     """A 64-chunk Wan-shaped clip (12 heads x 1536 tokens, window 2) in one
     call: its workspace is bounded by the launches' work groups (below 200 MB;
